@@ -1,0 +1,182 @@
+"""Plain fp64 CPU reference for Parallax attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  The library path never does, and the
+oracle shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (fp64, libm ``exp``); this module only
+builds it with gcc, marshals numpy arrays into it and returns fp64 results.
+What it computes (page "Parallax: Parameterized Local Linear Attention Gives
+Transformers a 'Second Eye'", section 1.3): for each query row,
+``o = o_SA - S_KV @ rho`` with ``o_SA`` the softmax attention output and
+``S_KV`` the softmax-weighted, centred covariance of values against keys.
+
+Array conventions (numpy):
+  * float64 / float32 arrays are read as such;
+  * uint16 arrays are raw bfloat16 bit patterns (widened exactly).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F64, F32, BF16 = 0, 1, 2
+EXPLICIT, STREAMING = 0, 1
+_FORMS = {"explicit": EXPLICIT, "streaming": STREAMING}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile oracle.c into liboracle.so with gcc (fp64, no FMA contraction)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99", "-fPIC",
+           "-shared", "-pthread", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, dbl, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.orc_decode.restype = i32
+    lib.orc_decode.argtypes = [i32, i32, i32, i32, i32, i32, dbl,
+                               vp, i32, vp, i32, vp, vp, i32,
+                               i64, i64, i64, i64, i64, i64,
+                               vp, i32, vp, i32, i32, vp, i32]
+    lib.orc_prefill.restype = i32
+    lib.orc_prefill.argtypes = [i32, i32, i32, i32, i32, i32, i32, dbl,
+                                vp, i32, vp, i32, vp, vp, i32,
+                                vp, i32, vp, i32]
+    _lib = lib
+    return lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float64:
+        return F64
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle: unsupported array dtype {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def decode(q, rho, k, v, scale, *, seq_lens=None, block_table=None, form="streaming",
+           threads=None):
+    """Decode attention rows, one per (batch, query head).
+
+    q, rho : [B, Hq, dk]
+    contiguous cache (block_table is None):
+        k [B, Hkv, Lcap, dk], v [B, Hkv, Lcap, dv]; row b sees seq_lens[b]
+        tokens (all Lcap when seq_lens is None)
+    paged cache:
+        k [NB, Hkv, P, dk], v [NB, Hkv, P, dv] (P tokens per page),
+        block_table [B, max_blocks] int32 of page ids, seq_lens [B] int32
+    Returns out [B, Hq, dv] float64.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    rho = np.ascontiguousarray(rho)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    B, Hq, dk = q.shape
+    if rho.shape != q.shape:
+        raise ValueError("rho must have q's shape")
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
+    Hkv = k.shape[1]
+    dv = v.shape[3]
+    if k.shape[3] != dk or v.shape[:3] != k.shape[:3]:
+        raise ValueError("inconsistent k/v shapes")
+    _, _, P, _ = k.shape
+    k_str = (Hkv * P * dk, P * dk, dk)
+    v_str = (Hkv * P * dv, P * dv, dv)
+    if seq_lens is not None:
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        if seq_lens.shape != (B,):
+            raise ValueError("seq_lens must be [B]")
+    if block_table is not None:
+        if seq_lens is None:
+            raise ValueError("paged decode needs seq_lens")
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        if block_table.ndim != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, max_blocks]")
+        max_blocks = block_table.shape[1]
+        if np.any(seq_lens > max_blocks * P):
+            raise ValueError("seq_lens exceed the block table")
+        L_all = 0
+    else:
+        max_blocks = 0
+        if k.shape[0] != B:
+            raise ValueError("contiguous k must be [B, Hkv, Lcap, dk]")
+        if seq_lens is not None and np.any(seq_lens > P):
+            raise ValueError("seq_lens exceed the cache capacity")
+        L_all = P
+    if seq_lens is not None and np.any(seq_lens < 0):
+        raise ValueError("negative seq_lens")
+    out = np.empty((B, Hq, dv), dtype=np.float64)
+    rc = lib.orc_decode(_FORMS[form], B, Hq, Hkv, dk, dv, float(scale),
+                        _ptr(q), _dtype_code(q), _ptr(rho), _dtype_code(rho),
+                        _ptr(k), _ptr(v), _dtype_code(k),
+                        *k_str, *v_str,
+                        _ptr(seq_lens), L_all,
+                        _ptr(block_table), P if block_table is not None else 0, max_blocks,
+                        _ptr(out), int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle: orc_decode rejected its arguments")
+    return out
+
+
+def prefill(q, rho, k, v, scale, *, rows=None, form="streaming", threads=None):
+    """Causal prefill rows: row i of (b, h) attends to keys 0..i.
+
+    q, rho : [B, S, Hq, dk];  k : [B, S, Hkv, dk];  v : [B, S, Hkv, dv]
+    rows   : query positions to evaluate (default: all S)
+    Returns out [B, len(rows), Hq, dv] float64.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    rho = np.ascontiguousarray(rho)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    B, S, Hq, dk = q.shape
+    Hkv = k.shape[2]
+    dv = v.shape[3]
+    if rho.shape != q.shape or k.shape != (B, S, Hkv, dk) or v.shape[:3] != (B, S, Hkv):
+        raise ValueError("inconsistent prefill shapes")
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
+    if rows is None:
+        rows = np.arange(S, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    out = np.empty((B, rows.size, Hq, dv), dtype=np.float64)
+    rc = lib.orc_prefill(_FORMS[form], B, S, Hq, Hkv, dk, dv, float(scale),
+                         _ptr(q), _dtype_code(q), _ptr(rho), _dtype_code(rho),
+                         _ptr(k), _ptr(v), _dtype_code(k),
+                         _ptr(rows), int(rows.size), _ptr(out),
+                         int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle: orc_prefill rejected its arguments")
+    return out

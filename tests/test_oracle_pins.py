@@ -1,0 +1,418 @@
+"""Pins for the fp64 oracle: each check is fixed by something other than the
+oracle itself -- a hand-worked example, a closed form, a library routine
+(scipy softmax, numpy.cov, numpy.linalg.lstsq), an algebraic invariant of the
+definition, or brute force on tiny inputs.
+
+The definition pinned here (page "Parallax: Parameterized Local Linear
+Attention Gives Transformers a 'Second Eye'", section 1.3): o = o_SA - S_KV rho
+with S_KV the softmax-weighted covariance of values against keys.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+
+FORMS = ["explicit", "streaming"]
+
+
+def one_row(form):
+    """The oracle on a single (batch, head) row: q, rho [dk], K [L, dk], V [L, dv]."""
+    def impl(q, rho, K, V, scale):
+        return oracle.decode(q[None, None], rho[None, None], K[None, None], V[None, None],
+                             scale, form=form, threads=1)[0, 0]
+    return impl
+
+
+def rand_row(rng, L, dk, dv, rho_std=0.5):
+    return (rng.standard_normal(dk), rho_std * rng.standard_normal(dk),
+            rng.standard_normal((L, dk)), rng.standard_normal((L, dv)))
+
+
+def rel_err(a, b):
+    return float(np.max(np.abs(a - b) / (1.0 + np.abs(b))))
+
+
+# ------------------------------------------------------------------ pins ---
+# Each pin takes an implementation of one row and returns its max relative
+# deviation from the pinned value.  test_mutants_are_caught checks that every
+# plausible mistake fails at least one of them.
+
+def pin_hand_example(impl):
+    """Worked by hand: scale 1, q = 1, keys (0, ln 3) -> p = (1/4, 3/4);
+    values (0, 4) -> o_SA = 3; cov = p1 p2 (v1-v2)(k1-k2) = (3/16)(-4)(-ln 3)
+    = (3/4) ln 3; rho = 1 -> o = 3 - (3/4) ln 3."""
+    o = impl(np.array([1.0]), np.array([1.0]), np.array([[0.0], [math.log(3.0)]]),
+             np.array([[0.0], [4.0]]), 1.0)
+    return rel_err(o, np.array([3.0 - 0.75 * math.log(3.0)]))
+
+
+def pin_two_tokens(impl):
+    """Two keys: S_KV = p1 p2 (v1 - v2)(k1 - k2)^T exactly (closed form)."""
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for dk, dv in [(3, 5), (4, 4), (6, 2)]:
+        q, rho, K, V = rand_row(rng, 2, dk, dv)
+        scale = 0.7
+        s1, s2 = scale * K[0] @ q, scale * K[1] @ q
+        p1 = 1.0 / (1.0 + math.exp(s2 - s1))
+        p2 = 1.0 - p1
+        want = p1 * V[0] + p2 * V[1] - p1 * p2 * (V[0] - V[1]) * ((K[0] - K[1]) @ rho)
+        worst = max(worst, rel_err(impl(q, rho, K, V, scale), want))
+    return worst
+
+
+def pin_numpy_cov(impl):
+    """o = softmax-mean of V minus numpy's weighted (biased) cross-covariance times rho."""
+    rng = np.random.default_rng(12)
+    worst = 0.0
+    for L, dk, dv in [(5, 3, 4), (17, 8, 8), (40, 4, 6), (64, 16, 16)]:
+        q, rho, K, V = rand_row(rng, L, dk, dv)
+        scale = 1.0 / math.sqrt(dk)
+        p = scipy.special.softmax(scale * (K @ q))
+        C = np.cov(np.vstack([V.T, K.T]), aweights=p, bias=True)[:dv, dv:]
+        want = p @ V - C @ rho
+        worst = max(worst, rel_err(impl(q, rho, K, V, scale), want))
+    return worst
+
+
+def pin_uniform_limit(impl):
+    """q = 0 makes every weight 1/L (the bandwidth -> infinity end of the
+    taxonomy, section 2.1): o = mean(V) - cov_unweighted(V, K) rho."""
+    rng = np.random.default_rng(13)
+    worst = 0.0
+    for L, dk, dv in [(7, 3, 5), (33, 8, 8)]:
+        _, rho, K, V = rand_row(rng, L, dk, dv)
+        C = np.cov(np.vstack([V.T, K.T]), bias=True)[:dv, dv:]
+        want = V.mean(axis=0) - C @ rho
+        worst = max(worst, rel_err(impl(np.zeros(dk), rho, K, V, 0.5), want))
+    return worst
+
+
+def pin_softmax_at_rho_zero(impl):
+    """rho = 0 (W_R = 0) is plain softmax attention."""
+    rng = np.random.default_rng(14)
+    worst = 0.0
+    for L, dk, dv in [(1, 4, 4), (9, 4, 3), (128, 64, 64)]:
+        q, _, K, V = rand_row(rng, L, dk, dv)
+        scale = 1.0 / math.sqrt(dk)
+        want = scipy.special.softmax(scale * (K @ q)) @ V
+        worst = max(worst, rel_err(impl(q, np.zeros(dk), K, V, scale), want))
+    return worst
+
+
+def pin_lla_intercept(impl):
+    """Local linear attention cross-check (sections 1.2-1.3).  The softmax-
+    weighted least-squares fit v ~ b + W (k - q) has intercept
+    b = vbar - S_VK S_KK^{-1} (kbar - q); so with the solved probe
+    rho* = S_KK^{-1} (kbar - q) the Parallax output must equal the intercept
+    that numpy.linalg.lstsq finds on sqrt(p)-weighted rows."""
+    rng = np.random.default_rng(15)
+    worst = 0.0
+    for L, dk, dv in [(30, 3, 5), (60, 6, 4)]:
+        q, _, K, V = rand_row(rng, L, dk, dv)
+        scale = 0.4
+        p = scipy.special.softmax(scale * (K @ q))
+        kbar = p @ K
+        Kc = K - kbar
+        S_KK = (Kc * p[:, None]).T @ Kc
+        rho_star = np.linalg.solve(S_KK, kbar - q)
+        X = np.hstack([np.ones((L, 1)), K - q])
+        w = np.sqrt(p)[:, None]
+        coef, *_ = np.linalg.lstsq(X * w, V * w, rcond=None)
+        worst = max(worst, rel_err(impl(q, rho_star, K, V, scale), coef[0]))
+    return worst
+
+
+def pin_single_key(impl):
+    """One key: every weight is 1 and the covariance vanishes, so o = v."""
+    rng = np.random.default_rng(16)
+    q, rho, K, V = rand_row(rng, 1, 8, 8)
+    return rel_err(impl(q, rho, K, V, 0.3), V[0])
+
+
+PINS = [pin_hand_example, pin_two_tokens, pin_numpy_cov, pin_uniform_limit,
+        pin_softmax_at_rho_zero, pin_lla_intercept, pin_single_key]
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_oracle_meets_pin(form, pin):
+    assert pin(one_row(form)) < 1e-12
+
+
+# --------------------------------------------------- mistakes are caught ---
+
+def _parts(q, rho, K, V, scale):
+    p = scipy.special.softmax(scale * (K @ q))
+    return p, p @ V, p @ K
+
+
+def mut_sign(q, rho, K, V, scale):
+    p, vbar, kbar = _parts(q, rho, K, V, scale)
+    return vbar + ((V - vbar) * p[:, None]).T @ ((K - kbar) @ rho)
+
+
+def mut_dropped_mean_term(q, rho, K, V, scale):  # o = A/Z - B/Z (A R / Z^2 dropped)
+    p, vbar, _ = _parts(q, rho, K, V, scale)
+    return vbar - (p * (K @ rho)) @ V
+
+
+def mut_transposed(q, rho, K, V, scale):  # rho contracted on the value side
+    p, vbar, kbar = _parts(q, rho, K, V, scale)
+    C = ((V - vbar) * p[:, None]).T @ (K - kbar)
+    return vbar - C.T @ rho if C.shape[0] == C.shape[1] else vbar * np.nan
+
+
+def mut_scaled_probe(q, rho, K, V, scale):  # logit scale applied to t = rho.k too
+    p, vbar, kbar = _parts(q, rho, K, V, scale)
+    return vbar - ((V - vbar) * p[:, None]).T @ (scale * (K - kbar) @ rho)
+
+
+def mut_unweighted_cov(q, rho, K, V, scale):
+    p, vbar, _ = _parts(q, rho, K, V, scale)
+    C = np.cov(np.vstack([V.T, K.T]), bias=True)[:V.shape[1], V.shape[1]:]
+    return vbar - C @ rho
+
+
+def mut_bessel(q, rho, K, V, scale):  # reliability-weights correction 1/(1 - sum p^2)
+    p, vbar, kbar = _parts(q, rho, K, V, scale)
+    C = ((V - vbar) * p[:, None]).T @ (K - kbar) / (1.0 - np.sum(p * p))
+    return vbar - C @ rho
+
+
+def mut_uncentred(q, rho, K, V, scale):
+    p, vbar, _ = _parts(q, rho, K, V, scale)
+    return vbar - (V * p[:, None]).T @ (K @ rho)
+
+
+def mut_unnormalised_weights(q, rho, K, V, scale):  # exp(s) used without dividing by Z
+    s = scale * (K @ q)
+    e = np.exp(s - s.max())
+    vbar = e @ V / e.sum()
+    kbar = e @ K / e.sum()
+    return vbar - ((V - vbar) * e[:, None]).T @ ((K - kbar) @ rho)
+
+
+MUTANTS = [mut_sign, mut_dropped_mean_term, mut_transposed, mut_scaled_probe,
+           mut_unweighted_cov, mut_bessel, mut_uncentred, mut_unnormalised_weights]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
+def test_mutants_are_caught(mutant):
+    """Every plausible mistake in the definition fails at least one pin."""
+    failures = []
+    for pin in PINS:
+        with np.errstate(all="ignore"):
+            e = pin(mutant)
+        if not (e < 1e-9):
+            failures.append(pin.__name__)
+    assert failures, f"{mutant.__name__} passes every pin"
+
+
+# ------------------------------------------------- oracle self-consistency ---
+
+@pytest.mark.parametrize("L", [1, 2, 3, 7, 16, 33])
+@pytest.mark.parametrize("d", [1, 2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2])
+def test_streaming_equals_explicit(L, d, G):
+    rng = np.random.default_rng(1000 * L + 10 * d + G)
+    B, Hkv = 2, 2
+    q = rng.standard_normal((B, Hkv * G, d))
+    rho = 0.3 * rng.standard_normal((B, Hkv * G, d))
+    k = rng.standard_normal((B, Hkv, L, d))
+    v = rng.standard_normal((B, Hkv, L, d))
+    a = oracle.decode(q, rho, k, v, 0.6, form="explicit")
+    b = oracle.decode(q, rho, k, v, 0.6, form="streaming")
+    assert rel_err(b, a) < 1e-12
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_single_key_is_bitwise_value(form):
+    rng = np.random.default_rng(3)
+    q, rho, K, V = rand_row(rng, 1, 64, 64)
+    o = one_row(form)(q, rho, K, V, 0.125)
+    assert np.array_equal(o, V[0])
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_rho_zero_bitwise_in_explicit_form(form):
+    """With rho = 0 the correction is an exact zero, so o is the softmax mean."""
+    rng = np.random.default_rng(4)
+    q, _, K, V = rand_row(rng, 50, 8, 8)
+    o0 = one_row(form)(q, np.zeros(8), K, V, 0.3)
+    want = one_row("explicit")(q, np.zeros(8), K, V, 0.3)
+    assert rel_err(o0, want) < 1e-14
+
+
+def test_empty_row_is_zero():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 2, 4))
+    k = rng.standard_normal((3, 2, 6, 4))
+    v = rng.standard_normal((3, 2, 6, 4))
+    for form in FORMS:
+        o = oracle.decode(q, q, k, v, 0.5, seq_lens=np.array([6, 0, 3]), form=form)
+        assert np.all(o[1] == 0.0) and np.all(np.isfinite(o))
+
+
+def test_large_logits_do_not_overflow():
+    """Logits in the hundreds, and a max that grows at every token."""
+    rng = np.random.default_rng(6)
+    d, L = 4, 40
+    q = rng.standard_normal(d)
+    u = q / np.linalg.norm(q)
+    K = np.outer(np.arange(L), u) * 3.0 + 0.01 * rng.standard_normal((L, d))
+    V = rng.standard_normal((L, d))
+    rho = 0.2 * rng.standard_normal(d)
+    scale = 50.0
+    p = scipy.special.softmax(scale * (K @ q))
+    C = np.cov(np.vstack([V.T, K.T]), aweights=p, bias=True)[:d, d:]
+    want = p @ V - C @ rho
+    for form in FORMS:
+        o = one_row(form)(q, rho, K, V, scale)
+        assert np.all(np.isfinite(o)) and rel_err(o, want) < 1e-10
+
+
+def test_invariants():
+    """Algebra of the definition: value shift, key shift, rho-linearity, token order."""
+    rng = np.random.default_rng(7)
+    L, d = 25, 6
+    q, rho, K, V = rand_row(rng, L, d, d)
+    f = one_row("streaming")
+    s = 0.4
+    c = rng.standard_normal(d)
+    assert rel_err(f(q, rho, K, V + c, s), f(q, rho, K, V, s) + c) < 1e-12
+    assert rel_err(f(q, rho, K + 0.5 * c, V, s), f(q, rho, K, V, s)) < 1e-12
+    r2 = 0.3 * rng.standard_normal(d)
+    lhs = f(q, rho + r2, K, V, s) + f(q, np.zeros(d), K, V, s)
+    rhs = f(q, rho, K, V, s) + f(q, r2, K, V, s)
+    assert rel_err(lhs, rhs) < 1e-12
+    perm = rng.permutation(L)
+    assert rel_err(f(q, rho, K[perm], V[perm], s), f(q, rho, K, V, s)) < 1e-12
+
+
+def test_gqa_mapping_consecutive_groups():
+    """Query head h reads KV head h // (Hq / Hkv)."""
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, L, d = 2, 6, 2, 9, 4
+    q = rng.standard_normal((B, Hq, d))
+    rho = 0.3 * rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, L, d))
+    v = rng.standard_normal((B, Hkv, L, d))
+    o = oracle.decode(q, rho, k, v, 0.5)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            ref = one_row("explicit")(q[b, h], rho[b, h], k[b, h // G], v[b, h // G], 0.5)
+            assert rel_err(o[b, h], ref) < 1e-12
+
+
+def test_paged_equals_contiguous_gather():
+    """A shuffled page pool read through the block table equals the contiguous
+    cache assembled from it with numpy indexing; slots past seq_lens are NaN."""
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, d, P = 4, 4, 2, 8, 16
+    lens = np.array([1, 16, 17, 45], dtype=np.int32)
+    nblk = (lens + P - 1) // P
+    NB = int(nblk.sum())
+    perm = rng.permutation(NB)
+    maxb = int(nblk.max())
+    table = np.full((B, maxb), NB, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+    kp = rng.standard_normal((NB + 1, Hkv, P, d))
+    vp = rng.standard_normal((NB + 1, Hkv, P, d))
+    kp[NB] = np.nan
+    vp[NB] = np.nan
+    for b in range(B):
+        if lens[b] % P:
+            kp[table[b, lens[b] // P], :, lens[b] % P:] = np.nan
+            vp[table[b, lens[b] // P], :, lens[b] % P:] = np.nan
+    q = rng.standard_normal((B, Hq, d))
+    rho = 0.3 * rng.standard_normal((B, Hq, d))
+    Lcap = maxb * P
+    kc = np.zeros((B, Hkv, Lcap, d))
+    vc = np.zeros((B, Hkv, Lcap, d))
+    for b in range(B):
+        j = np.arange(lens[b])
+        kc[b, :, :lens[b]] = kp[table[b, j // P], :, j % P].transpose(1, 0, 2)
+        vc[b, :, :lens[b]] = vp[table[b, j // P], :, j % P].transpose(1, 0, 2)
+    for form in FORMS:
+        op = oracle.decode(q, rho, kp, vp, 0.35, seq_lens=lens, block_table=table, form=form)
+        oc = oracle.decode(q, rho, kc, vc, 0.35, seq_lens=lens, form=form)
+        assert np.all(np.isfinite(op))
+        assert np.array_equal(op, oc)
+
+
+def test_bf16_widening_is_exact():
+    rng = np.random.default_rng(10)
+    bits = (rng.integers(0, 1 << 16, size=(1, 2, 12, 8), dtype=np.uint32) & 0xBFFF).astype(np.uint16)
+    bits_v = (rng.integers(0, 1 << 16, size=(1, 2, 12, 8), dtype=np.uint32) & 0xBFFF).astype(np.uint16)
+    as_f32 = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    q = rng.standard_normal((1, 4, 8)).astype(np.float32)
+    rho = (0.1 * rng.standard_normal((1, 4, 8))).astype(np.float32)
+    a = oracle.decode(q, rho, bits, bits_v, 0.35)
+    b = oracle.decode(q, rho, as_f32(bits), as_f32(bits_v), 0.35)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- prefill ---
+
+def _prefill_case(seed, B=2, S=37, Hq=4, Hkv=2, d=8):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, S, Hq, d))
+    rho = 0.3 * rng.standard_normal((B, S, Hq, d))
+    k = rng.standard_normal((B, S, Hkv, d))
+    v = rng.standard_normal((B, S, Hkv, d))
+    return q, rho, k, v
+
+
+def test_prefill_row_is_decode_over_prefix():
+    q, rho, k, v = _prefill_case(20)
+    B, S, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    rows = np.array([0, 1, 5, 17, 36], dtype=np.int32)
+    for form in FORMS:
+        o = oracle.prefill(q, rho, k, v, 0.4, rows=rows, form=form)
+        for ri, i in enumerate(rows):
+            for b in range(B):
+                for h in range(Hq):
+                    ref = one_row("explicit")(q[b, i, h], rho[b, i, h], k[b, :i + 1, h // G],
+                                              v[b, :i + 1, h // G], 0.4)
+                    assert rel_err(o[b, ri, h], ref) < 1e-12
+
+
+def test_prefill_first_row_is_first_value():
+    q, rho, k, v = _prefill_case(21)
+    G = q.shape[2] // k.shape[2]
+    o = oracle.prefill(q, rho, k, v, 0.4, rows=[0])
+    for h in range(q.shape[2]):
+        assert np.array_equal(o[:, 0, h], v[:, 0, h // G])
+
+
+def test_prefill_rho_zero_is_causal_softmax():
+    q, _, k, v = _prefill_case(22)
+    B, S, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    o = oracle.prefill(q, np.zeros_like(q), k, v, 0.4)
+    mask = np.tril(np.ones((S, S), dtype=bool))
+    for b in range(B):
+        for h in range(Hq):
+            logits = 0.4 * q[b, :, h] @ k[b, :, h // G].T
+            p = scipy.special.softmax(np.where(mask, logits, -np.inf), axis=1)
+            assert rel_err(o[b, :, h], p @ v[b, :, h // G]) < 1e-12
+
+
+def test_prefill_uniform_limit():
+    q, rho, k, v = _prefill_case(23)
+    G = q.shape[2] // k.shape[2]
+    o = oracle.prefill(np.zeros_like(q), rho, k, v, 0.4, rows=[3, 20, 36])
+    for ri, i in enumerate([3, 20, 36]):
+        for h in range(q.shape[2]):
+            K, V = k[0, :i + 1, h // G], v[0, :i + 1, h // G]
+            C = np.cov(np.vstack([V.T, K.T]), bias=True)[:8, 8:]
+            assert rel_err(o[0, ri, h], V.mean(0) - C @ rho[0, i, h]) < 1e-12
