@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the Parallax attention hot path on one MI355X (gfx950).
+
+Default workload: decode, batch 8, 16 query / 8 KV heads, d = 128, 4096
+cached tokens per sequence, contiguous bf16 KV cache, fp32 q / rho / out.
+One step = one parallax_decode call (one kernel launch) over the whole batch.
+
+The KV cache is resident in HBM before timing starts.  To keep the 256 MB
+last-level cache from serving it, R copies of the inputs (R * KV >= 1 GiB)
+are rotated, step i using copy i % R.  Steps are timed with HIP events on the
+stream the kernels are launched on.
+
+Prints ONE JSON line.  Other workloads: --workload paged (256 sequences, ctx
+U[128, 32768], 16-token pages), prefill (batch 4, seq 8192, 16/8 heads),
+sweep (batch x ctx grid), copy (a plain device copy used to calibrate the
+HBM byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "Parallax decode KV GB/s (% of HBM peak) + tokens/s over batch×ctx sweep"
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "decode": ["parallax_local_linear_decode_amd/csrc/decode.hip",
+               "parallax_local_linear_decode_amd/csrc/kernels.hpp"],
+    "paged": ["parallax_local_linear_decode_amd/csrc/decode.hip",
+              "parallax_local_linear_decode_amd/csrc/kernels.hpp"],
+    "prefill": ["parallax_local_linear_decode_amd/csrc/prefill.hip",
+                "parallax_local_linear_decode_amd/csrc/kernels.hpp"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha(workload):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES.get(workload, []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload):
+    """HBM bytes per launch from committed counter runs, if they were taken on
+    the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha(workload):
+        return None
+    return float(t["bytes_per_launch"])
+
+
+# ------------------------------------------------------------------ decode ---
+
+def decode_bytes(B, Hq, Hkv, d, lens, kv_elem=2):
+    """Algorithmic bytes: every K and V element once, plus q, rho and out."""
+    return sum(lens) * Hkv * d * 2 * kv_elem + B * Hq * d * 4 * 3
+
+
+def time_launches(torch, launch, n_bufs, steps, warmup):
+    for i in range(warmup):
+        launch(i % n_bufs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        launch(i % n_bufs)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1000.0  # seconds
+
+
+def make_decode_launcher(torch, plx, sets, out, split):
+    """Pre-marshalled C-ABI calls, one per input copy, so the host loop is a
+    single ctypes call per step."""
+    import ctypes
+    lib = plx.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = []
+    for inp in sets:
+        a = plx._decode_args(inp.q, inp.rho, inp.k, inp.v, out, inp.scale, inp.seq_lens,
+                             inp.block_table, None, split)
+        n = ctypes.c_size_t(0)
+        st = lib.parallax_decode_workspace_size(ctypes.byref(a), ctypes.byref(n))
+        if st != 0:
+            plx._raise(st, lib)
+        ws = torch.zeros(max(n.value, 16), dtype=torch.uint8, device=out.device)
+        calls.append((a, ws))
+
+    def launch(i):
+        a, ws = calls[i]
+        st = lib.parallax_decode(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
+                                 ws.numel(), stream)
+        if st != 0:
+            plx._raise(st, lib)
+    return launch
+
+
+def cpu_baseline_decode(inp, nbytes, budget_s=12.0):
+    """The oracle (fp64 C, all host cores) on the same workload; repeated until
+    about budget_s of CPU time has passed."""
+    import oracle
+    from parallax_local_linear_decode_amd.workloads import host_array
+    import numpy as np
+    args = dict(q=host_array(inp.q), rho=host_array(inp.rho), k=host_array(inp.k),
+                v=host_array(inp.v))
+    sl = None if inp.seq_lens is None else host_array(inp.seq_lens).astype(np.int32)
+    bt = None if inp.block_table is None else host_array(inp.block_table)
+    threads = oracle.default_threads()
+    reps, elapsed, ref = 0, 0.0, None
+    while elapsed < budget_s and reps < 50:
+        t = time.perf_counter()
+        ref = oracle.decode(args["q"], args["rho"], args["k"], args["v"], inp.scale,
+                            seq_lens=sl, block_table=bt, threads=threads)
+        elapsed += time.perf_counter() - t
+        reps += 1
+    per = elapsed / reps
+    return ref, {"value": nbytes / per / 1e9, "unit": "GB/s", "cores": threads,
+                 "kind": "oracle", "seconds_per_step": per,
+                 "sample": f"the full workload, {reps} repetition(s), fp64 streaming form"}
+
+
+def run_decode(args, torch, plx):
+    from parallax_local_linear_decode_amd.workloads import decode_inputs
+    B, Hq, Hkv, d, L = args.batch, 16, 8, 128, args.ctx
+    dev = torch.device("cuda:0")
+    kv_bytes = B * Hkv * L * d * 2 * 2
+    n_bufs = max(1, math.ceil(args.cold_bytes / kv_bytes))
+    sets = [decode_inputs(B, Hq, Hkv, d, L, seed=i, device=dev) for i in range(n_bufs)]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    launch = make_decode_launcher(torch, plx, sets, out, args.split)
+    nbytes = decode_bytes(B, Hq, Hkv, d, [L] * B)
+
+    # parity gate on the data being timed (copy 0) before any number is reported
+    launch(0)
+    torch.cuda.synchronize()
+    gpu0 = out.double().cpu().numpy()
+    cpu = None
+    if args.cpu_baseline:
+        ref, cpu = cpu_baseline_decode(sets[0], nbytes)
+        gate(gpu0, ref, 2e-2, 1e-3)
+
+    secs = time_launches(torch, launch, n_bufs, args.steps, args.warmup)
+    per = secs / args.steps
+    warm = time_launches(torch, launch, 1, args.steps, args.warmup) / args.steps
+    gbps = nbytes / per / 1e9
+    traffic = traffic_for("decode")
+    return {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s",
+        "ms_per_step": per * 1e3, "dtype": "f32",
+        "config": {"workload": f"decode: batch {B}, 16 query / 8 KV heads, d 128, ctx {L}, "
+                               "contiguous bf16 KV cache, fp32 q/rho/out",
+                   "batch": B, "ctx": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": d, "kv_dtype": "bf16", "cold_copies": n_bufs,
+                   "split_tokens": args.split},
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": B / per, "kv_tokens_per_s": B * L / per,
+        "warm_cache_gbps": round(nbytes / warm / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_paged(args, torch, plx):
+    from parallax_local_linear_decode_amd.workloads import paged_inputs
+    import numpy as np
+    dev = torch.device("cuda:0")
+    inp = paged_inputs(256, 16, 8, 128, seed=0, rho_zero_rows=32, device=dev)
+    lens = inp.seq_lens.cpu().tolist()
+    out = torch.empty((256, 16, 128), dtype=torch.float32, device=dev)
+    launch = make_decode_launcher(torch, plx, [inp], out, args.split)
+    nbytes = decode_bytes(256, 16, 8, 128, lens) + sum((L + 15) // 16 for L in lens) * 4
+    launch(0)
+    torch.cuda.synchronize()
+    if not torch.isfinite(out).all():
+        raise SystemExit("paged: non-finite output")
+    secs = time_launches(torch, launch, 1, args.steps, args.warmup)
+    per = secs / args.steps
+    gbps = nbytes / per / 1e9
+    return {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": per * 1e3,
+        "dtype": "f32",
+        "config": {"workload": "paged decode: batch 256, 16 query / 8 KV heads, d 128, "
+                               "ctx U[128, 32768], 16-token pages, shuffled block table, bf16",
+                   "batch": 256, "total_tokens": int(sum(lens)), "kv_gb": nbytes / 1e9},
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": 256 / per, "kv_tokens_per_s": sum(lens) / per,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for("paged")},
+        "cpu_baseline": None,
+    }
+
+
+def run_sweep(args, torch, plx):
+    from parallax_local_linear_decode_amd.workloads import decode_inputs
+    dev = torch.device("cuda:0")
+    points = []
+    free = torch.cuda.mem_get_info()[0]
+    for B in (1, 16, 128, 1024, 2048):
+        for L in (128, 1024, 8192, 32768):
+            kv = B * 8 * L * 128 * 2 * 2
+            if kv > 200e9 or kv * 1.1 > free:
+                points.append({"batch": B, "ctx": L, "skipped": "KV above 200 GB or free HBM"})
+                continue
+            n_bufs = max(1, math.ceil(args.cold_bytes / kv))
+            sets = [decode_inputs(B, 16, 8, 128, L, seed=1000 + i, device=dev)
+                    for i in range(n_bufs)]
+            out = torch.empty((B, 16, 128), dtype=torch.float32, device=dev)
+            launch = make_decode_launcher(torch, plx, sets, out, 0)
+            steps = max(5, min(args.steps, int(2e9 / kv) + 5))
+            per = time_launches(torch, launch, n_bufs, steps, min(args.warmup, steps)) / steps
+            nbytes = decode_bytes(B, 16, 8, 128, [L] * B)
+            gbps = nbytes / per / 1e9
+            points.append({"batch": B, "ctx": L, "us": per * 1e6, "gbps": round(gbps, 1),
+                           "pct_hbm": round(100 * gbps / HBM_PEAK_GBPS, 1),
+                           "tokens_per_s": B / per})
+            log(json.dumps(points[-1]))
+            del sets, out, launch
+            torch.cuda.empty_cache()
+    best = max((p["gbps"] for p in points if "gbps" in p), default=0.0)
+    return {"metric": METRIC, "value": best, "unit": "GB/s", "ms_per_step": None,
+            "dtype": "f32", "config": {"workload": "decode sweep: batch x ctx grid, 16/8 heads, "
+                                                   "d 128, bf16 KV", "points": points},
+            "roofline": None, "cpu_baseline": None}
+
+
+def run_copy(args, torch, plx):
+    """A plain device-to-device copy of a known size, to calibrate counters."""
+    n = args.copy_bytes
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    secs = time_launches(torch, lambda i: b.copy_(a), 1, args.steps, args.warmup)
+    per = secs / args.steps
+    return {"metric": "device copy GB/s (read + write)", "value": 2 * n / per / 1e9,
+            "unit": "GB/s", "ms_per_step": per * 1e3, "dtype": "u8",
+            "config": {"workload": f"copy {n} bytes"}, "roofline": None, "cpu_baseline": None}
+
+
+def gate(gpu, ref, tau, rms):
+    import numpy as np
+    ratio = float(np.max(np.abs(gpu - ref) / (1 + np.abs(ref))))
+    r = float(np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300))
+    log(f"parity vs oracle: max err ratio {ratio:.3e}, rel-RMS {r:.3e}")
+    if not (ratio <= tau and r <= rms) or not np.all(np.isfinite(gpu)):
+        raise SystemExit(f"parity gate failed (ratio {ratio:.3e}, rel-RMS {r:.3e})")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "paged", "prefill", "sweep", "copy"])
+    ap.add_argument("--batch", type=int, default=8)
+    ap.add_argument("--ctx", type=int, default=4096)
+    ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
+    ap.add_argument("--cold-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if "RANK" in os.environ and os.environ.get("WORLD_SIZE", "1") != "1":
+        print("bench.py runs as a single process on one GPU", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    sys.path.insert(0, ROOT)
+    import parallax_local_linear_decode_amd as plx
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    plx.load_library()
+    runner = {"decode": run_decode, "paged": run_paged, "sweep": run_sweep,
+              "copy": run_copy}.get(args.workload)
+    if runner is None:
+        raise SystemExit(f"workload {args.workload} is not available")
+    rec = runner(args, torch, plx)
+    line = {"metric": rec["metric"], "value": rec["value"], "unit": rec["unit"], "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": rec["dtype"], "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1^2) rho)",
+            "config": rec["config"]}
+    for k in ("pct_hbm_peak", "tokens_per_s", "kv_tokens_per_s", "warm_cache_gbps",
+              "mfma_util"):
+        if k in rec:
+            line[k] = rec[k]
+    line["roofline"] = rec["roofline"]
+    line["cpu_baseline"] = rec["cpu_baseline"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

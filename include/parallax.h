@@ -1,0 +1,174 @@
+/*
+ * parallax.h -- C ABI of libparallax: Parallax attention on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (page "Parallax: Parameterized Local Linear Attention Gives
+ * Transformers a 'Second Eye'", section 1.3, and the formula quoted at its
+ * top): for each query row with query q, probe rho and the keys k_j / values
+ * v_j it attends to,
+ *
+ *     s_j  = scale * (q . k_j),   p_j = softmax(s)_j,   t_j = rho . k_j
+ *     o_SA = sum_j p_j v_j
+ *     S_KV = sum_j p_j (v_j - vbar)(k_j - kbar)^T      (weighted covariance of K and V)
+ *     o    = o_SA - S_KV rho
+ *
+ * which one pass over the cache evaluates through Z = sum e^{s_j},
+ * R = sum e^{s_j} t_j, A = sum e^{s_j} v_j, B = sum e^{s_j} t_j v_j as
+ * o = A/Z - B/Z + A R / Z^2.  The keys and values are read once and serve both
+ * the softmax branch and the covariance branch (page "Parallax keeps softmax,
+ * adds covariance correction branch", second paragraph).  rho is an input:
+ * in the model it is a learned projection W_R x of the layer input (page
+ * "Parallax: Parameterized Local Linear Attention...", section 1.3); W_R = 0
+ * gives plain softmax attention.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or synchronises.
+ *   - Strides are in ELEMENTS of the tensor's own type; the last (head-dim)
+ *     axis is always contiguous.
+ *   - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream).  A status of PARALLAX_OK means the work was enqueued.
+ *   - All argument checks run on the host before any HIP call; on error
+ *     nothing is launched and no memory is touched.  parallax_last_error()
+ *     then describes the failure (thread-local).
+ *   - Grouped-query attention: query head h reads KV head h / (Hq / Hkv).
+ *   - Supported head dims: 64 and 128 (d_k = d_v = head_dim).
+ *   - Every key/value/query/probe/output row, and every pointer, must be
+ *     16-byte aligned (strides times element size multiples of 16 bytes);
+ *     otherwise PARALLAX_ERR_UNSUPPORTED.
+ */
+#ifndef PARALLAX_H
+#define PARALLAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PARALLAX_ABI_VERSION 1
+
+typedef enum {
+    PARALLAX_OK = 0,
+    PARALLAX_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes */
+    PARALLAX_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype, alignment) */
+    PARALLAX_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    PARALLAX_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} parallax_status_t;
+
+typedef enum { PARALLAX_F32 = 0, PARALLAX_BF16 = 1 } parallax_dtype_t;
+
+/* ------------------------------------------------------------- decode --- */
+/*
+ * Decode: one query row per (batch b, query head h), attending to every
+ * cached token 0 .. L_b-1 of its KV head (the cache already holds the
+ * current token).  L_b = seq_lens[b] if seq_lens is given, else max_seq_len.
+ * A row with L_b = 0 yields o = 0.
+ *
+ * Cache layouts (`kv_dtype` elements; k and v each have their own strides):
+ *   contiguous (block_table == NULL): token j of (b, hk) at
+ *       k + b*k_stride_0 + hk*k_stride_h + j*k_stride_t
+ *     with L_b <= max_seq_len <= the cache capacity (not checked on device).
+ *   paged (block_table != NULL): token j lives in physical page
+ *       pg = block_table[b*max_blocks_per_seq + j/block_size], slot j%block_size:
+ *       k + pg*k_stride_0 + hk*k_stride_h + slot*k_stride_t
+ *     block_size must be 16.  seq_lens is required; the caller guarantees
+ *     0 <= seq_lens[b] <= max_blocks_per_seq*16 and valid page ids.  Entries
+ *     of block_table past a sequence's last block are never read, nor are
+ *     slots past its last token.
+ *
+ * Inputs: q, rho fp32 [B, Hq, d] (strides q_stride_b, q_stride_h ...);
+ * output out fp32 [B, Hq, d].  Arithmetic: fp32 accumulation; bf16 keys
+ * meet q and rho through two-term (hi + lo) bf16 splits of q and rho.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(parallax_decode_args_t) */
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    float scale; /* logit scale, usually 1/sqrt(head_dim) */
+
+    const float *q;
+    int64_t q_stride_b, q_stride_h;
+    const float *rho;
+    int64_t rho_stride_b, rho_stride_h;
+    float *out;
+    int64_t out_stride_b, out_stride_h;
+
+    int32_t kv_dtype; /* parallax_dtype_t */
+    const void *k;
+    int64_t k_stride_0, k_stride_h, k_stride_t;
+    const void *v;
+    int64_t v_stride_0, v_stride_h, v_stride_t;
+
+    const int32_t *seq_lens; /* [B] device, or NULL */
+    int32_t max_seq_len;     /* >= every seq_lens[b]; >= 1 */
+
+    const int32_t *block_table; /* [B, max_blocks_per_seq] device, or NULL */
+    int32_t block_size;
+    int32_t max_blocks_per_seq;
+
+    int32_t split_tokens; /* tokens per context split; 0 = chosen by the library,
+                             else a positive multiple of 64 */
+} parallax_decode_args_t;
+
+/*
+ * Bytes of device workspace parallax_decode needs for these arguments
+ * (written to *bytes; 0 when one split covers every sequence).  The
+ * workspace holds per-split partial sums and one arrival counter per
+ * (batch, KV head).  It must be zero-filled before its first use; every
+ * completed call leaves it zero-filled again, so it can be reused by later
+ * calls on the same stream.  Two calls that run concurrently need separate
+ * workspaces.
+ */
+parallax_status_t parallax_decode_workspace_size(const parallax_decode_args_t *args,
+                                                 size_t *bytes);
+
+/* Enqueue a decode.  workspace may be NULL only if the required size is 0. */
+parallax_status_t parallax_decode(const parallax_decode_args_t *args, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------ prefill --- */
+/*
+ * Causal prefill: row i of (b, h) attends to keys 0..i of KV head
+ * h / (Hq/Hkv).  q, rho bf16 [B, S, Hq, d]; k, v bf16 [B, S, Hkv, d];
+ * out fp32 [B, S, Hq, d].  causal must be 1.  Products run on the bf16
+ * matrix cores with fp32 accumulation; the softmax numerators e^{s} and
+ * e^{s} t are rounded to bf16 before they multiply V.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(parallax_prefill_args_t) */
+    int32_t batch;
+    int32_t seq_len;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    float scale;
+    int32_t causal;
+
+    const void *q;
+    int64_t q_stride_b, q_stride_s, q_stride_h;
+    const void *rho;
+    int64_t rho_stride_b, rho_stride_s, rho_stride_h;
+    const void *k;
+    int64_t k_stride_b, k_stride_s, k_stride_h;
+    const void *v;
+    int64_t v_stride_b, v_stride_s, v_stride_h;
+    float *out;
+    int64_t out_stride_b, out_stride_s, out_stride_h;
+} parallax_prefill_args_t;
+
+parallax_status_t parallax_prefill(const parallax_prefill_args_t *args, void *hip_stream);
+
+/* ------------------------------------------------------------- misc --- */
+const char *parallax_status_string(parallax_status_t status);
+const char *parallax_last_error(void); /* detail of this thread's last non-OK status */
+int parallax_abi_version(void);        /* PARALLAX_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARALLAX_H */

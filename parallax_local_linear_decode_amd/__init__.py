@@ -1,0 +1,266 @@
+"""Python binding of libparallax (Parallax attention on MI355X / gfx950).
+
+The functions here carry the names of the C entry points in
+``include/parallax.h`` and do argument marshalling only: torch tensors become
+device pointers, element strides and the current HIP stream, and non-OK
+statuses become exceptions.  Every step of the computation runs in the HIP
+kernels of ``libparallax.so``; there is no fallback.  If the library is not
+built, every call raises.
+
+Operation (page "Parallax: Parameterized Local Linear Attention Gives
+Transformers a 'Second Eye'", section 1.3): o = o_SA - S_KV rho, softmax
+attention minus the softmax-weighted key/value covariance applied to the
+per-query probe rho.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libparallax.so")
+
+PARALLAX_OK = 0
+PARALLAX_ERR_INVALID_ARG = 1
+PARALLAX_ERR_UNSUPPORTED = 2
+PARALLAX_ERR_WORKSPACE = 3
+PARALLAX_ERR_HIP = 4
+PARALLAX_F32 = 0
+PARALLAX_BF16 = 1
+ABI_VERSION = 1
+
+_i32, _i64, _u32, _f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float,
+                               ctypes.c_void_p)
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of parallax_decode_args_t."""
+    _fields_ = [
+        ("struct_size", _u32), ("batch", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
+        ("head_dim", _i32), ("scale", _f32),
+        ("q", _vp), ("q_stride_b", _i64), ("q_stride_h", _i64),
+        ("rho", _vp), ("rho_stride_b", _i64), ("rho_stride_h", _i64),
+        ("out", _vp), ("out_stride_b", _i64), ("out_stride_h", _i64),
+        ("kv_dtype", _i32),
+        ("k", _vp), ("k_stride_0", _i64), ("k_stride_h", _i64), ("k_stride_t", _i64),
+        ("v", _vp), ("v_stride_0", _i64), ("v_stride_h", _i64), ("v_stride_t", _i64),
+        ("seq_lens", _vp), ("max_seq_len", _i32),
+        ("block_table", _vp), ("block_size", _i32), ("max_blocks_per_seq", _i32),
+        ("split_tokens", _i32),
+    ]
+
+
+class PrefillArgs(ctypes.Structure):
+    """Mirror of parallax_prefill_args_t."""
+    _fields_ = [
+        ("struct_size", _u32), ("batch", _i32), ("seq_len", _i32), ("num_q_heads", _i32),
+        ("num_kv_heads", _i32), ("head_dim", _i32), ("scale", _f32), ("causal", _i32),
+        ("q", _vp), ("q_stride_b", _i64), ("q_stride_s", _i64), ("q_stride_h", _i64),
+        ("rho", _vp), ("rho_stride_b", _i64), ("rho_stride_s", _i64), ("rho_stride_h", _i64),
+        ("k", _vp), ("k_stride_b", _i64), ("k_stride_s", _i64), ("k_stride_h", _i64),
+        ("v", _vp), ("v_stride_b", _i64), ("v_stride_s", _i64), ("v_stride_h", _i64),
+        ("out", _vp), ("out_stride_b", _i64), ("out_stride_s", _i64), ("out_stride_h", _i64),
+    ]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libparallax.so (built by ``python -m parallax_local_linear_decode_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libparallax.so is not built ({LIB_PATH}); run "
+                           "`python -m parallax_local_linear_decode_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.parallax_abi_version.restype = ctypes.c_int
+    lib.parallax_status_string.restype = ctypes.c_char_p
+    lib.parallax_status_string.argtypes = [ctypes.c_int]
+    lib.parallax_last_error.restype = ctypes.c_char_p
+    lib.parallax_decode_workspace_size.restype = ctypes.c_int
+    lib.parallax_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeArgs),
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+    lib.parallax_decode.restype = ctypes.c_int
+    lib.parallax_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
+    lib.parallax_prefill.restype = ctypes.c_int
+    lib.parallax_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
+    if lib.parallax_abi_version() != ABI_VERSION:
+        raise RuntimeError("libparallax ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+class ParallaxError(RuntimeError):
+    pass
+
+
+def _raise(status: int, lib) -> None:
+    msg = f"{lib.parallax_status_string(status).decode()}: {lib.parallax_last_error().decode()}"
+    if status == PARALLAX_ERR_INVALID_ARG:
+        raise ValueError(msg)
+    if status == PARALLAX_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise ParallaxError(msg)
+
+
+def parallax_abi_version() -> int:
+    return load_library().parallax_abi_version()
+
+
+def parallax_status_string(status: int) -> str:
+    return load_library().parallax_status_string(status).decode()
+
+
+def parallax_last_error() -> str:
+    return load_library().parallax_last_error().decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(t: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _decode_args(q, rho, k, v, out, scale, seq_lens, block_table, max_seq_len, split_tokens):
+    if q.dim() != 3 or rho.shape != q.shape:
+        raise ValueError("q and rho must be [B, Hq, d] of the same shape")
+    if q.dtype != torch.float32 or rho.dtype != torch.float32 or out.dtype != torch.float32:
+        raise TypeError("q, rho and out must be float32")
+    if k.dtype != v.dtype or k.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("k and v must both be float32 or both bfloat16")
+    if k.dim() != 4 or v.dim() != 4:
+        raise ValueError("k and v must be 4-d ([B, Hkv, L, d] or [pages, Hkv, 16, d])")
+    for name, t in (("q", q), ("rho", rho), ("out", out), ("k", k), ("v", v)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: the head-dim axis must be contiguous")
+    B, Hq, d = q.shape
+    paged = block_table is not None
+    if max_seq_len is None:
+        if paged:
+            max_seq_len = block_table.shape[1] * k.shape[2]
+        else:
+            max_seq_len = k.shape[2]
+    a = DecodeArgs()
+    a.struct_size = ctypes.sizeof(DecodeArgs)
+    a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim = B, Hq, k.shape[1], d
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d))
+    a.q, a.q_stride_b, a.q_stride_h = _ptr(q), q.stride(0), q.stride(1)
+    a.rho, a.rho_stride_b, a.rho_stride_h = _ptr(rho), rho.stride(0), rho.stride(1)
+    a.out, a.out_stride_b, a.out_stride_h = _ptr(out), out.stride(0), out.stride(1)
+    a.kv_dtype = PARALLAX_BF16 if k.dtype == torch.bfloat16 else PARALLAX_F32
+    a.k, a.k_stride_0, a.k_stride_h, a.k_stride_t = _ptr(k), k.stride(0), k.stride(1), k.stride(2)
+    a.v, a.v_stride_0, a.v_stride_h, a.v_stride_t = _ptr(v), v.stride(0), v.stride(1), v.stride(2)
+    if seq_lens is not None:
+        if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_contiguous():
+            raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    a.seq_lens = _ptr(seq_lens)
+    a.max_seq_len = int(max_seq_len)
+    if paged:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or \
+                block_table.shape[0] != B or not block_table.is_contiguous():
+            raise ValueError("block_table must be a contiguous int32 [B, max_blocks] tensor")
+        a.block_table = _ptr(block_table)
+        a.block_size = k.shape[2]
+        a.max_blocks_per_seq = block_table.shape[1]
+    a.split_tokens = int(split_tokens)
+    return a
+
+
+_workspaces: dict = {}
+
+
+def _workspace(device, stream, nbytes):
+    """A zero-filled workspace per (device, stream), grown on demand.  The
+    decode kernel leaves it zero-filled, so it is reused across calls."""
+    key = (str(device), stream.value)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def parallax_decode_workspace_size(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None,
+                                   max_seq_len=None, split_tokens=0) -> int:
+    """Bytes of workspace parallax_decode needs for these tensors."""
+    lib = load_library()
+    # The size depends on shapes only; q stands in for the output tensor.
+    a = _decode_args(q, rho, k, v, q, scale, seq_lens, block_table, max_seq_len, split_tokens)
+    nbytes = ctypes.c_size_t(0)
+    st = lib.parallax_decode_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    return nbytes.value
+
+
+def parallax_decode(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None,
+                    max_seq_len=None, out=None, workspace=None, split_tokens=0, stream=None):
+    """Parallax decode over a contiguous ([B, Hkv, L, d]) or paged
+    ([pages, Hkv, 16, d] + block_table [B, max_blocks]) KV cache.
+
+    q, rho: float32 [B, Hq, d]; k, v: bfloat16 or float32; seq_lens int32 [B]
+    (required when paged).  Returns out float32 [B, Hq, d].  `workspace`, if
+    given, is a zero-initialised uint8 device tensor of at least
+    parallax_decode_workspace_size(...) bytes.
+    """
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    a = _decode_args(q, rho, k, v, out, scale, seq_lens, block_table, max_seq_len, split_tokens)
+    nbytes = ctypes.c_size_t(0)
+    st = lib.parallax_decode_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    s = _stream_handle(q, stream)
+    if workspace is None and nbytes.value > 0:
+        workspace = _workspace(q.device, s, nbytes.value)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.parallax_decode(ctypes.byref(a), ws_ptr, ws_bytes, s)
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    return out
+
+
+def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, stream=None):
+    """Causal Parallax prefill.  q, rho bf16 [B, S, Hq, d]; k, v bf16
+    [B, S, Hkv, d].  Returns out float32 [B, S, Hq, d]."""
+    lib = load_library()
+    for name, t in (("q", q), ("rho", rho), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a 4-d bfloat16 tensor with contiguous head dim")
+    B, S, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, S, Hq, d), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.stride(-1) != 1:
+        raise ValueError("out must be float32 with a contiguous head dim")
+    a = PrefillArgs()
+    a.struct_size = ctypes.sizeof(PrefillArgs)
+    a.batch, a.seq_len, a.num_q_heads, a.num_kv_heads, a.head_dim = B, S, Hq, k.shape[2], d
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d))
+    a.causal = 1 if causal else 0
+    a.q, a.q_stride_b, a.q_stride_s, a.q_stride_h = _ptr(q), *q.stride()[:3]
+    a.rho, a.rho_stride_b, a.rho_stride_s, a.rho_stride_h = _ptr(rho), *rho.stride()[:3]
+    a.k, a.k_stride_b, a.k_stride_s, a.k_stride_h = _ptr(k), *k.stride()[:3]
+    a.v, a.v_stride_b, a.v_stride_s, a.v_stride_h = _ptr(v), *v.stride()[:3]
+    a.out, a.out_stride_b, a.out_stride_s, a.out_stride_h = _ptr(out), *out.stride()[:3]
+    st = lib.parallax_prefill(ctypes.byref(a), _stream_handle(q, stream))
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    return out
+
+
+__all__ = [
+    "parallax_decode", "parallax_decode_workspace_size", "parallax_prefill",
+    "parallax_status_string", "parallax_last_error", "parallax_abi_version", "load_library",
+    "DecodeArgs", "PrefillArgs", "ParallaxError",
+]

@@ -1,0 +1,282 @@
+// api.hip -- the C ABI of libparallax (declared in include/parallax.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so argument errors are reported (and testable) on machines
+// without a GPU.  Nothing runs at load time.
+#include "parallax.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kernels.hpp"
+
+#define PLX_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+parallax_status_t fail(parallax_status_t s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool bytes16(int64_t stride_elems, int64_t elem_size) {
+    return ((stride_elems * elem_size) & 15) == 0;
+}
+
+constexpr int64_t kTargetWorkgroups = 2048;  // 8 per CU on a 256-CU MI355X
+constexpr int kSplitQuantum = plx::kDecodeWaves * plx::kDecodeStepTokens;  // 64 tokens
+
+struct DecodePlan {
+    int group;
+    bool paged;
+    int split;
+    int nsplit;
+    size_t counters_bytes;
+    size_t workspace_bytes;
+};
+
+int round_up(int64_t x, int64_t q) { return (int)(((x + q - 1) / q) * q); }
+
+// Context split: long rows get at least ~16 splits (so rows of very
+// different lengths balance), and the grid gets at least kTargetWorkgroups
+// workgroups while splits stay >= 128 tokens.
+int choose_split(int64_t units, int max_len) {
+    int64_t split = round_up((max_len + 15) / 16, kSplitQuantum);
+    if (split < 256) split = 256;
+    while (split > 128 && units * ((max_len + split - 1) / split) < kTargetWorkgroups)
+        split = round_up(split / 2, kSplitQuantum);
+    if (split > max_len) split = round_up(max_len, kSplitQuantum);
+    return (int)split;
+}
+
+parallax_status_t plan_decode(const parallax_decode_args_t *a, DecodePlan *pl) {
+    if (a == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "decode: args is NULL");
+    if (a->struct_size != sizeof(parallax_decode_args_t))
+        return fail(PARALLAX_ERR_INVALID_ARG, "decode: struct_size %u, expected %zu",
+                    a->struct_size, sizeof(parallax_decode_args_t));
+    if (a->batch < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+        return fail(PARALLAX_ERR_INVALID_ARG, "decode: batch and head counts must be >= 1");
+    if (a->num_q_heads % a->num_kv_heads != 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "decode: num_q_heads %% num_kv_heads != 0");
+    const int group = a->num_q_heads / a->num_kv_heads;
+    if (a->head_dim < 1) return fail(PARALLAX_ERR_INVALID_ARG, "decode: head_dim must be >= 1");
+    if (a->kv_dtype != PARALLAX_F32 && a->kv_dtype != PARALLAX_BF16)
+        return fail(PARALLAX_ERR_INVALID_ARG, "decode: unknown kv_dtype %d", a->kv_dtype);
+    if (!isfinite(a->scale)) return fail(PARALLAX_ERR_INVALID_ARG, "decode: scale is not finite");
+    if (!a->q || !a->rho || !a->out || !a->k || !a->v)
+        return fail(PARALLAX_ERR_INVALID_ARG, "decode: q, rho, out, k and v must be non-NULL");
+    if (a->max_seq_len < 1) return fail(PARALLAX_ERR_INVALID_ARG, "decode: max_seq_len must be >= 1");
+    if (a->q_stride_b < 0 || a->q_stride_h < 0 || a->rho_stride_b < 0 || a->rho_stride_h < 0 ||
+        a->out_stride_b < 0 || a->out_stride_h < 0 || a->k_stride_0 < 0 || a->k_stride_h < 0 ||
+        a->k_stride_t < 0 || a->v_stride_0 < 0 || a->v_stride_h < 0 || a->v_stride_t < 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "decode: strides must be non-negative");
+    if (a->split_tokens < 0 || (a->split_tokens > 0 && a->split_tokens % kSplitQuantum != 0))
+        return fail(PARALLAX_ERR_INVALID_ARG, "decode: split_tokens must be 0 or a multiple of %d",
+                    kSplitQuantum);
+    const bool paged = a->block_table != nullptr;
+    if (paged) {
+        if (a->seq_lens == nullptr)
+            return fail(PARALLAX_ERR_INVALID_ARG, "decode: a paged cache needs seq_lens");
+        if (a->max_blocks_per_seq < 1)
+            return fail(PARALLAX_ERR_INVALID_ARG, "decode: max_blocks_per_seq must be >= 1");
+        if (a->block_size != plx::kDecodeStepTokens)
+            return fail(PARALLAX_ERR_UNSUPPORTED, "decode: block_size %d (only 16 is supported)",
+                        a->block_size);
+        if ((int64_t)a->max_seq_len > (int64_t)a->max_blocks_per_seq * a->block_size)
+            return fail(PARALLAX_ERR_INVALID_ARG,
+                        "decode: max_seq_len exceeds max_blocks_per_seq * block_size");
+    }
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "decode: head_dim %d (supported: 64, 128)",
+                    a->head_dim);
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "decode: GQA group %d (supported: 1, 2, 4, 8)",
+                    group);
+    const int64_t kv_es = a->kv_dtype == PARALLAX_BF16 ? 2 : 4;
+    if (!aligned16(a->q) || !aligned16(a->rho) || !aligned16(a->out) || !aligned16(a->k) ||
+        !aligned16(a->v))
+        return fail(PARALLAX_ERR_UNSUPPORTED, "decode: every pointer must be 16-byte aligned");
+    if (!bytes16(a->q_stride_b, 4) || !bytes16(a->q_stride_h, 4) || !bytes16(a->rho_stride_b, 4) ||
+        !bytes16(a->rho_stride_h, 4) || !bytes16(a->out_stride_b, 4) ||
+        !bytes16(a->out_stride_h, 4) || !bytes16(a->k_stride_0, kv_es) ||
+        !bytes16(a->k_stride_h, kv_es) || !bytes16(a->k_stride_t, kv_es) ||
+        !bytes16(a->v_stride_0, kv_es) || !bytes16(a->v_stride_h, kv_es) ||
+        !bytes16(a->v_stride_t, kv_es))
+        return fail(PARALLAX_ERR_UNSUPPORTED, "decode: every stride must span a multiple of 16 bytes");
+
+    const int64_t units = (int64_t)a->batch * a->num_kv_heads;
+    int split = a->split_tokens > 0 ? a->split_tokens : choose_split(units, a->max_seq_len);
+    int nsplit = (a->max_seq_len + split - 1) / split;
+    if (units * nsplit > 0x7fffffffLL)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "decode: grid too large (%lld workgroups)",
+                    (long long)(units * nsplit));
+    pl->group = group;
+    pl->paged = paged;
+    pl->split = split;
+    pl->nsplit = nsplit;
+    if (nsplit > 1) {
+        pl->counters_bytes = (size_t)round_up(units * 4, 256);
+        pl->workspace_bytes = pl->counters_bytes + (size_t)units * nsplit * group *
+                                                       plx::partial_floats(a->head_dim) * 4;
+    } else {
+        pl->counters_bytes = 0;
+        pl->workspace_bytes = 0;
+    }
+    return PARALLAX_OK;
+}
+
+parallax_status_t check_prefill(const parallax_prefill_args_t *a) {
+    if (a == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "prefill: args is NULL");
+    if (a->struct_size != sizeof(parallax_prefill_args_t))
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill: struct_size %u, expected %zu",
+                    a->struct_size, sizeof(parallax_prefill_args_t));
+    if (a->batch < 1 || a->seq_len < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill: batch, seq_len and head counts must be >= 1");
+    if (a->num_q_heads % a->num_kv_heads != 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill: num_q_heads %% num_kv_heads != 0");
+    if (!isfinite(a->scale)) return fail(PARALLAX_ERR_INVALID_ARG, "prefill: scale is not finite");
+    if (!a->q || !a->rho || !a->k || !a->v || !a->out)
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill: q, rho, k, v and out must be non-NULL");
+    const int64_t strides[] = {a->q_stride_b, a->q_stride_s, a->q_stride_h, a->rho_stride_b,
+                               a->rho_stride_s, a->rho_stride_h, a->k_stride_b, a->k_stride_s,
+                               a->k_stride_h, a->v_stride_b, a->v_stride_s, a->v_stride_h,
+                               a->out_stride_b, a->out_stride_s, a->out_stride_h};
+    for (int64_t s : strides)
+        if (s < 0) return fail(PARALLAX_ERR_INVALID_ARG, "prefill: strides must be non-negative");
+    if (a->causal != 1)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: only causal = 1 is supported");
+    if (a->head_dim != 128)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 128)", a->head_dim);
+    if (!aligned16(a->q) || !aligned16(a->rho) || !aligned16(a->k) || !aligned16(a->v) ||
+        !aligned16(a->out))
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: every pointer must be 16-byte aligned");
+    for (int i = 0; i < 12; ++i)
+        if (!bytes16(strides[i], 2))
+            return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: strides must span multiples of 16 bytes");
+    for (int i = 12; i < 15; ++i)
+        if (!bytes16(strides[i], 4))
+            return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: strides must span multiples of 16 bytes");
+    return PARALLAX_OK;
+}
+
+parallax_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return PARALLAX_OK;
+    return fail(PARALLAX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+PLX_EXPORT int parallax_abi_version(void) { return PARALLAX_ABI_VERSION; }
+
+PLX_EXPORT const char *parallax_status_string(parallax_status_t s) {
+    switch (s) {
+        case PARALLAX_OK: return "PARALLAX_OK";
+        case PARALLAX_ERR_INVALID_ARG: return "PARALLAX_ERR_INVALID_ARG";
+        case PARALLAX_ERR_UNSUPPORTED: return "PARALLAX_ERR_UNSUPPORTED";
+        case PARALLAX_ERR_WORKSPACE: return "PARALLAX_ERR_WORKSPACE";
+        case PARALLAX_ERR_HIP: return "PARALLAX_ERR_HIP";
+    }
+    return "PARALLAX_ERR_UNKNOWN";
+}
+
+PLX_EXPORT const char *parallax_last_error(void) { return g_last_error; }
+
+PLX_EXPORT parallax_status_t parallax_decode_workspace_size(const parallax_decode_args_t *args,
+                                                            size_t *bytes) {
+    if (bytes == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "decode: bytes is NULL");
+    DecodePlan pl;
+    parallax_status_t s = plan_decode(args, &pl);
+    if (s != PARALLAX_OK) return s;
+    *bytes = pl.workspace_bytes;
+    return PARALLAX_OK;
+}
+
+PLX_EXPORT parallax_status_t parallax_decode(const parallax_decode_args_t *a, void *workspace,
+                                             size_t workspace_bytes, void *hip_stream) {
+    DecodePlan pl;
+    parallax_status_t s = plan_decode(a, &pl);
+    if (s != PARALLAX_OK) return s;
+    if (pl.workspace_bytes > 0) {
+        if (workspace == nullptr || workspace_bytes < pl.workspace_bytes)
+            return fail(PARALLAX_ERR_WORKSPACE, "decode: workspace of %zu bytes needed, %zu given",
+                        pl.workspace_bytes, workspace == nullptr ? (size_t)0 : workspace_bytes);
+        if (!aligned16(workspace))
+            return fail(PARALLAX_ERR_WORKSPACE, "decode: workspace must be 16-byte aligned");
+    }
+    plx::DecodeParams p;
+    p.q = a->q;
+    p.rho = a->rho;
+    p.out = a->out;
+    p.q_sb = a->q_stride_b;
+    p.q_sh = a->q_stride_h;
+    p.rho_sb = a->rho_stride_b;
+    p.rho_sh = a->rho_stride_h;
+    p.out_sb = a->out_stride_b;
+    p.out_sh = a->out_stride_h;
+    p.k = a->k;
+    p.v = a->v;
+    p.k_s0 = a->k_stride_0;
+    p.k_sh = a->k_stride_h;
+    p.k_st = a->k_stride_t;
+    p.v_s0 = a->v_stride_0;
+    p.v_sh = a->v_stride_h;
+    p.v_st = a->v_stride_t;
+    p.seq_lens = a->seq_lens;
+    p.block_table = a->block_table;
+    p.max_seq_len = a->max_seq_len;
+    p.max_blocks = pl.paged ? a->max_blocks_per_seq : 0;
+    p.num_kv_heads = a->num_kv_heads;
+    p.split = pl.split;
+    p.nsplit = pl.nsplit;
+    p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
+    if (pl.workspace_bytes > 0) {
+        p.counters = static_cast<uint32_t *>(workspace);
+        p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.counters_bytes);
+    } else {
+        p.counters = nullptr;
+        p.partials = nullptr;
+    }
+    return hip_status(plx::launch_decode(p, a->kv_dtype, a->head_dim, pl.group, pl.paged, a->batch,
+                                         static_cast<hipStream_t>(hip_stream)),
+                      "decode launch");
+}
+
+PLX_EXPORT parallax_status_t parallax_prefill(const parallax_prefill_args_t *a, void *hip_stream) {
+    parallax_status_t s = check_prefill(a);
+    if (s != PARALLAX_OK) return s;
+    plx::PrefillParams p;
+    p.q = static_cast<const uint16_t *>(a->q);
+    p.rho = static_cast<const uint16_t *>(a->rho);
+    p.k = static_cast<const uint16_t *>(a->k);
+    p.v = static_cast<const uint16_t *>(a->v);
+    p.out = a->out;
+    p.q_sb = a->q_stride_b;
+    p.q_ss = a->q_stride_s;
+    p.q_sh = a->q_stride_h;
+    p.r_sb = a->rho_stride_b;
+    p.r_ss = a->rho_stride_s;
+    p.r_sh = a->rho_stride_h;
+    p.k_sb = a->k_stride_b;
+    p.k_ss = a->k_stride_s;
+    p.k_sh = a->k_stride_h;
+    p.v_sb = a->v_stride_b;
+    p.v_ss = a->v_stride_s;
+    p.v_sh = a->v_stride_h;
+    p.o_sb = a->out_stride_b;
+    p.o_ss = a->out_stride_s;
+    p.o_sh = a->out_stride_h;
+    p.batch = a->batch;
+    p.seq_len = a->seq_len;
+    p.num_q_heads = a->num_q_heads;
+    p.num_kv_heads = a->num_kv_heads;
+    p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
+    return hip_status(plx::launch_prefill(p, a->head_dim, static_cast<hipStream_t>(hip_stream)),
+                      "prefill launch");
+}

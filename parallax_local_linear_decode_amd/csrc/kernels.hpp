@@ -1,0 +1,62 @@
+// Internal launch parameters shared by the host dispatcher (api.hip) and the
+// gfx950 kernels (decode.hip, prefill.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace plx {
+
+// Number of floats in one split's partial record for one query head:
+// A[d], B[d], m, Z, R and one pad word (keeps records 16-byte aligned).
+__host__ __device__ constexpr int partial_floats(int d) { return 2 * d + 4; }
+
+// Tokens one wave consumes per step of the decode loop; also the page size
+// of the paged cache, so one step reads exactly one page.
+constexpr int kDecodeStepTokens = 16;
+// Waves per decode workgroup.
+constexpr int kDecodeWaves = 4;
+
+struct DecodeParams {
+    const float *q;
+    const float *rho;
+    float *out;
+    int64_t q_sb, q_sh, rho_sb, rho_sh, out_sb, out_sh;
+    const void *k;
+    const void *v;
+    int64_t k_s0, k_sh, k_st;
+    int64_t v_s0, v_sh, v_st;
+    const int32_t *seq_lens;  // may be null: every row has max_seq_len tokens
+    const int32_t *block_table;
+    int32_t max_seq_len;
+    int32_t max_blocks;
+    int32_t num_kv_heads;
+    int32_t split;      // tokens per split (multiple of kDecodeWaves*kDecodeStepTokens)
+    int32_t nsplit;     // splits per (batch, kv head) in the grid
+    float scale_log2;   // logit scale times log2(e): logits are kept in base 2
+    float *partials;    // [B*Hkv*nsplit][G][partial_floats(d)] or null when nsplit == 1
+    uint32_t *counters; // [B*Hkv] arrival counters, zero between calls
+};
+
+struct PrefillParams {
+    const uint16_t *q;
+    const uint16_t *rho;
+    const uint16_t *k;
+    const uint16_t *v;
+    float *out;
+    int64_t q_sb, q_ss, q_sh;
+    int64_t r_sb, r_ss, r_sh;
+    int64_t k_sb, k_ss, k_sh;
+    int64_t v_sb, v_ss, v_sh;
+    int64_t o_sb, o_ss, o_sh;
+    int32_t batch, seq_len, num_q_heads, num_kv_heads;
+    float scale_log2;
+};
+
+// Launchers (defined next to their kernels).  They return the HIP status of
+// the launch.
+hipError_t launch_decode(const DecodeParams &p, int kv_dtype, int d, int group, bool paged,
+                         int batch, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream);
+
+}  // namespace plx

@@ -1,0 +1,166 @@
+"""The C ABI on the host: the library loads without a GPU, exports every
+function include/parallax.h declares, and rejects each invalid argument with
+its status code before any HIP call (fake, never-dereferenced pointers)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import parallax_local_linear_decode_amd as plx
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "parallax.h")
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return plx.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    text = open(HEADER).read()
+    names = set(re.findall(r"\b(parallax_[a-z_]+)\s*\(", text))
+    assert {"parallax_decode", "parallax_prefill", "parallax_decode_workspace_size",
+            "parallax_status_string", "parallax_last_error", "parallax_abi_version"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} is declared but not exported"
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.parallax_abi_version() == plx.ABI_VERSION
+    for code, name in [(0, "PARALLAX_OK"), (1, "PARALLAX_ERR_INVALID_ARG"),
+                       (2, "PARALLAX_ERR_UNSUPPORTED"), (3, "PARALLAX_ERR_WORKSPACE"),
+                       (4, "PARALLAX_ERR_HIP")]:
+        assert plx.parallax_status_string(code) == name
+
+
+def good_decode(**over):
+    a = plx.DecodeArgs()
+    a.struct_size = ctypes.sizeof(plx.DecodeArgs)
+    a.batch, a.num_q_heads, a.num_kv_heads, a.head_dim = 8, 16, 8, 128
+    a.scale = 128 ** -0.5
+    a.q = a.rho = a.out = a.k = a.v = FAKE
+    a.q_stride_b, a.q_stride_h = 16 * 128, 128
+    a.rho_stride_b, a.rho_stride_h = 16 * 128, 128
+    a.out_stride_b, a.out_stride_h = 16 * 128, 128
+    a.kv_dtype = plx.PARALLAX_BF16
+    a.k_stride_0, a.k_stride_h, a.k_stride_t = 8 * 4096 * 128, 4096 * 128, 128
+    a.v_stride_0, a.v_stride_h, a.v_stride_t = 8 * 4096 * 128, 4096 * 128, 128
+    a.max_seq_len = 4096
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def ws_size(lib, a):
+    n = ctypes.c_size_t(123)
+    st = lib.parallax_decode_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_valid_decode_plan(lib):
+    st, n = ws_size(lib, good_decode())
+    assert st == plx.PARALLAX_OK and n > 0
+    # a single split needs no workspace
+    st, n = ws_size(lib, good_decode(split_tokens=4096))
+    assert st == plx.PARALLAX_OK and n == 0
+    # explicit split: counters (rounded to 256 B) + one record per split and head
+    st, n = ws_size(lib, good_decode(split_tokens=1024))
+    assert n == 256 + 64 * 4 * 2 * (2 * 128 + 4) * 4
+
+
+INVALID = plx.PARALLAX_ERR_INVALID_ARG
+UNSUPP = plx.PARALLAX_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(struct_size=8), INVALID, "struct_size"),
+    (dict(batch=0), INVALID, "batch"),
+    (dict(num_kv_heads=3), INVALID, "num_q_heads"),
+    (dict(num_q_heads=24), UNSUPP, "group"),
+    (dict(head_dim=96), UNSUPP, "head_dim"),
+    (dict(kv_dtype=7), INVALID, "kv_dtype"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(q=None), INVALID, "non-NULL"),
+    (dict(v=None), INVALID, "non-NULL"),
+    (dict(max_seq_len=0), INVALID, "max_seq_len"),
+    (dict(k_stride_t=-128), INVALID, "non-negative"),
+    (dict(k=FAKE + 4), UNSUPP, "aligned"),
+    (dict(out=FAKE + 8), UNSUPP, "aligned"),
+    (dict(k_stride_t=132), UNSUPP, "16 bytes"),
+    (dict(q_stride_h=130), UNSUPP, "16 bytes"),
+    (dict(split_tokens=100), INVALID, "split_tokens"),
+    (dict(split_tokens=-64), INVALID, "split_tokens"),
+    (dict(block_table=FAKE, block_size=16, max_blocks_per_seq=256), INVALID, "seq_lens"),
+    (dict(block_table=FAKE, seq_lens=FAKE, block_size=32, max_blocks_per_seq=256), UNSUPP,
+     "block_size"),
+    (dict(block_table=FAKE, seq_lens=FAKE, block_size=16, max_blocks_per_seq=100), INVALID,
+     "max_blocks_per_seq"),
+    (dict(block_table=FAKE, seq_lens=FAKE, block_size=16, max_blocks_per_seq=0), INVALID,
+     "max_blocks_per_seq"),
+])
+def test_decode_rejects(lib, over, status, needle):
+    a = good_decode(**over)
+    st, _ = ws_size(lib, a)
+    assert st == status
+    assert needle in plx.parallax_last_error()
+    st = lib.parallax_decode(ctypes.byref(a), FAKE, 1 << 30, None)
+    assert st == status
+
+
+def test_decode_null_args(lib):
+    assert lib.parallax_decode(None, None, 0, None) == INVALID
+    n = ctypes.c_size_t(0)
+    assert lib.parallax_decode_workspace_size(None, ctypes.byref(n)) == INVALID
+    assert lib.parallax_decode_workspace_size(ctypes.byref(good_decode()), None) == INVALID
+
+
+def test_decode_workspace_checks(lib):
+    a = good_decode()
+    st, need = ws_size(lib, a)
+    assert need > 0
+    assert lib.parallax_decode(ctypes.byref(a), None, need, None) == plx.PARALLAX_ERR_WORKSPACE
+    assert lib.parallax_decode(ctypes.byref(a), FAKE, need - 1, None) == \
+        plx.PARALLAX_ERR_WORKSPACE
+    assert lib.parallax_decode(ctypes.byref(a), FAKE + 4, need, None) == \
+        plx.PARALLAX_ERR_WORKSPACE
+    assert "workspace" in plx.parallax_last_error()
+
+
+def good_prefill(**over):
+    a = plx.PrefillArgs()
+    a.struct_size = ctypes.sizeof(plx.PrefillArgs)
+    a.batch, a.seq_len, a.num_q_heads, a.num_kv_heads, a.head_dim = 4, 8192, 16, 8, 128
+    a.scale = 128 ** -0.5
+    a.causal = 1
+    a.q = a.rho = a.k = a.v = a.out = FAKE
+    a.q_stride_b, a.q_stride_s, a.q_stride_h = 8192 * 16 * 128, 16 * 128, 128
+    a.rho_stride_b, a.rho_stride_s, a.rho_stride_h = 8192 * 16 * 128, 16 * 128, 128
+    a.k_stride_b, a.k_stride_s, a.k_stride_h = 8192 * 8 * 128, 8 * 128, 128
+    a.v_stride_b, a.v_stride_s, a.v_stride_h = 8192 * 8 * 128, 8 * 128, 128
+    a.out_stride_b, a.out_stride_s, a.out_stride_h = 8192 * 16 * 128, 16 * 128, 128
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(struct_size=4), INVALID, "struct_size"),
+    (dict(seq_len=0), INVALID, "seq_len"),
+    (dict(num_kv_heads=5), INVALID, "num_q_heads"),
+    (dict(scale=float("inf")), INVALID, "scale"),
+    (dict(rho=None), INVALID, "non-NULL"),
+    (dict(k_stride_s=-1), INVALID, "non-negative"),
+    (dict(causal=0), UNSUPP, "causal"),
+    (dict(head_dim=64), UNSUPP, "head_dim"),
+    (dict(v=FAKE + 2), UNSUPP, "aligned"),
+    (dict(q_stride_s=2052), UNSUPP, "16 bytes"),
+    (dict(out_stride_h=130), UNSUPP, "16 bytes"),
+])
+def test_prefill_rejects(lib, over, status, needle):
+    a = good_prefill(**over)
+    assert lib.parallax_prefill(ctypes.byref(a), None) == status
+    assert needle in plx.parallax_last_error()
+    assert lib.parallax_prefill(None, None) == INVALID
