@@ -79,8 +79,10 @@ typedef enum { PARALLAX_F32 = 0, PARALLAX_BF16 = 1 } parallax_dtype_t;
  *     slots past its last token.
  *
  * Inputs: q, rho fp32 [B, Hq, d] (strides q_stride_b, q_stride_h ...);
- * output out fp32 [B, Hq, d].  Arithmetic: fp32 accumulation; bf16 keys
- * meet q and rho through two-term (hi + lo) bf16 splits of q and rho.
+ * output out fp32 [B, Hq, d].  Arithmetic: fp32 accumulation.  With a bf16
+ * cache the products run on bf16 matrix cores: q, rho and the softmax
+ * weights enter as two-term (hi + lo) bf16 splits (about 16 significant
+ * bits).  With an fp32 cache everything runs in fp32 on the vector ALUs.
  */
 typedef struct {
     uint32_t struct_size; /* = sizeof(parallax_decode_args_t) */
@@ -111,17 +113,16 @@ typedef struct {
     int32_t max_blocks_per_seq;
 
     int32_t split_tokens; /* tokens per context split; 0 = chosen by the library,
-                             else a positive multiple of 64 */
+                             else a positive multiple of 256 */
 } parallax_decode_args_t;
 
 /*
  * Bytes of device workspace parallax_decode needs for these arguments
  * (written to *bytes; 0 when one split covers every sequence).  The
- * workspace holds per-split partial sums and one arrival counter per
- * (batch, KV head).  It must be zero-filled before its first use; every
- * completed call leaves it zero-filled again, so it can be reused by later
- * calls on the same stream.  Two calls that run concurrently need separate
- * workspaces.
+ * workspace holds one partial record (running max, Z, R, A, B) per split
+ * and query head; a second, small kernel on the same stream merges them.
+ * Its contents before the call do not matter.  Two calls that can run
+ * concurrently need separate workspaces.  16-byte alignment is required.
  */
 parallax_status_t parallax_decode_workspace_size(const parallax_decode_args_t *args,
                                                  size_t *bytes);

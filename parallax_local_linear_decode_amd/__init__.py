@@ -179,8 +179,8 @@ _workspaces: dict = {}
 
 
 def _workspace(device, stream, nbytes):
-    """A zero-filled workspace per (device, stream), grown on demand.  The
-    decode kernel leaves it zero-filled, so it is reused across calls."""
+    """A workspace per (device, stream), grown on demand and reused across
+    calls (its contents need no initialisation)."""
     key = (str(device), stream.value)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -209,8 +209,8 @@ def parallax_decode(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None
 
     q, rho: float32 [B, Hq, d]; k, v: bfloat16 or float32; seq_lens int32 [B]
     (required when paged).  Returns out float32 [B, Hq, d].  `workspace`, if
-    given, is a zero-initialised uint8 device tensor of at least
-    parallax_decode_workspace_size(...) bytes.
+    given, is a uint8 device tensor of at least
+    parallax_decode_workspace_size(...) bytes (any contents).
     """
     lib = load_library()
     if out is None:

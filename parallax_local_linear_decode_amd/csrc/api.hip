@@ -30,29 +30,30 @@ bool bytes16(int64_t stride_elems, int64_t elem_size) {
     return ((stride_elems * elem_size) & 15) == 0;
 }
 
-constexpr int64_t kTargetWorkgroups = 2048;  // 8 per CU on a 256-CU MI355X
-constexpr int kSplitQuantum = plx::kDecodeWaves * plx::kDecodeStepTokens;  // 64 tokens
+// Splits are whole numbers of 256 tokens: 8 waves x 32-token steps of the
+// bf16 kernel (and 4 x 16-token steps x 4 of the fp32 kernel).
+constexpr int kSplitQuantum = 256;
+// About two workgroups per CU of a 256-CU MI355X in one launch.
+constexpr int64_t kTargetWorkgroups = 512;
+// Longest split: bounds the tail left by the longest rows of a ragged batch.
+constexpr int kMaxSplit = 4096;
 
 struct DecodePlan {
     int group;
     bool paged;
     int split;
     int nsplit;
-    size_t counters_bytes;
     size_t workspace_bytes;
 };
 
-int round_up(int64_t x, int64_t q) { return (int)(((x + q - 1) / q) * q); }
+int64_t round_up(int64_t x, int64_t q) { return ((x + q - 1) / q) * q; }
 
-// Context split: long rows get at least ~16 splits (so rows of very
-// different lengths balance), and the grid gets at least kTargetWorkgroups
-// workgroups while splits stay >= 128 tokens.
 int choose_split(int64_t units, int max_len) {
-    int64_t split = round_up((max_len + 15) / 16, kSplitQuantum);
-    if (split < 256) split = 256;
-    while (split > 128 && units * ((max_len + split - 1) / split) < kTargetWorkgroups)
-        split = round_up(split / 2, kSplitQuantum);
-    if (split > max_len) split = round_up(max_len, kSplitQuantum);
+    int64_t split = round_up((max_len * units + kTargetWorkgroups - 1) / kTargetWorkgroups,
+                             kSplitQuantum);
+    if (split > kMaxSplit) split = kMaxSplit;
+    if (split > round_up(max_len, kSplitQuantum)) split = round_up(max_len, kSplitQuantum);
+    if (split < kSplitQuantum) split = kSplitQuantum;
     return (int)split;
 }
 
@@ -121,14 +122,8 @@ parallax_status_t plan_decode(const parallax_decode_args_t *a, DecodePlan *pl) {
     pl->paged = paged;
     pl->split = split;
     pl->nsplit = nsplit;
-    if (nsplit > 1) {
-        pl->counters_bytes = (size_t)round_up(units * 4, 256);
-        pl->workspace_bytes = pl->counters_bytes + (size_t)units * nsplit * group *
-                                                       plx::partial_floats(a->head_dim) * 4;
-    } else {
-        pl->counters_bytes = 0;
-        pl->workspace_bytes = 0;
-    }
+    pl->workspace_bytes =
+        nsplit > 1 ? (size_t)units * nsplit * group * plx::partial_floats(a->head_dim) * 4 : 0;
     return PARALLAX_OK;
 }
 
@@ -236,13 +231,7 @@ PLX_EXPORT parallax_status_t parallax_decode(const parallax_decode_args_t *a, vo
     p.split = pl.split;
     p.nsplit = pl.nsplit;
     p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
-    if (pl.workspace_bytes > 0) {
-        p.counters = static_cast<uint32_t *>(workspace);
-        p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + pl.counters_bytes);
-    } else {
-        p.counters = nullptr;
-        p.partials = nullptr;
-    }
+    p.partials = pl.workspace_bytes > 0 ? static_cast<float *>(workspace) : nullptr;
     return hip_status(plx::launch_decode(p, a->kv_dtype, a->head_dim, pl.group, pl.paged, a->batch,
                                          static_cast<hipStream_t>(hip_stream)),
                       "decode launch");

@@ -12,25 +12,36 @@
 //
 // which equals o_SA - S_KV rho for the softmax-weighted covariance S_KV.
 //
-// Design (decode is bound by HBM reads of K and V: 4 flop per KV byte at
-// GQA group 2, far under the chip's VALU balance, so no matrix cores):
-//   * grid: (batch, KV head, context split); one workgroup of 4 waves reads
-//     each key/value row once and serves all G query heads of its KV head.
-//   * lanes: a token row is split into 16-byte pieces, one per lane
-//     (16 lanes per row for bf16 d=128), so one wave-wide load covers whole
-//     rows and is fully coalesced; each wave step covers 16 tokens (= one
-//     page of the paged cache).
-//   * bf16 keys meet q and rho through v_dot2_f32_bf16 with q and rho split
-//     into bf16 hi + lo parts (about 16 mantissa bits); values are widened to
-//     fp32 exactly and accumulated with fp32 FMA.
-//   * per-token dot products are summed across the lanes of a row with DPP
-//     butterflies, which leave every lane of the row with bitwise the same sum.
-//   * logits are kept in base 2 (scale * log2 e folded into q); the running
-//     reference max is only raised when a logit exceeds it by more than 8, so
-//     the rescale of A and B is rare; every weight stays below 2^8.
-//   * splits of one (batch, KV head) write partial (m, Z, R, A, B) records;
-//     the last split to arrive (atomic ticket) merges them and writes o, then
-//     re-arms the ticket, so a single launch does the whole decode.
+// Common structure: grid = (batch x KV head) units x context splits.  A
+// workgroup reads each key/value row of its split once and serves all G
+// query heads of its KV head.  Logits are kept in base 2 (scale * log2 e
+// folded into q).  The running reference max only moves when a logit exceeds
+// it by more than 8, so rescaling is rare and every weight stays below 2^8.
+// Each split leaves a partial record (m, Z, R, A, B) per query head; with
+// more than one split a small merge kernel combines them.  Every launch is
+// self-contained: no cross-workgroup fences, atomics or counters.
+//
+// bf16 cache -- matrix-core kernel.  Scores and both value sums are dense
+// contractions over the shared KV stream, so they run on bf16 MFMA
+// (16x16x32, fp32 accumulate):
+//   scores  D1[token][col] = K[token][:] . C[col][:]   with columns
+//           q_h hi, rho_h hi, q_h lo, rho_h lo   (two-term bf16 splits of
+//           fp32 q and rho, about 16 significant bits);
+//   sums    D2[d][col] = sum_token V[token][d] . P[token][col]   with columns
+//           w_h hi, w_h t_h hi, w_h lo, w_h t_h lo  (w = e^{s - m}),
+//   so A_h, B_h come out of the same MFMAs as hi + lo column pairs.  The
+//   softmax step works directly in the MFMA accumulator layout, using DPP
+//   row shifts to move values between columns.  V reaches the MFMA through a
+//   wave-private LDS tile read back with ds_read_b64_tr_b16, which returns
+//   the token-major tile transposed into operand layout.  Eight waves per
+//   workgroup, 32 tokens per wave step, next step's loads in flight while the
+//   current step computes.
+//
+// fp32 cache -- VALU kernel (the fp32 path exists for fp32-accurate checks;
+// matrix cores have no fp32-exact mode at this precision):
+//   a token row is split into 16-byte pieces, one per lane, so one wave-wide
+//   load covers whole rows; per-token dot products are summed across the row
+//   with DPP butterflies; values accumulate with fp32 FMA.
 #include "kernels.hpp"
 
 #include <math.h>
@@ -38,335 +49,73 @@
 namespace plx {
 namespace {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kRescaleSlack = 8.0f;  // base-2 headroom before the reference max moves
 
 template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
+__device__ __forceinline__ float dpp_f(float x) {
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, true);
+}
+// Within each row of 16 lanes: lane i receives lane i+N (shl) / i-N (shr);
+// lanes whose source falls outside the row receive 0.
+template <int N> __device__ __forceinline__ float row_shl(float x) { return dpp_f<0x100 + N>(x); }
+template <int N> __device__ __forceinline__ float row_shr(float x) { return dpp_f<0x110 + N>(x); }
+template <int N> __device__ __forceinline__ uint32_t row_shr_u(uint32_t x) { return dpp_u<0x110 + N>(x); }
+
+__device__ __forceinline__ float read_lane(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
-// Sum over aligned groups of N lanes (N in 2..32).  Each step adds a value
-// and its partner's, so partners compute the same sum in swapped order and
-// every lane of the group ends with bitwise the same result.
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-    x += dpp_mov<0xB1>(x);                          // quad_perm [1,0,3,2]
-    if constexpr (N >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
-    if constexpr (N >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror
-    if constexpr (N >= 16) x += dpp_mov<0x140>(x);  // row_mirror
-    if constexpr (N >= 32) x += __shfl_xor(x, 16);
-    return x;
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
 }
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ bf16x2_t pack_bf16(float a, float b) {
-    bf16x2_t r = {(__bf16)a, (__bf16)b};
-    return r;
-}
-
-// Lane geometry for a cache element type and head dim.
-template <typename KV, int D>
-struct Geo {
-    static constexpr int VEC = 16 / (int)sizeof(KV);     // elements per 16-byte lane load
-    static constexpr int LPT = D / VEC;                  // lanes per token row
-    static constexpr int TPL = 64 / LPT;                 // token rows per wave-wide load
-    static constexpr int U = kDecodeStepTokens / TPL;    // loads per 16-token step
-    static_assert(LPT >= 2 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "unsupported geometry");
-    static_assert(U * TPL == kDecodeStepTokens, "step must be a whole number of loads");
-};
-
-// Query-side operands of one lane: its VEC-wide slice of q (pre-scaled to
-// base-2 logits) and of rho for each of the G heads.
-template <typename KV, int D, int G>
-struct QueryRegs;
-
-template <int D, int G>
-struct QueryRegs<uint16_t, D, G> {  // bf16 cache: two-term bf16 splits
-    static constexpr int P = Geo<uint16_t, D>::VEC / 2;
-    bf16x2_t qh[G][P], ql[G][P], rh[G][P], rl[G][P];
-
-    __device__ void set(int g, const float *q, const float *r) {
-        for (int i = 0; i < P; ++i) {
-            float q0 = q[2 * i], q1 = q[2 * i + 1], r0 = r[2 * i], r1 = r[2 * i + 1];
-            qh[g][i] = pack_bf16(q0, q1);
-            rh[g][i] = pack_bf16(r0, r1);
-            ql[g][i] = pack_bf16(q0 - (float)qh[g][i][0], q1 - (float)qh[g][i][1]);
-            rl[g][i] = pack_bf16(r0 - (float)rh[g][i][0], r1 - (float)rh[g][i][1]);
-        }
-    }
-    // Partial (this lane's slice) of q.k and rho.k for head g.
-    __device__ __forceinline__ void dots(int g, const uint4 &kw, float &s, float &t) const {
-        const uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
-        float sh = 0.f, sl = 0.f, th = 0.f, tl = 0.f;
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
-            bf16x2_t kk = __builtin_bit_cast(bf16x2_t, w[i]);
-            sh = __builtin_amdgcn_fdot2_f32_bf16(qh[g][i], kk, sh, false);
-            sl = __builtin_amdgcn_fdot2_f32_bf16(ql[g][i], kk, sl, false);
-            th = __builtin_amdgcn_fdot2_f32_bf16(rh[g][i], kk, th, false);
-            tl = __builtin_amdgcn_fdot2_f32_bf16(rl[g][i], kk, tl, false);
-        }
-        s = sh + sl;
-        t = th + tl;
-    }
-    __device__ __forceinline__ static void widen(const uint4 &vw, float *vf) {
-        const uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            vf[2 * i] = bf16_lo(w[i]);
-            vf[2 * i + 1] = bf16_hi(w[i]);
-        }
-    }
-};
-
-template <int D, int G>
-struct QueryRegs<float, D, G> {  // fp32 cache: plain fp32 FMA
-    static constexpr int VEC = 4;
-    float qf[G][VEC], rf[G][VEC];
-
-    __device__ void set(int g, const float *q, const float *r) {
-        for (int i = 0; i < VEC; ++i) {
-            qf[g][i] = q[i];
-            rf[g][i] = r[i];
-        }
-    }
-    __device__ __forceinline__ void dots(int g, const uint4 &kw, float &s, float &t) const {
-        const float k[4] = {__uint_as_float(kw.x), __uint_as_float(kw.y), __uint_as_float(kw.z),
-                            __uint_as_float(kw.w)};
-        float s0 = qf[g][0] * k[0], t0 = rf[g][0] * k[0];
-#pragma unroll
-        for (int i = 1; i < VEC; ++i) {
-            s0 = fmaf(qf[g][i], k[i], s0);
-            t0 = fmaf(rf[g][i], k[i], t0);
-        }
-        s = s0;
-        t = t0;
-    }
-    __device__ __forceinline__ static void widen(const uint4 &vw, float *vf) {
-        vf[0] = __uint_as_float(vw.x);
-        vf[1] = __uint_as_float(vw.y);
-        vf[2] = __uint_as_float(vw.z);
-        vf[3] = __uint_as_float(vw.w);
-    }
-};
-
-// Running sums of one lane for one head: reference max m (base 2), Z, R and
-// this lane's VEC-wide slices of A and B.
-template <int VEC>
-struct Acc {
-    float m, Z, R, A[VEC], B[VEC];
-    __device__ void init() {
-        m = -INFINITY;
-        Z = R = 0.f;
-        for (int e = 0; e < VEC; ++e) A[e] = B[e] = 0.f;
-    }
-    __device__ __forceinline__ void scale_by(float alpha) {
-        Z *= alpha;
-        R *= alpha;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            A[e] *= alpha;
-            B[e] *= alpha;
-        }
-    }
-    // Fold another lane's state (same slice) into this one.
-    __device__ __forceinline__ void merge(float m2, float Z2, float R2, const float *A2,
-                                          const float *B2) {
-        float mn = fmaxf(m, m2);
-        float a1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-        float a2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
-        Z = a1 * Z + a2 * Z2;
-        R = a1 * R + a2 * R2;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            A[e] = a1 * A[e] + a2 * A2[e];
-            B[e] = a1 * B[e] + a2 * B2[e];
-        }
-        m = mn;
-    }
-};
 
 __device__ __forceinline__ uint4 load16(const void *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
 
-template <typename KV, int D, int G, bool PAGED>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeParams p) {
-    using Gm = Geo<KV, D>;
-    constexpr int VEC = Gm::VEC, LPT = Gm::LPT, TPL = Gm::TPL, U = Gm::U;
-    constexpr int REC = partial_floats(D);
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int row = lane / LPT;  // token row of this lane within a wave-wide load
-    const int sub = lane % LPT;  // 16-byte piece of the row
-
-    const int split_idx = blockIdx.x % p.nsplit;
-    const int unit = blockIdx.x / p.nsplit;  // b * Hkv + hk
-    const int b = unit / p.num_kv_heads;
-    const int hk = unit % p.num_kv_heads;
-
-    int L = p.seq_lens ? p.seq_lens[b] : p.max_seq_len;
+// Sequence length of batch row b, clamped to what the cache can hold, and
+// the number of splits that row uses (at least one, so an empty row still
+// gets its zero output written).
+template <bool PAGED>
+__device__ __forceinline__ void row_extent(const DecodeParams &p, int b, int &L, int &nsp) {
+    L = p.seq_lens ? p.seq_lens[b] : p.max_seq_len;
     L = max(0, min(L, PAGED ? p.max_blocks * kDecodeStepTokens : p.max_seq_len));
-    const int nsp = max(1, min(p.nsplit, (L + p.split - 1) / p.split));
-    if (split_idx >= nsp) return;
-    const int t0 = split_idx * p.split;
-    const int t1 = min(L, t0 + p.split);
-    const int nsteps = max(0, (t1 - t0 + kDecodeStepTokens - 1) / kDecodeStepTokens);
+    nsp = max(1, min(p.nsplit, (L + p.split - 1) / p.split));
+}
 
-    // ---- query operands
-    QueryRegs<KV, D, G> qr;
-    {
-        const int h0 = hk * G;
-        for (int g = 0; g < G; ++g) {
-            const float *qp = p.q + b * p.q_sb + (int64_t)(h0 + g) * p.q_sh + sub * VEC;
-            const float *rp = p.rho + b * p.rho_sb + (int64_t)(h0 + g) * p.rho_sh + sub * VEC;
-            float qv[VEC], rv[VEC];
-            for (int i = 0; i < VEC; i += 4) {
-                float4 a = *reinterpret_cast<const float4 *>(qp + i);
-                float4 c = *reinterpret_cast<const float4 *>(rp + i);
-                qv[i] = a.x * p.scale_log2;
-                qv[i + 1] = a.y * p.scale_log2;
-                qv[i + 2] = a.z * p.scale_log2;
-                qv[i + 3] = a.w * p.scale_log2;
-                rv[i] = c.x;
-                rv[i + 1] = c.y;
-                rv[i + 2] = c.z;
-                rv[i + 3] = c.w;
-            }
-            qr.set(g, qv, rv);
-        }
-    }
+__device__ __forceinline__ float finish(float A, float B, float Z, float R) {
+    if (!(Z > 0.f)) return 0.f;  // empty row
+    const float inv = 1.0f / Z;
+    const float a = A * inv, bb = B * inv, r = R * inv;
+    return a - (bb - a * r);
+}
 
-    Acc<VEC> acc[G];
-    for (int g = 0; g < G; ++g) acc[g].init();
-
-    const KV *kc = static_cast<const KV *>(p.k);
-    const KV *vc = static_cast<const KV *>(p.v);
-    const int64_t row_off_k = (int64_t)sub * VEC;
-
-    // Base pointers of the 16-token step starting at token `base`.
-    auto step_bases = [&](int base, const KV *&kb, const KV *&vb) {
-        if constexpr (PAGED) {
-            const int pg = p.block_table[(int64_t)b * p.max_blocks + base / kDecodeStepTokens];
-            kb = kc + (int64_t)pg * p.k_s0 + (int64_t)hk * p.k_sh;
-            vb = vc + (int64_t)pg * p.v_s0 + (int64_t)hk * p.v_sh;
-        } else {
-            kb = kc + (int64_t)b * p.k_s0 + (int64_t)hk * p.k_sh + (int64_t)base * p.k_st;
-            vb = vc + (int64_t)b * p.v_s0 + (int64_t)hk * p.v_sh + (int64_t)base * p.v_st;
-        }
-    };
-    // Issue the loads of one step.  Rows past t1 re-read the step's last
-    // valid token (always in bounds); their weight is forced to zero.
-    auto issue = [&](int st, uint4 *kw, uint4 *vw) {
-        const int base = t0 + st * kDecodeStepTokens;
-        const KV *kb, *vb;
-        step_bases(base, kb, vb);
-        const int last = t1 - 1 - base;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int j = u * TPL + row;
-            j = j <= last ? j : last;
-            kw[u] = load16(kb + (int64_t)j * p.k_st + row_off_k);
-            vw[u] = load16(vb + (int64_t)j * p.v_st + row_off_k);
-        }
-    };
-
-    uint4 kw[U], vw[U];
-    int st = wave;
-    if (st < nsteps) issue(st, kw, vw);
-    while (st < nsteps) {
-        uint4 kcur[U], vcur[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            kcur[u] = kw[u];
-            vcur[u] = vw[u];
-        }
-        const int base = t0 + st * kDecodeStepTokens;
-        const int nst = st + kDecodeWaves;
-        if (nst < nsteps) issue(nst, kw, vw);  // prefetch the next step
-
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool valid = base + u * TPL + row < t1;
-            float vf[VEC];
-            QueryRegs<KV, D, G>::widen(vcur[u], vf);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float s, t;
-                qr.dots(g, kcur[u], s, t);
-                s = group_sum<LPT>(s);
-                t = group_sum<LPT>(t);
-                s = valid ? s : -INFINITY;
-                Acc<VEC> &a = acc[g];
-                if (s > a.m + kRescaleSlack) {  // also taken by the first token
-                    a.scale_by(__builtin_amdgcn_exp2f(a.m - s));
-                    a.m = s;
-                }
-                const float w = valid ? __builtin_amdgcn_exp2f(s - a.m) : 0.f;
-                const float wt = w * t;
-                a.Z += w;
-                a.R += wt;
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    a.A[e] = fmaf(w, vf[e], a.A[e]);
-                    a.B[e] = fmaf(wt, vf[e], a.B[e]);
-                }
-            }
-        }
-        st = nst;
-    }
-
-    // ---- merge the token rows of this wave (lanes LPT, 2*LPT, ... apart)
-#pragma unroll
-    for (int off = LPT; off < 64; off *= 2) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            Acc<VEC> &a = acc[g];
-            float m2 = __shfl_xor(a.m, off), Z2 = __shfl_xor(a.Z, off),
-                  R2 = __shfl_xor(a.R, off);
-            float A2[VEC], B2[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                A2[e] = __shfl_xor(a.A[e], off);
-                B2[e] = __shfl_xor(a.B[e], off);
-            }
-            a.merge(m2, Z2, R2, A2, B2);
-        }
-    }
-
-    // ---- merge the waves through LDS
-    __shared__ float red[kDecodeWaves][G][REC];
-    if (row == 0) {
-        for (int g = 0; g < G; ++g) {
-            for (int e = 0; e < VEC; ++e) {
-                red[wave][g][sub * VEC + e] = acc[g].A[e];
-                red[wave][g][D + sub * VEC + e] = acc[g].B[e];
-            }
-            if (sub == 0) {
-                red[wave][g][2 * D] = acc[g].m;
-                red[wave][g][2 * D + 1] = acc[g].Z;
-                red[wave][g][2 * D + 2] = acc[g].R;
-            }
-        }
-    }
-    __syncthreads();
-
-    const bool single = nsp == 1;
-    float *my_rec = single ? nullptr
-                           : p.partials + ((int64_t)unit * p.nsplit + split_idx) * G * REC;
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kDecodeWaves) {
+// Merge NW per-wave records (red[w][head][...]) of this workgroup; write
+// the output if the row has a single split, else this split's record.
+template <int D, int G, int NW>
+__device__ void finish_block(const DecodeParams &p, float (*red)[G][partial_floats(D)], int b,
+                             int hk, int unit, int split_idx, int nsp) {
+    constexpr int REC = partial_floats(D);
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
         const int g = idx / D, e = idx % D;
         float M = -INFINITY;
-        for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, red[w][g][2 * D]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, red[w][g][2 * D]);
         float Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
         if (M != -INFINITY) {
-            for (int w = 0; w < kDecodeWaves; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 const float al = __builtin_amdgcn_exp2f(red[w][g][2 * D] - M);
                 Z += al * red[w][g][2 * D + 1];
                 R += al * red[w][g][2 * D + 2];
@@ -374,16 +123,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeParams 
                 B += al * red[w][g][D + e];
             }
         }
-        if (single) {
-            float o = 0.f;
-            if (Z > 0.f) {
-                const float inv = 1.0f / Z;
-                const float av = A * inv, bv = B * inv, r = R * inv;
-                o = av - (bv - av * r);
-            }
-            p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = o;
+        if (nsp == 1) {
+            p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = finish(A, B, Z, R);
         } else {
-            float *rec = my_rec + g * REC;
+            float *rec = p.partials + (((int64_t)unit * p.nsplit + split_idx) * G + g) * REC;
             rec[e] = A;
             rec[D + e] = B;
             if (e == 0) {
@@ -393,60 +136,528 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeParams 
             }
         }
     }
-    if (single) return;
+}
 
-    // ---- the last split of this (batch, KV head) to finish merges all splits
-    __shared__ int is_last;
-    __threadfence();  // release this split's record to the whole device
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(&p.counters[unit], 1u);
-        is_last = prev == (unsigned)(nsp - 1);
+// ===================================================== bf16: matrix cores ===
+
+constexpr int kMfmaStep = 32;  // tokens per wave step (two 16-token MFMA row blocks)
+
+// Waves per workgroup: 8 (two per SIMD), or 4 when eight query heads per KV
+// head at d = 128 need more than the 256 registers two waves can each hold.
+template <int D, int G>
+constexpr int mfma_waves() { return (D == 128 && G == 8) ? 4 : 8; }
+
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__((64 * mfma_waves<D, G>())) void decode_mfma_kernel(DecodeParams p) {
+    constexpr int kMfmaWaves = mfma_waves<D, G>();
+    constexpr int HS = G < 4 ? G : 4;     // query heads per 16-column set
+    constexpr int NCS = G / HS;           // column sets (2 when G = 8)
+    constexpr int KS = D / 32;            // score MFMAs per row block (K = 32 each)
+    constexpr int DB = D / 16;            // 16-row blocks of the value sums
+    constexpr int DQ = D / 4;             // head-dim values per lane group in the scores
+    constexpr int LPR = D / 8;            // lanes per V row in a coalesced 16-byte load
+    constexpr int RPL = 64 / LPR;         // V rows per wave-wide load
+    constexpr int VLD = kMfmaStep / RPL;  // V loads per lane per step
+    constexpr int VROW = 2 * D + 16;      // bytes per LDS row of the V tile (padded)
+    constexpr int REC = partial_floats(D);
+
+    __shared__ __attribute__((aligned(16))) unsigned char vtile[kMfmaWaves][kMfmaStep * VROW];
+    __shared__ float red[kMfmaWaves][G][REC];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane & 15;  // MFMA column (scores/sums) or row (V^T) index
+    const int g = lane >> 4;  // lane group: which 8 k-slots of an MFMA operand
+
+    const int split_idx = blockIdx.x % p.nsplit;
+    const int unit = blockIdx.x / p.nsplit;
+    const int b = unit / p.num_kv_heads;
+    const int hk = unit % p.num_kv_heads;
+    int L, nsp;
+    row_extent<PAGED>(p, b, L, nsp);
+    if (split_idx >= nsp) return;
+    const int t0 = split_idx * p.split;
+    const int t1 = min(L, t0 + p.split);
+    const int nsteps = (t1 - t0 + kMfmaStep - 1) / kMfmaStep;
+
+    // ---- running state: reference max per head (wave-uniform), value sums
+    // in the MFMA accumulator layout, per-lane partial column totals
+    float mref[NCS][HS];
+    f32x4_t acc[NCS][DB];
+    float ztot[NCS];
+#pragma unroll
+    for (int s = 0; s < NCS; ++s) {
+        for (int h = 0; h < HS; ++h) mref[s][h] = -INFINITY;
+        for (int db = 0; db < DB; ++db) acc[s][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        ztot[s] = 0.f;
+    }
+
+    const uint16_t *kc = static_cast<const uint16_t *>(p.k);
+    const uint16_t *vc = static_cast<const uint16_t *>(p.v);
+    // Element offset of token j (already clamped to a valid token) of this (b, hk).
+    auto tok_k = [&](int j) -> int64_t {
+        if constexpr (PAGED) {
+            const int pg = p.block_table[(int64_t)b * p.max_blocks + j / kDecodeStepTokens];
+            return (int64_t)pg * p.k_s0 + (int64_t)hk * p.k_sh +
+                   (int64_t)(j % kDecodeStepTokens) * p.k_st;
+        } else {
+            return (int64_t)b * p.k_s0 + (int64_t)hk * p.k_sh + (int64_t)j * p.k_st;
+        }
+    };
+    auto tok_v = [&](int j) -> int64_t {
+        if constexpr (PAGED) {
+            const int pg = p.block_table[(int64_t)b * p.max_blocks + j / kDecodeStepTokens];
+            return (int64_t)pg * p.v_s0 + (int64_t)hk * p.v_sh +
+                   (int64_t)(j % kDecodeStepTokens) * p.v_st;
+        } else {
+            return (int64_t)b * p.v_s0 + (int64_t)hk * p.v_sh + (int64_t)j * p.v_st;
+        }
+    };
+
+    // Loads of one step: K straight into score-operand layout (lane c, g of
+    // row block rb holds token 16*rb + c, head-dim values DQ*g + 8*ks ..),
+    // V as coalesced 16-byte row pieces.  Tokens past t1 re-read token t1-1.
+    auto issue_k = [&](int st, uint4 (&kr)[2][KS]) {
+        const int base = t0 + st * kMfmaStep;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int64_t off = tok_k(min(base + 16 * rb + c, t1 - 1)) + DQ * g;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kr[rb][ks] = load16(kc + off + 8 * ks);
+        }
+    };
+    auto issue_v = [&](int st, uint4 (&vr)[VLD]) {
+        const int base = t0 + st * kMfmaStep;
+#pragma unroll
+        for (int u = 0; u < VLD; ++u) {
+            const int j = min(base + RPL * u + lane / LPR, t1 - 1);
+            vr[u] = load16(vc + tok_v(j) + 8 * (lane % LPR));
+        }
+    };
+
+    // the first step's loads go out before the query-side setup below
+    uint4 kr[2][KS], vr[VLD];
+    if (wave < nsteps) {
+        issue_k(wave, kr);
+        issue_v(wave, vr);
+    }
+
+    // ---- score-side operands: column c of set s is q or rho of head
+    // hk*G + s*HS + c%HS, its bf16 hi part (c < 2*HS) or lo part; head-dim
+    // value d = DQ*g + 8*ks + i sits in k-slot 8*g + i of score MFMA ks.
+    const int which = c / HS;  // 0 q hi, 1 rho hi, 2 q lo, 3 rho lo, >= 4 unused
+    bf16x8_t bq[NCS][KS];
+#pragma unroll
+    for (int s = 0; s < NCS; ++s) {
+        const int head = hk * G + s * HS + (c % HS);
+        const bool is_rho = which & 1;
+        const float *src = is_rho ? p.rho + b * p.rho_sb + (int64_t)head * p.rho_sh
+                                  : p.q + b * p.q_sb + (int64_t)head * p.q_sh;
+        const float mul = is_rho ? 1.0f : p.scale_log2;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float x[8];
+            if (which < 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(src + DQ * g + 8 * ks);
+                const float4 e = *reinterpret_cast<const float4 *>(src + DQ * g + 8 * ks + 4);
+                x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+                x[4] = e.x; x[5] = e.y; x[6] = e.z; x[7] = e.w;
+            } else {
+                for (int i = 0; i < 8; ++i) x[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = x[i] * mul;
+                const __bf16 hi = (__bf16)v;
+                bq[s][ks][i] = which < 2 ? hi : (__bf16)(v - (float)hi);
+            }
+        }
+    }
+
+    unsigned char *vt = vtile[wave];
+
+    auto process = [&](int st, int nst, uint4 (&kr)[2][KS], uint4 (&vr)[VLD]) {
+        const int base = t0 + st * kMfmaStep;
+        // V rows into the wave's LDS tile (row-major, padded rows)
+#pragma unroll
+        for (int u = 0; u < VLD; ++u)
+            *reinterpret_cast<uint4 *>(vt + (RPL * u + lane / LPR) * VROW + 16 * (lane % LPR)) =
+                vr[u];
+        if (nst >= 0) issue_v(nst, vr);
+
+        // scores: d1[s][rb] lane (c, g) = column c, tokens 16*rb + 4*g + j
+        f32x4_t d1[NCS][2];
+#pragma unroll
+        for (int s = 0; s < NCS; ++s)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, kr[rb][ks]), bq[s][ks], a, 0, 0, 0);
+                d1[s][rb] = a;
+            }
+        if (nst >= 0) issue_k(nst, kr);
+
+        // k-slot r (0..7) of this lane's group <-> token of the step
+        bool valid[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            valid[r] = base + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4) < t1;
+
+        bf16x8_t pw[NCS];
+#pragma unroll
+        for (int s = 0; s < NCS; ++s) {
+            float y[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float x = r < 4 ? d1[s][0][r] : d1[s][1][r - 4];
+                y[r] = x + row_shl<2 * HS>(x);  // hi + lo columns: lanes c < HS hold s, next HS hold t
+            }
+            // step max of each head's logits (lanes c < HS), over all 4 groups
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) mx = fmaxf(mx, valid[r] ? y[r] : -INFINITY);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            bool moved = false;
+            float alpha[HS];
+#pragma unroll
+            for (int h = 0; h < HS; ++h) {
+                const float tm = read_lane(mx, h);
+                alpha[h] = 1.0f;
+                if (tm > mref[s][h] + kRescaleSlack) {  // wave-uniform
+                    alpha[h] = __builtin_amdgcn_exp2f(mref[s][h] - tm);
+                    mref[s][h] = tm;
+                    moved = true;
+                }
+            }
+            float m_lane = mref[s][0];
+#pragma unroll
+            for (int h = 1; h < HS; ++h) m_lane = (c % HS) == h ? mref[s][h] : m_lane;
+            if (moved) {  // rescale the sums of every column of a moved head
+                float al = alpha[0];
+#pragma unroll
+                for (int h = 1; h < HS; ++h) al = (c % HS) == h ? alpha[h] : al;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[s][db] *= al;
+                ztot[s] *= al;
+            }
+            // weights and probe-weighted weights, split into bf16 hi + lo
+            uint32_t opw[4];
+            float colsum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 8; r += 2) {
+                float full[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const float w = valid[r + q] ? __builtin_amdgcn_exp2f(y[r + q] - m_lane) : 0.f;
+                    const float wt = w * row_shl<HS>(y[r + q]);  // t of head c sits HS lanes up
+                    const float wt_here = row_shr<HS>(wt);        // lanes HS..2HS-1 take it
+                    full[q] = c < HS ? w : (c < 2 * HS ? wt_here : 0.f);
+                }
+                const uint32_t hi = pack_bf16x2(full[0], full[1]);
+                const uint32_t lo =
+                    pack_bf16x2(full[0] - bf16_lo(hi), full[1] - bf16_hi(hi));
+                const uint32_t lo_here = row_shr_u<2 * HS>(lo);  // lo parts move 2*HS lanes up
+                const uint32_t o = c < 2 * HS ? hi : (c < 4 * HS ? lo_here : 0u);
+                opw[r / 2] = o;
+                colsum += bf16_lo(o) + bf16_hi(o);
+            }
+            ztot[s] += colsum;
+            pw[s] = __builtin_bit_cast(bf16x8_t, uint4{opw[0], opw[1], opw[2], opw[3]});
+        }
+
+        // value sums: V^T operand rows d = 16*db + c, k-slots as above, read
+        // transposed out of the LDS tile (4 tokens x 16 head-dim values per read)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+            const int col = 16 * db + 4 * (c % 4);
+            const unsigned char *a0 = vt + (4 * g + c / 4) * VROW + 2 * col;
+            const unsigned char *a1 = vt + (16 + 4 * g + c / 4) * VROW + 2 * col;
+            const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a0);
+            const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a1);
+            const bf16x8_t vop = __builtin_bit_cast(
+                bf16x8_t, (short __attribute__((ext_vector_type(8)))){lo4[0], lo4[1], lo4[2], lo4[3],
+                                                                      hi4[0], hi4[1], hi4[2], hi4[3]});
+#pragma unroll
+            for (int s = 0; s < NCS; ++s)
+                acc[s][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pw[s], acc[s][db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One register buffer per operand: the next step's V loads start as soon
+    // as this step's V rows are in LDS, its K loads as soon as the score
+    // MFMAs have consumed K; the other waves of the CU cover the latency.
+    {
+        int st = wave;
+        while (st < nsteps) {
+            const int nst = st + kMfmaWaves;
+            process(st, nst < nsteps ? nst : -1, kr, vr);
+            st = nst;
+        }
+    }
+
+    // ---- this wave's record per head: hi + lo columns summed
+#pragma unroll
+    for (int s = 0; s < NCS; ++s) {
+        float zr = ztot[s] + row_shl<2 * HS>(ztot[s]);
+        zr += __shfl_xor(zr, 16);
+        zr += __shfl_xor(zr, 32);
+        const int head = s * HS + (c % HS);
+        float *rec = red[wave][head];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = acc[s][db][j] + row_shl<2 * HS>(acc[s][db][j]);
+                const int d = 16 * db + 4 * g + j;
+                if (c < HS) rec[d] = v;               // A
+                else if (c < 2 * HS) rec[D + d] = v;  // B
+            }
+        if (g == 0 && c < HS) {
+            float m_lane = mref[s][0];
+            for (int h = 1; h < HS; ++h) m_lane = c == h ? mref[s][h] : m_lane;
+            rec[2 * D] = m_lane;
+            rec[2 * D + 1] = zr;
+        } else if (g == 0 && c < 2 * HS) {
+            rec[2 * D + 2] = zr;
+        }
     }
     __syncthreads();
-    if (!is_last) return;
-    __threadfence();  // acquire the other splits' records
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&p.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    finish_block<D, G, kMfmaWaves>(p, red, b, hk, unit, split_idx, nsp);
+}
 
-    const float *recs = p.partials + (int64_t)unit * p.nsplit * G * REC;
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kDecodeWaves) {
-        const int g = idx / D, e = idx % D;
-        float M = -INFINITY;
-        for (int c = 0; c < nsp; ++c) M = fmaxf(M, recs[(c * G + g) * REC + 2 * D]);
-        float Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
-        for (int c = 0; c < nsp; ++c) {
-            const float *rec = recs + (c * G + g) * REC;
-            const float al = __builtin_amdgcn_exp2f(rec[2 * D] - M);
-            Z += al * rec[2 * D + 1];
-            R += al * rec[2 * D + 2];
-            A += al * rec[e];
-            B += al * rec[D + e];
+// ============================================================ fp32: VALU ===
+
+constexpr int kValuWaves = 4;
+
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodeParams p) {
+    constexpr int VEC = 4;                          // fp32 values per 16-byte load
+    constexpr int LPT = D / VEC;                    // lanes per token row
+    constexpr int TPL = 64 / LPT;                   // token rows per wave-wide load
+    constexpr int U = kDecodeStepTokens / TPL;      // loads per 16-token step
+    constexpr int REC = partial_floats(D);
+    static_assert(LPT == 16 || LPT == 32, "fp32 rows of 64 or 128 values");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = lane / LPT;
+    const int sub = lane % LPT;
+
+    const int split_idx = blockIdx.x % p.nsplit;
+    const int unit = blockIdx.x / p.nsplit;
+    const int b = unit / p.num_kv_heads;
+    const int hk = unit % p.num_kv_heads;
+    int L, nsp;
+    row_extent<PAGED>(p, b, L, nsp);
+    if (split_idx >= nsp) return;
+    const int t0 = split_idx * p.split;
+    const int t1 = min(L, t0 + p.split);
+    const int nsteps = (t1 - t0 + kDecodeStepTokens - 1) / kDecodeStepTokens;
+
+    float qv[G][VEC], rv[G][VEC];
+    for (int h = 0; h < G; ++h) {
+        const float4 a = *reinterpret_cast<const float4 *>(
+            p.q + b * p.q_sb + (int64_t)(hk * G + h) * p.q_sh + sub * VEC);
+        const float4 e = *reinterpret_cast<const float4 *>(
+            p.rho + b * p.rho_sb + (int64_t)(hk * G + h) * p.rho_sh + sub * VEC);
+        qv[h][0] = a.x * p.scale_log2; qv[h][1] = a.y * p.scale_log2;
+        qv[h][2] = a.z * p.scale_log2; qv[h][3] = a.w * p.scale_log2;
+        rv[h][0] = e.x; rv[h][1] = e.y; rv[h][2] = e.z; rv[h][3] = e.w;
+    }
+    float m[G], Z[G], R[G], A[G][VEC], B[G][VEC];
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        Z[h] = R[h] = 0.f;
+        for (int e = 0; e < VEC; ++e) A[h][e] = B[h][e] = 0.f;
+    }
+
+    const float *kc = static_cast<const float *>(p.k);
+    const float *vc = static_cast<const float *>(p.v);
+    for (int st = wave; st < nsteps; st += kValuWaves) {
+        const int base = t0 + st * kDecodeStepTokens;
+        int64_t kb, vb;
+        if constexpr (PAGED) {
+            const int pg = p.block_table[(int64_t)b * p.max_blocks + base / kDecodeStepTokens];
+            kb = (int64_t)pg * p.k_s0 + (int64_t)hk * p.k_sh - (int64_t)base * p.k_st;
+            vb = (int64_t)pg * p.v_s0 + (int64_t)hk * p.v_sh - (int64_t)base * p.v_st;
+        } else {
+            kb = (int64_t)b * p.k_s0 + (int64_t)hk * p.k_sh;
+            vb = (int64_t)b * p.v_s0 + (int64_t)hk * p.v_sh;
         }
-        const float inv = 1.0f / Z;
-        const float av = A * inv, bv = B * inv, r = R * inv;
-        p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = av - (bv - av * r);
+        uint4 kw[U], vw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(base + u * TPL + row, t1 - 1);  // rows past t1 re-read t1-1
+            kw[u] = load16(kc + kb + (int64_t)j * p.k_st + sub * VEC);
+            vw[u] = load16(vc + vb + (int64_t)j * p.v_st + sub * VEC);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = base + u * TPL + row < t1;
+            const float kf[4] = {__uint_as_float(kw[u].x), __uint_as_float(kw[u].y),
+                                 __uint_as_float(kw[u].z), __uint_as_float(kw[u].w)};
+            const float vf[4] = {__uint_as_float(vw[u].x), __uint_as_float(vw[u].y),
+                                 __uint_as_float(vw[u].z), __uint_as_float(vw[u].w)};
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float s = qv[h][0] * kf[0], t = rv[h][0] * kf[0];
+#pragma unroll
+                for (int e = 1; e < VEC; ++e) {
+                    s = fmaf(qv[h][e], kf[e], s);
+                    t = fmaf(rv[h][e], kf[e], t);
+                }
+                // butterfly sums over the row's lanes: partners add in swapped
+                // order, so every lane of a row ends with the same bits
+                s += dpp_f<0xB1>(s); t += dpp_f<0xB1>(t);    // quad_perm [1,0,3,2]
+                s += dpp_f<0x4E>(s); t += dpp_f<0x4E>(t);    // quad_perm [2,3,0,1]
+                s += dpp_f<0x141>(s); t += dpp_f<0x141>(t);  // row_half_mirror
+                s += dpp_f<0x140>(s); t += dpp_f<0x140>(t);  // row_mirror
+                if constexpr (LPT == 32) {
+                    s += __shfl_xor(s, 16);
+                    t += __shfl_xor(t, 16);
+                }
+                s = valid ? s : -INFINITY;
+                if (s > m[h] + kRescaleSlack) {
+                    const float al = __builtin_amdgcn_exp2f(m[h] - s);
+                    Z[h] *= al; R[h] *= al;
+                    for (int e = 0; e < VEC; ++e) { A[h][e] *= al; B[h][e] *= al; }
+                    m[h] = s;
+                }
+                const float w = valid ? __builtin_amdgcn_exp2f(s - m[h]) : 0.f;
+                const float wt = w * t;
+                Z[h] += w;
+                R[h] += wt;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    A[h][e] = fmaf(w, vf[e], A[h][e]);
+                    B[h][e] = fmaf(wt, vf[e], B[h][e]);
+                }
+            }
+        }
+    }
+
+    // merge the token rows of this wave, then the waves through LDS
+    for (int off = LPT; off < 64; off *= 2)
+        for (int h = 0; h < G; ++h) {
+            const float m2 = __shfl_xor(m[h], off), Z2 = __shfl_xor(Z[h], off),
+                        R2 = __shfl_xor(R[h], off);
+            const float mn = fmaxf(m[h], m2);
+            const float a1 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+            const float a2 = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+            Z[h] = a1 * Z[h] + a2 * Z2;
+            R[h] = a1 * R[h] + a2 * R2;
+            for (int e = 0; e < VEC; ++e) {
+                const float A2 = __shfl_xor(A[h][e], off), B2 = __shfl_xor(B[h][e], off);
+                A[h][e] = a1 * A[h][e] + a2 * A2;
+                B[h][e] = a1 * B[h][e] + a2 * B2;
+            }
+            m[h] = mn;
+        }
+    __shared__ float red[kValuWaves][G][REC];
+    if (row == 0)
+        for (int h = 0; h < G; ++h) {
+            for (int e = 0; e < VEC; ++e) {
+                red[wave][h][sub * VEC + e] = A[h][e];
+                red[wave][h][D + sub * VEC + e] = B[h][e];
+            }
+            if (sub == 0) {
+                red[wave][h][2 * D] = m[h];
+                red[wave][h][2 * D + 1] = Z[h];
+                red[wave][h][2 * D + 2] = R[h];
+            }
+        }
+    __syncthreads();
+    finish_block<D, G, kValuWaves>(p, red, b, hk, unit, split_idx, nsp);
+}
+
+// ================================================================ merge ===
+
+// One workgroup per (batch, KV head): combine the split records of rows
+// that used more than one split and write o.
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
+    constexpr int REC = partial_floats(D);
+    const int unit = blockIdx.x;
+    const int b = unit / p.num_kv_heads;
+    const int hk = unit % p.num_kv_heads;
+    int L, nsp;
+    row_extent<PAGED>(p, b, L, nsp);
+    if (nsp <= 1) return;  // written by the split kernel
+    const float *recs = p.partials + (int64_t)unit * p.nsplit * G * REC;
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+        const int g = idx / D, e = idx % D;
+        float M = -INFINITY, Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
+        for (int c0 = 0; c0 < nsp; c0 += 4) {  // four records' loads in flight at once
+            float mm[4], zz[4], rr[4], aa[4], bb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float *rec = recs + (min(c0 + i, nsp - 1) * G + g) * REC;
+                const bool live = c0 + i < nsp;
+                mm[i] = live ? rec[2 * D] : -INFINITY;
+                zz[i] = rec[2 * D + 1];
+                rr[i] = rec[2 * D + 2];
+                aa[i] = rec[e];
+                bb[i] = rec[D + e];
+            }
+            const float Mn = fmaxf(fmaxf(M, fmaxf(mm[0], mm[1])), fmaxf(mm[2], mm[3]));
+            const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+            Z *= sc;
+            R *= sc;
+            A *= sc;
+            B *= sc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float al = mm[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[i] - Mn);
+                Z += al * zz[i];
+                R += al * rr[i];
+                A += al * aa[i];
+                B += al * bb[i];
+            }
+            M = Mn;
+        }
+        p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = finish(A, B, Z, R);
     }
 }
 
-template <typename KV, int D, int G>
-hipError_t launch_g(const DecodeParams &p, bool paged, int batch, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)batch * p.num_kv_heads * p.nsplit));
-    const dim3 block(64 * kDecodeWaves);
-    if (paged)
-        hipLaunchKernelGGL((decode_kernel<KV, D, G, true>), grid, block, 0, stream, p);
+template <int D, int G, bool PAGED>
+hipError_t launch_all(const DecodeParams &p, bool bf16, int batch, hipStream_t stream) {
+    const unsigned units = (unsigned)((int64_t)batch * p.num_kv_heads);
+    const dim3 grid((unsigned)((int64_t)units * p.nsplit));
+    if (bf16)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, G, PAGED>), grid, dim3(64 * mfma_waves<D, G>()), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((decode_kernel<KV, D, G, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_valu_kernel<D, G, PAGED>), grid, dim3(64 * kValuWaves), 0,
+                           stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.nsplit == 1) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<D, G, PAGED>), dim3(units), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename KV, int D>
-hipError_t launch_d(const DecodeParams &p, int group, bool paged, int batch, hipStream_t s) {
+template <int D, int G>
+hipError_t launch_g(const DecodeParams &p, bool bf16, bool paged, int batch, hipStream_t s) {
+    return paged ? launch_all<D, G, true>(p, bf16, batch, s)
+                 : launch_all<D, G, false>(p, bf16, batch, s);
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams &p, bool bf16, int group, bool paged, int batch,
+                    hipStream_t s) {
     switch (group) {
-        case 1: return launch_g<KV, D, 1>(p, paged, batch, s);
-        case 2: return launch_g<KV, D, 2>(p, paged, batch, s);
-        case 4: return launch_g<KV, D, 4>(p, paged, batch, s);
-        case 8: return launch_g<KV, D, 8>(p, paged, batch, s);
+        case 1: return launch_g<D, 1>(p, bf16, paged, batch, s);
+        case 2: return launch_g<D, 2>(p, bf16, paged, batch, s);
+        case 4: return launch_g<D, 4>(p, bf16, paged, batch, s);
+        case 8: return launch_g<D, 8>(p, bf16, paged, batch, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -455,13 +666,9 @@ hipError_t launch_d(const DecodeParams &p, int group, bool paged, int batch, hip
 
 hipError_t launch_decode(const DecodeParams &p, int kv_dtype, int d, int group, bool paged,
                          int batch, hipStream_t stream) {
-    if (kv_dtype == 1) {  // bf16
-        if (d == 128) return launch_d<uint16_t, 128>(p, group, paged, batch, stream);
-        if (d == 64) return launch_d<uint16_t, 64>(p, group, paged, batch, stream);
-    } else {
-        if (d == 128) return launch_d<float, 128>(p, group, paged, batch, stream);
-        if (d == 64) return launch_d<float, 64>(p, group, paged, batch, stream);
-    }
+    const bool bf16 = kv_dtype == 1;
+    if (d == 128) return launch_d<128>(p, bf16, group, paged, batch, stream);
+    if (d == 64) return launch_d<64>(p, bf16, group, paged, batch, stream);
     return hipErrorInvalidValue;
 }
 

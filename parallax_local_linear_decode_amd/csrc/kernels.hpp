@@ -11,11 +11,9 @@ namespace plx {
 // A[d], B[d], m, Z, R and one pad word (keeps records 16-byte aligned).
 __host__ __device__ constexpr int partial_floats(int d) { return 2 * d + 4; }
 
-// Tokens one wave consumes per step of the decode loop; also the page size
-// of the paged cache, so one step reads exactly one page.
+// Page size of the paged cache (tokens per block-table entry); also the
+// step of the fp32 decode loop, so one of its steps reads exactly one page.
 constexpr int kDecodeStepTokens = 16;
-// Waves per decode workgroup.
-constexpr int kDecodeWaves = 4;
 
 struct DecodeParams {
     const float *q;
@@ -31,11 +29,10 @@ struct DecodeParams {
     int32_t max_seq_len;
     int32_t max_blocks;
     int32_t num_kv_heads;
-    int32_t split;      // tokens per split (multiple of kDecodeWaves*kDecodeStepTokens)
+    int32_t split;      // tokens per split (a multiple of 256)
     int32_t nsplit;     // splits per (batch, kv head) in the grid
     float scale_log2;   // logit scale times log2(e): logits are kept in base 2
     float *partials;    // [B*Hkv*nsplit][G][partial_floats(d)] or null when nsplit == 1
-    uint32_t *counters; // [B*Hkv] arrival counters, zero between calls
 };
 
 struct PrefillParams {

@@ -66,9 +66,9 @@ def test_valid_decode_plan(lib):
     # a single split needs no workspace
     st, n = ws_size(lib, good_decode(split_tokens=4096))
     assert st == plx.PARALLAX_OK and n == 0
-    # explicit split: counters (rounded to 256 B) + one record per split and head
+    # explicit split: one record (A, B: d floats each; m, Z, R, pad) per split and head
     st, n = ws_size(lib, good_decode(split_tokens=1024))
-    assert n == 256 + 64 * 4 * 2 * (2 * 128 + 4) * 4
+    assert n == 64 * 4 * 2 * (2 * 128 + 4) * 4
 
 
 INVALID = plx.PARALLAX_ERR_INVALID_ARG
@@ -92,7 +92,8 @@ UNSUPP = plx.PARALLAX_ERR_UNSUPPORTED
     (dict(k_stride_t=132), UNSUPP, "16 bytes"),
     (dict(q_stride_h=130), UNSUPP, "16 bytes"),
     (dict(split_tokens=100), INVALID, "split_tokens"),
-    (dict(split_tokens=-64), INVALID, "split_tokens"),
+    (dict(split_tokens=64), INVALID, "split_tokens"),
+    (dict(split_tokens=-256), INVALID, "split_tokens"),
     (dict(block_table=FAKE, block_size=16, max_blocks_per_seq=256), INVALID, "seq_lens"),
     (dict(block_table=FAKE, seq_lens=FAKE, block_size=32, max_blocks_per_seq=256), UNSUPP,
      "block_size"),

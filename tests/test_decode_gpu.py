@@ -131,7 +131,7 @@ def test_ragged_lengths(gpu, kv_dtype, d, G):
     ref = oracle_decode(inp)
     inp = to(inp, gpu)
     tau = TAU_F32 * 5 if kv_dtype == torch.float32 else TAU_BF16
-    for split in (0, 64, 128):
+    for split in (0, 256):
         out = run(inp, split_tokens=split)
         assert_parity(out, ref, tau, None if kv_dtype == torch.float32 else RMS_DECODE_BF16,
                       what=f"ragged split={split}")
@@ -142,7 +142,7 @@ def test_split_choices_agree(gpu):
     inp = to(decode_inputs(3, 16, 8, 128, 3000, seed=7), gpu)
     ref = oracle_decode(inp)
     outs = []
-    for split in (64, 192, 320, 1024, 2048, 3008):
+    for split in (256, 512, 768, 1024, 2048, 3072):
         out = run(inp, split_tokens=split).clone()
         assert_parity(out, ref, TAU_BF16, RMS_DECODE_BF16, what=f"split={split}")
         outs.append(out)
@@ -158,16 +158,36 @@ def test_deterministic(gpu):
 
 
 def test_workspace_reuse_across_shapes(gpu):
-    """One workspace serves calls of different shapes back to back (the kernel
-    re-arms its counters)."""
-    ws = torch.zeros(1 << 24, dtype=torch.uint8, device=gpu)
-    for i, (B, L) in enumerate([(8, 4096), (2, 700), (8, 4096), (5, 1500)]):
+    """One workspace, filled with garbage first, serves calls of different
+    shapes back to back (arrival words from other calls count as zero)."""
+    ws = torch.randint(0, 256, (1 << 24,), dtype=torch.uint8, device=gpu)
+    for i, (B, L) in enumerate([(2, 700), (8, 4096), (2, 700), (12, 3000), (5, 1500)]):
         inp = to(decode_inputs(B, 16, 8, 128, L, seed=20 + i), gpu)
         out = run(inp, workspace=ws)
         assert_parity(out, oracle_decode(inp), TAU_BF16, RMS_DECODE_BF16, what=f"reuse {i}")
-    # the arrival counters (one uint32 per batch x KV head, first 256 bytes
-    # here) are re-armed by every call
-    assert int(ws[:256].count_nonzero()) == 0
+
+
+def test_graph_replay(gpu):
+    """A captured decode replays correctly several times, with eager calls on
+    the same workspace in between."""
+    inp = to(decode_inputs(4, 16, 8, 128, 2000, seed=30), gpu)
+    ref = oracle_decode(inp)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=gpu)
+    out = torch.empty((4, 16, 128), dtype=torch.float32, device=gpu)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        run(inp, workspace=ws, out=out)  # warm up on the capture stream
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            plx.parallax_decode(inp.q, inp.rho, inp.k, inp.v, scale=inp.scale, out=out,
+                                workspace=ws)
+    other = to(decode_inputs(2, 16, 8, 128, 900, seed=31), gpu)
+    for r in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_parity(out, ref, TAU_BF16, RMS_DECODE_BF16, what=f"replay {r}")
+        run(other, workspace=ws)  # an eager call of another shape in between
 
 
 # ------------------------------------------------------------------ paged ---
@@ -176,7 +196,7 @@ def test_paged_small(gpu):
     inp = paged_inputs(12, 16, 8, 128, ctx_lo=1, ctx_hi=700, seed=0, rho_zero_rows=3)
     ref = oracle_decode(inp)
     inp = to(inp, gpu)
-    for split in (0, 64, 256):
+    for split in (0, 256, 512):
         assert_parity(run(inp, split_tokens=split), ref, TAU_BF16, RMS_DECODE_BF16,
                       what=f"paged split={split}")
 
