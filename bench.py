@@ -256,6 +256,76 @@ def run_copy(args, torch, plx):
             "config": {"workload": f"copy {n} bytes"}, "roofline": None, "cpu_baseline": None}
 
 
+def prefill_flops(B, S, Hq, d):
+    """Algorithmic flops: per causal (query, key) pair and query head, the two
+    score products (q.k, rho.k) and the two value products (E v, E t v), each
+    2*d flops."""
+    return 4 * 2 * d * (S * (S + 1) // 2) * B * Hq
+
+
+def run_prefill(args, torch, plx):
+    import numpy as np
+    import oracle
+    from parallax_local_linear_decode_amd.workloads import host_array, prefill_inputs
+    B, S, Hq, Hkv, d = 4, 8192, 16, 8, 128
+    dev = torch.device("cuda:0")
+    q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, d, seed=0, device=dev)
+    out = torch.empty((B, S, Hq, d), dtype=torch.float32, device=dev)
+    import ctypes
+    lib = plx.load_library()
+    a = plx.PrefillArgs()
+    a.struct_size = ctypes.sizeof(plx.PrefillArgs)
+    a.batch, a.seq_len, a.num_q_heads, a.num_kv_heads, a.head_dim = B, S, Hq, Hkv, d
+    a.scale, a.causal = scale, 1
+    a.q, a.q_stride_b, a.q_stride_s, a.q_stride_h = q.data_ptr(), *q.stride()[:3]
+    a.rho, a.rho_stride_b, a.rho_stride_s, a.rho_stride_h = rho.data_ptr(), *rho.stride()[:3]
+    a.k, a.k_stride_b, a.k_stride_s, a.k_stride_h = k.data_ptr(), *k.stride()[:3]
+    a.v, a.v_stride_b, a.v_stride_s, a.v_stride_h = v.data_ptr(), *v.stride()[:3]
+    a.out, a.out_stride_b, a.out_stride_s, a.out_stride_h = out.data_ptr(), *out.stride()[:3]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(i):
+        st = lib.parallax_prefill(ctypes.byref(a), stream)
+        if st != 0:
+            plx._raise(st, lib)
+
+    launch(0)
+    torch.cuda.synchronize()
+    cpu = None
+    if args.cpu_baseline:
+        # sampled query rows of every (batch, head); their causal pairs scale
+        # the oracle's time to the whole workload
+        rng = np.random.default_rng(0)
+        rows = np.sort(rng.choice(S, 24, replace=False)).astype(np.int32)
+        hq, hr, hk, hv = (host_array(t) for t in (q, rho, k, v))
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        ref = oracle.prefill(hq, hr, hk, hv, scale, rows=rows, threads=threads)
+        secs = time.perf_counter() - t0
+        gate(out[:, rows.tolist()].double().cpu().numpy(), ref, 2e-2, 1e-2)
+        frac = float(np.sum(rows + 1)) / (S * (S + 1) / 2)
+        full = secs / frac
+        cpu = {"value": prefill_flops(B, S, Hq, d) / full / 1e12, "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle", "seconds_per_step": full,
+               "sample": f"{rows.size} query rows x all (batch, head), fp64 streaming form; "
+                         f"time scaled by causal pairs ({secs:.1f} s measured)"}
+    secs = time_launches(torch, launch, 1, args.steps, args.warmup)
+    per = secs / args.steps
+    tflops = prefill_flops(B, S, Hq, d) / per / 1e12
+    return {
+        "metric": "Parallax causal prefill TFLOP/s (% of bf16 MFMA peak)", "value": round(tflops, 1),
+        "unit": "TFLOP/s", "ms_per_step": per * 1e3, "dtype": "bf16",
+        "config": {"workload": "causal prefill: batch 4, seq 8192, 16 query / 8 KV heads, d 128, "
+                               "bf16 q/rho/k/v, fp32 out", "batch": B, "seq_len": S},
+        "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "tokens_per_s": B * S / per,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_for("prefill")},
+        "cpu_baseline": cpu,
+    }
+
+
 def gate(gpu, ref, tau, rms):
     import numpy as np
     ratio = float(np.max(np.abs(gpu - ref) / (1 + np.abs(ref))))
@@ -293,7 +363,7 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     plx.load_library()
     runner = {"decode": run_decode, "paged": run_paged, "sweep": run_sweep,
-              "copy": run_copy}.get(args.workload)
+              "copy": run_copy, "prefill": run_prefill}.get(args.workload)
     if runner is None:
         raise SystemExit(f"workload {args.workload} is not available")
     rec = runner(args, torch, plx)

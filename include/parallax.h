@@ -135,9 +135,10 @@ parallax_status_t parallax_decode(const parallax_decode_args_t *args, void *work
 /*
  * Causal prefill: row i of (b, h) attends to keys 0..i of KV head
  * h / (Hq/Hkv).  q, rho bf16 [B, S, Hq, d]; k, v bf16 [B, S, Hkv, d];
- * out fp32 [B, S, Hq, d].  causal must be 1.  Products run on the bf16
- * matrix cores with fp32 accumulation; the softmax numerators e^{s} and
- * e^{s} t are rounded to bf16 before they multiply V.
+ * out fp32 [B, S, Hq, d].  causal must be 1; head_dim must be 128; the GQA
+ * group Hq/Hkv must be 1, 2 or 4 (else PARALLAX_ERR_UNSUPPORTED).  Products
+ * run on the bf16 matrix cores with fp32 accumulation; the softmax
+ * numerators e^{s} and e^{s} t are rounded to bf16 before they multiply V.
  */
 typedef struct {
     uint32_t struct_size; /* = sizeof(parallax_prefill_args_t) */

@@ -149,6 +149,11 @@ parallax_status_t check_prefill(const parallax_prefill_args_t *a) {
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: only causal = 1 is supported");
     if (a->head_dim != 128)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 128)", a->head_dim);
+    const int group = a->num_q_heads / a->num_kv_heads;
+    if (group != 1 && group != 2 && group != 4)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: GQA group %d (supported: 1, 2, 4)", group);
+    if ((int64_t)a->batch * a->num_kv_heads * ((a->seq_len + 31) / 32) > 0x7fffffffLL)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: grid too large");
     if (!aligned16(a->q) || !aligned16(a->rho) || !aligned16(a->k) || !aligned16(a->v) ||
         !aligned16(a->out))
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: every pointer must be 16-byte aligned");

@@ -194,52 +194,63 @@ __global__ __launch_bounds__((64 * mfma_waves<D, G>())) void decode_mfma_kernel(
 
     const uint16_t *kc = static_cast<const uint16_t *>(p.k);
     const uint16_t *vc = static_cast<const uint16_t *>(p.v);
-    // Element offset of token j (already clamped to a valid token) of this (b, hk).
-    auto tok_k = [&](int j) -> int64_t {
-        if constexpr (PAGED) {
-            const int pg = p.block_table[(int64_t)b * p.max_blocks + j / kDecodeStepTokens];
-            return (int64_t)pg * p.k_s0 + (int64_t)hk * p.k_sh +
-                   (int64_t)(j % kDecodeStepTokens) * p.k_st;
-        } else {
-            return (int64_t)b * p.k_s0 + (int64_t)hk * p.k_sh + (int64_t)j * p.k_st;
-        }
+    // A step's 32 tokens start on a page boundary, so a paged step spans two
+    // pages; their ids are wave-uniform and are fetched a step ahead.
+    struct Pages {
+        int p0, p1;
     };
-    auto tok_v = [&](int j) -> int64_t {
+    auto step_pages = [&](int st) -> Pages {
+        Pages pg = {0, 0};
         if constexpr (PAGED) {
-            const int pg = p.block_table[(int64_t)b * p.max_blocks + j / kDecodeStepTokens];
-            return (int64_t)pg * p.v_s0 + (int64_t)hk * p.v_sh +
-                   (int64_t)(j % kDecodeStepTokens) * p.v_st;
+            const int base = t0 + st * kMfmaStep;
+            const int32_t *row = p.block_table + (int64_t)b * p.max_blocks;
+            pg.p0 = __builtin_amdgcn_readfirstlane(row[base / kDecodeStepTokens]);
+            pg.p1 = __builtin_amdgcn_readfirstlane(
+                row[min(base + kDecodeStepTokens, t1 - 1) / kDecodeStepTokens]);
+        }
+        return pg;
+    };
+    // Element offset of token j (clamped to [base, t1)) of this (b, hk).
+    auto tok_off = [&](int j, int base, const Pages &pg, int64_t s0, int64_t sh,
+                       int64_t stt) -> int64_t {
+        if constexpr (PAGED) {
+            const int pgid = j - base < kDecodeStepTokens ? pg.p0 : pg.p1;
+            return (int64_t)pgid * s0 + (int64_t)hk * sh + (int64_t)(j % kDecodeStepTokens) * stt;
         } else {
-            return (int64_t)b * p.v_s0 + (int64_t)hk * p.v_sh + (int64_t)j * p.v_st;
+            return (int64_t)b * s0 + (int64_t)hk * sh + (int64_t)j * stt;
         }
     };
 
     // Loads of one step: K straight into score-operand layout (lane c, g of
     // row block rb holds token 16*rb + c, head-dim values DQ*g + 8*ks ..),
     // V as coalesced 16-byte row pieces.  Tokens past t1 re-read token t1-1.
-    auto issue_k = [&](int st, uint4 (&kr)[2][KS]) {
+    auto issue_k = [&](int st, const Pages &pg, uint4 (&kr)[2][KS]) {
         const int base = t0 + st * kMfmaStep;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            const int64_t off = tok_k(min(base + 16 * rb + c, t1 - 1)) + DQ * g;
+            const int j = min(base + 16 * rb + c, t1 - 1);
+            const int64_t off = tok_off(j, base, pg, p.k_s0, p.k_sh, p.k_st) + DQ * g;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) kr[rb][ks] = load16(kc + off + 8 * ks);
         }
     };
-    auto issue_v = [&](int st, uint4 (&vr)[VLD]) {
+    auto issue_v = [&](int st, const Pages &pg, uint4 (&vr)[VLD]) {
         const int base = t0 + st * kMfmaStep;
 #pragma unroll
         for (int u = 0; u < VLD; ++u) {
             const int j = min(base + RPL * u + lane / LPR, t1 - 1);
-            vr[u] = load16(vc + tok_v(j) + 8 * (lane % LPR));
+            vr[u] = load16(vc + tok_off(j, base, pg, p.v_s0, p.v_sh, p.v_st) + 8 * (lane % LPR));
         }
     };
 
     // the first step's loads go out before the query-side setup below
     uint4 kr[2][KS], vr[VLD];
+    Pages pg_next = {0, 0};
     if (wave < nsteps) {
-        issue_k(wave, kr);
-        issue_v(wave, vr);
+        const Pages pg = step_pages(wave);
+        issue_k(wave, pg, kr);
+        issue_v(wave, pg, vr);
+        if (wave + kMfmaWaves < nsteps) pg_next = step_pages(wave + kMfmaWaves);
     }
 
     // ---- score-side operands: column c of set s is q or rho of head
@@ -278,12 +289,14 @@ __global__ __launch_bounds__((64 * mfma_waves<D, G>())) void decode_mfma_kernel(
 
     auto process = [&](int st, int nst, uint4 (&kr)[2][KS], uint4 (&vr)[VLD]) {
         const int base = t0 + st * kMfmaStep;
+        const Pages pg = pg_next;  // pages of step nst
+        if (nst >= 0 && nst + kMfmaWaves < nsteps) pg_next = step_pages(nst + kMfmaWaves);
         // V rows into the wave's LDS tile (row-major, padded rows)
 #pragma unroll
         for (int u = 0; u < VLD; ++u)
             *reinterpret_cast<uint4 *>(vt + (RPL * u + lane / LPR) * VROW + 16 * (lane % LPR)) =
                 vr[u];
-        if (nst >= 0) issue_v(nst, vr);
+        if (nst >= 0) issue_v(nst, pg, vr);
 
         // scores: d1[s][rb] lane (c, g) = column c, tokens 16*rb + 4*g + j
         f32x4_t d1[NCS][2];
@@ -298,7 +311,7 @@ __global__ __launch_bounds__((64 * mfma_waves<D, G>())) void decode_mfma_kernel(
                         __builtin_bit_cast(bf16x8_t, kr[rb][ks]), bq[s][ks], a, 0, 0, 0);
                 d1[s][rb] = a;
             }
-        if (nst >= 0) issue_k(nst, kr);
+        if (nst >= 0) issue_k(nst, pg, kr);
 
         // k-slot r (0..7) of this lane's group <-> token of the step
         bool valid[8];

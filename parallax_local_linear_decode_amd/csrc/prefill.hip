@@ -1,8 +1,273 @@
-// prefill.hip -- causal Parallax prefill for gfx950 (matrix-core kernel: in progress).
+// prefill.hip -- causal Parallax prefill for gfx950 (CDNA4), bf16 matrix cores.
+//
+// Row i of (batch b, query head h) attends to keys 0..i of KV head h/G and
+// computes o_i = o_SA,i - S_KV^(i) rho_i (page "Parallax: Parameterized Local
+// Linear Attention Gives Transformers a 'Second Eye'", section 1.3), through
+// the same sums as decode: with s_ij = scale q_i.k_j and t_ij = rho_i.k_j,
+//   Z_i = sum_j e^{s_ij}, R_i = sum_j e^{s_ij} t_ij,
+//   A_i = sum_j e^{s_ij} v_j, B_i = sum_j e^{s_ij} t_ij v_j,
+//   o_i = a - (b - a r),  a = A/Z, r = R/Z, b = B/Z.
+// Both products are dense matrix products over a shared K/V tile (section
+// 2.2 of that page: the covariance work is arranged for the matrix cores):
+//   scores  D1[key][col] = K[key][:] . X[col][:]   X = the wave's 32 q rows
+//           and its 32 rho rows (64 columns, 4 blocks of 16);
+//   sums    D2[d][col]   = sum_key V[key][d] . P[key][col]   P = E (32 cols)
+//           and E*T (32 cols), E = e^{s - m} rounded to bf16;
+// all as 16x16x32 bf16 MFMAs with fp32 accumulation.  s and t of the same
+// query row land in the same lane, so the softmax needs no data movement
+// except the row max across the four lane groups; the rescale of a row's
+// sums is a per-lane multiply.
+//
+// Workgroup: 4 waves (one per SIMD; each holds 32 query rows, its Q / rho
+// operands and 128 accumulators) covering 128/G rows of each of the G query
+// heads of one KV head, so every K/V tile in LDS serves the whole GQA group.
+// K/V tiles of 32 keys are double-buffered in LDS (one barrier per tile, the
+// next tile's global loads in flight during the current tile's math).  V
+// reaches the MFMA through ds_read_b64_tr_b16.  Query blocks are scheduled
+// longest (highest causal row) first; tiles past a wave's last row are skipped.
 #include "kernels.hpp"
 
-namespace plx {
+#include <math.h>
 
-hipError_t launch_prefill(const PrefillParams &, int, hipStream_t) { return hipErrorNotSupported; }
+namespace plx {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kPfWaves = 4;               // waves per workgroup
+constexpr int kPfRows = 32;               // query rows per wave
+constexpr int kPfKeys = 32;               // keys per tile
+constexpr int kPfD = 128;                 // head dim
+constexpr int kPfRowBytes = 2 * kPfD + 16;  // LDS bytes per tile row (16-byte pad)
+constexpr float kSlack = 8.0f;            // base-2 headroom before a row's reference max moves
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int G>
+__global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p) {
+    constexpr int D = kPfD;
+    constexpr int KS = D / 32;                      // score MFMAs per 16-key block
+    constexpr int DB = D / 16;                      // 16-row blocks of the sums
+    constexpr int WPH = kPfWaves / G;               // waves per query head
+    constexpr int QB = kPfRows * WPH;               // query rows per head per workgroup
+    constexpr int TILE = kPfKeys * kPfRowBytes;
+
+    __shared__ __attribute__((aligned(16))) unsigned char ktile[2][TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char vtile[2][TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int S = p.seq_len;
+
+    const int units = p.batch * p.num_kv_heads;
+    const int nqb = (S + QB - 1) / QB;
+    const int qb = nqb - 1 - (int)(blockIdx.x / units);  // longest causal rows first
+    const int unit = blockIdx.x % units;
+    const int b = unit / p.num_kv_heads;
+    const int hk = unit % p.num_kv_heads;
+    const int head = hk * G + wave / WPH;
+    const int r0 = qb * QB + (wave % WPH) * kPfRows;  // first query row of this wave
+    const int key_end = min(S, (qb + 1) * QB);        // keys this workgroup needs
+    const int ntiles = (key_end + kPfKeys - 1) / kPfKeys;
+    const int wave_tiles = min(ntiles, (min(S, r0 + kPfRows) + kPfKeys - 1) / kPfKeys);
+
+    // ---- cooperative tile loads: thread t moves 16 bytes of key 16u + t/16
+    const uint16_t *kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
+    const uint16_t *vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
+    uint4 kst[2], vst[2];
+    auto issue = [&](int t) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int key = min(t * kPfKeys + 16 * u + tid / 16, S - 1);
+            kst[u] = ld16(kg + (int64_t)key * p.k_ss + 8 * (tid % 16));
+            vst[u] = ld16(vg + (int64_t)key * p.v_ss + 8 * (tid % 16));
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int off = (16 * u + tid / 16) * kPfRowBytes + 16 * (tid % 16);
+            *reinterpret_cast<uint4 *>(ktile[buf] + off) = kst[u];
+            *reinterpret_cast<uint4 *>(vtile[buf] + off) = vst[u];
+        }
+    };
+
+    issue(0);
+
+    // ---- query-side operands: column block cb < 2 holds q rows r0 + 16cb + c,
+    // cb >= 2 the rho rows of the same queries; head-dim value 32g + 8ks + i
+    // sits in k-slot 8g + i of score MFMA ks (the same slots the K operand uses)
+    bf16x8_t xop[4][KS];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const int row = min(r0 + 16 * (cb & 1) + c, S - 1);
+        const uint16_t *src = cb < 2 ? p.q + (int64_t)b * p.q_sb + (int64_t)row * p.q_ss +
+                                           (int64_t)head * p.q_sh
+                                     : p.rho + (int64_t)b * p.r_sb + (int64_t)row * p.r_ss +
+                                           (int64_t)head * p.r_sh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            xop[cb][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + 32 * g + 8 * ks));
+    }
+
+    f32x4_t acc[DB][4];  // [d block][column block: E rows 0-15, 16-31, E*T rows 0-15, 16-31]
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[db][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float mref[2] = {-INFINITY, -INFINITY};  // per query row (this lane's column)
+    float zs[2] = {0.f, 0.f}, rs[2] = {0.f, 0.f};
+
+    store(0);
+    if (ntiles > 1) issue(1);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t < wave_tiles) {
+            const unsigned char *kt = ktile[buf];
+            const unsigned char *vt = vtile[buf];
+            // scores and probe projections: d1[rb][cb] lane (c, g) = column c of
+            // block cb, keys 32t + 16rb + 4g + j
+            f32x4_t d1[2][4];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8_t kop = __builtin_bit_cast(
+                        bf16x8_t, ld16(kt + (16 * rb + c) * kPfRowBytes + 64 * g + 16 * ks));
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb)
+                        d1[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, xop[cb][ks],
+                                                                             d1[rb][cb], 0, 0, 0);
+                }
+            }
+            // softmax numerators of the two query blocks; k-slot r of the value
+            // MFMA holds key 4g + r (r < 4) or 16 + 4g + r - 4 of the tile
+            bf16x8_t pop[4];
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc) {
+                const int qi = r0 + 16 * qc + c;
+                float s2[8], tt[8];
+                float tmax = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int key = t * kPfKeys + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4);
+                    const float sv = (r < 4 ? d1[0][qc][r] : d1[1][qc][r - 4]) * p.scale_log2;
+                    tt[r] = r < 4 ? d1[0][qc + 2][r] : d1[1][qc + 2][r - 4];
+                    s2[r] = key <= qi && key < S ? sv : -INFINITY;
+                    tmax = fmaxf(tmax, s2[r]);
+                }
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                if (tmax > mref[qc] + kSlack) {  // rare: move this row's reference max
+                    const float al = __builtin_amdgcn_exp2f(mref[qc] - tmax);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        acc[db][qc] *= al;
+                        acc[db][qc + 2] *= al;
+                    }
+                    zs[qc] *= al;
+                    rs[qc] *= al;
+                    mref[qc] = tmax;
+                }
+                uint32_t ew[4], etw[4];
+#pragma unroll
+                for (int r = 0; r < 8; r += 2) {
+                    const float e0 = __builtin_amdgcn_exp2f(s2[r] - mref[qc]);
+                    const float e1 = __builtin_amdgcn_exp2f(s2[r + 1] - mref[qc]);
+                    ew[r / 2] = pack_bf16x2(e0, e1);
+                    etw[r / 2] = pack_bf16x2(e0 * tt[r], e1 * tt[r + 1]);
+                    zs[qc] += lo_f(ew[r / 2]) + hi_f(ew[r / 2]);
+                    rs[qc] += lo_f(etw[r / 2]) + hi_f(etw[r / 2]);
+                }
+                pop[qc] = __builtin_bit_cast(bf16x8_t, uint4{ew[0], ew[1], ew[2], ew[3]});
+                pop[qc + 2] = __builtin_bit_cast(bf16x8_t, uint4{etw[0], etw[1], etw[2], etw[3]});
+            }
+            // value sums: V^T operand rows d = 16db + c, read transposed from LDS
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+                const int col = 16 * db + 4 * (c % 4);
+                const unsigned char *a0 = vt + (4 * g + c / 4) * kPfRowBytes + 2 * col;
+                const unsigned char *a1 = vt + (16 + 4 * g + c / 4) * kPfRowBytes + 2 * col;
+                const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a0);
+                const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a1);
+                const bf16x8_t vop = __builtin_bit_cast(
+                    bf16x8_t, i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb)
+                    acc[db][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[cb], acc[db][cb],
+                                                                          0, 0, 0);
+            }
+        }
+        if (t + 1 < ntiles) {
+            store(buf ^ 1);  // tile t+1; its buffer held tile t-1, finished before the last barrier
+            if (t + 2 < ntiles) issue(t + 2);
+        }
+        __syncthreads();
+    }
+
+    // ---- o = a - (b - a r) per query row; lane (c, g) holds d = 16db + 4g + j
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+        float Z = zs[qc], R = rs[qc];
+        Z += __shfl_xor(Z, 16);
+        Z += __shfl_xor(Z, 32);
+        R += __shfl_xor(R, 16);
+        R += __shfl_xor(R, 32);
+        const int qi = r0 + 16 * qc + c;
+        if (qi >= S) continue;
+        const float inv = 1.0f / Z;
+        const float r = R * inv;
+        float *orow = p.out + (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)head * p.o_sh;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = acc[db][qc][j] * inv, bb = acc[db][qc + 2][j] * inv;
+                o[j] = a - (bb - a * r);
+            }
+            *reinterpret_cast<float4 *>(orow + 16 * db + 4 * g) = float4{o[0], o[1], o[2], o[3]};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream) {
+    if (d != kPfD) return hipErrorInvalidValue;
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const int units = p.batch * p.num_kv_heads;
+    const int qb_rows = kPfRows * kPfWaves / G;
+    const dim3 grid((unsigned)(units * ((p.seq_len + qb_rows - 1) / qb_rows)));
+    const dim3 block(64 * kPfWaves);
+    switch (G) {
+        case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, block, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, block, 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 }  // namespace plx

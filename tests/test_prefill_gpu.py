@@ -1,0 +1,94 @@
+"""GPU parity of parallax_prefill (causal, bf16 matrix cores) against the
+fp64 oracle, through the C ABI.
+
+Small cases compare every row (ragged sequence lengths around the 32-key
+tile and 64-row block edges, GQA groups 1/2/4); the full-size workload
+(batch 4, 8192 tokens, 16 query / 8 KV heads, d = 128) compares sampled rows.
+"""
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import parallax_local_linear_decode_amd as plx
+from parallax_local_linear_decode_amd.workloads import host_array, prefill_inputs
+
+from helpers import RMS_PREFILL, TAU_BF16, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def run(q, rho, k, v, scale):
+    out = plx.parallax_prefill(q, rho, k, v, scale=scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def host(*ts):
+    return [host_array(t) for t in ts]
+
+
+@pytest.mark.parametrize("S", [1, 17, 31, 32, 33, 64, 100, 257])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2), (8, 2)])
+def test_small_all_rows(gpu, S, Hq, Hkv):
+    q, rho, k, v, scale = prefill_inputs(2, S, Hq, Hkv, 128, seed=S * 10 + Hq)
+    ref = oracle.prefill(*host(q, rho, k, v), scale)
+    out = run(*(t.to(gpu) for t in (q, rho, k, v)), scale)
+    assert_parity(out, ref, TAU_BF16, RMS_PREFILL, what=f"S={S} {Hq}/{Hkv}")
+
+
+def test_first_row_is_first_value(gpu):
+    q, rho, k, v, scale = prefill_inputs(2, 70, 4, 2, 128, seed=5)
+    out = run(*(t.to(gpu) for t in (q, rho, k, v)), scale)
+    vv = v.float()
+    for h in range(4):
+        assert (out[:, 0, h].cpu() - vv[:, 0, h // 2]).abs().max().item() < 1e-5
+
+
+def test_rho_zero_is_causal_softmax(gpu):
+    q, rho, k, v, scale = prefill_inputs(1, 150, 2, 1, 128, seed=6)
+    rho = torch.zeros_like(rho)
+    out = run(*(t.to(gpu) for t in (q, rho, k, v)), scale)
+    qq, kk, vv = (t.double().numpy()[0] for t in (q, k, v))
+    S = 150
+    mask = np.tril(np.ones((S, S), dtype=bool))
+    for h in range(2):
+        logits = scale * qq[:, h] @ kk[:, 0].T
+        p = scipy.special.softmax(np.where(mask, logits, -np.inf), axis=1)
+        assert_parity(out[0, :, h], p @ vv[:, 0], TAU_BF16, RMS_PREFILL, what=f"rho=0 h={h}")
+
+
+def test_correlated_values(gpu):
+    """V = K M^T + noise makes the covariance branch large; every row checked."""
+    q, rho, k, v, scale = prefill_inputs(1, 300, 4, 2, 128, seed=7)
+    g = torch.Generator().manual_seed(8)
+    M = torch.randn(128, 128, generator=g) / 128 ** 0.5
+    v = (k.float() @ M.T + 0.1 * torch.randn(k.shape, generator=g)).to(torch.bfloat16)
+    rho = (3.0 * rho.float()).to(torch.bfloat16)
+    ref = oracle.prefill(*host(q, rho, k, v), scale)
+    out = run(*(t.to(gpu) for t in (q, rho, k, v)), scale)
+    assert_parity(out, ref, TAU_BF16, RMS_PREFILL, what="correlated")
+
+
+def test_deterministic(gpu):
+    q, rho, k, v, scale = (t.to(gpu) if isinstance(t, torch.Tensor) else t
+                           for t in prefill_inputs(2, 500, 4, 2, 128, seed=9))
+    first = run(q, rho, k, v, scale).clone()
+    for _ in range(5):
+        assert torch.equal(run(q, rho, k, v, scale), first)
+
+
+@pytest.mark.slow
+def test_full_size_sampled_rows(gpu):
+    """Batch 4, 8192 tokens, 16/8 heads, d = 128: rows at the tile, block and
+    sequence edges plus 32 random rows, for every (batch, head)."""
+    B, S, Hq, Hkv = 4, 8192, 16, 8
+    q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, 128, seed=0, device=gpu)
+    out = run(q, rho, k, v, scale)
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, 4095, 4096, 8190, 8191] +
+                      list(rng.integers(0, S, 32))))
+    ref = oracle.prefill(*host(q, rho, k, v), scale, rows=np.array(rows, dtype=np.int32))
+    assert_parity(out[:, rows], ref, TAU_BF16, RMS_PREFILL, what="prefill full size")
