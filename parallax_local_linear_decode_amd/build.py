@@ -18,10 +18,14 @@ LIB = os.path.join(PKG, "libparallax.so")
 SOURCES = ["api.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 
-# Packed fp32 VALU instructions are kept out of the generated code.
+# Packed fp32 VALU instructions are kept out of the generated code.  MFMA
+# accumulators are allocated in the VGPR form: the kernels' accumulators are
+# updated by VALU code too (rescaling), and with the AGPR form the compiler
+# shuttles them between register files every loop iteration.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

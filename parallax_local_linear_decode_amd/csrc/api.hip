@@ -33,8 +33,9 @@ bool bytes16(int64_t stride_elems, int64_t elem_size) {
 // Splits are whole numbers of 256 tokens: 8 waves x 32-token steps of the
 // bf16 kernel (and 4 x 16-token steps x 4 of the fp32 kernel).
 constexpr int kSplitQuantum = 256;
-// About two workgroups per CU of a 256-CU MI355X in one launch.
-constexpr int64_t kTargetWorkgroups = 512;
+// About one 8-wave workgroup per CU of a 256-CU MI355X: more, shorter splits
+// lose more to per-workgroup setup and to the merge than they gain.
+constexpr int64_t kTargetWorkgroups = 256;
 // Longest split: bounds the tail left by the longest rows of a ragged batch.
 constexpr int kMaxSplit = 4096;
 

@@ -29,6 +29,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace plx {
 namespace {
 
@@ -51,14 +53,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf16x2_t r = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, r);
 }
-__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Max over the four 16-lane groups (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float group_max(float x) {
+    const int xi = __builtin_bit_cast(int, x);
+    auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);  // rows 0<->1, 2<->3
+    x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+    const int yi = __builtin_bit_cast(int, x);
+    auto b2 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);  // halves 0<->1
+    return fmaxf(__builtin_bit_cast(float, (int)b2[0]), __builtin_bit_cast(float, (int)b2[1]));
+}
 
 template <int G>
 __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p) {
     constexpr int D = kPfD;
     constexpr int KS = D / 32;                      // score MFMAs per 16-key block
-    constexpr int DB = D / 16;                      // 16-row blocks of the sums
+    constexpr int DB = D / 16;                      // 16-row blocks of the value sums
     constexpr int WPH = kPfWaves / G;               // waves per query head
     constexpr int QB = kPfRows * WPH;               // query rows per head per workgroup
     constexpr int TILE = kPfKeys * kPfRowBytes;
@@ -72,6 +82,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
     const int c = lane & 15;
     const int g = lane >> 4;
     const int S = p.seq_len;
+    const float c2 = p.scale_log2;
 
     const int units = p.batch * p.num_kv_heads;
     const int nqb = (S + QB - 1) / QB;
@@ -85,28 +96,35 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
     const int ntiles = (key_end + kPfKeys - 1) / kPfKeys;
     const int wave_tiles = min(ntiles, (min(S, r0 + kPfRows) + kPfKeys - 1) / kPfKeys);
 
-    // ---- cooperative tile loads: thread t moves 16 bytes of key 16u + t/16
+    // ---- cooperative tile loads: thread t moves 16 bytes of key 16u + t/16.
+    // K runs two tiles ahead of the math and V one tile ahead, so the scores
+    // of tile t+1 can be computed while tile t's softmax runs.
     const uint16_t *kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
     const uint16_t *vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
     uint4 kst[2], vst[2];
-    auto issue = [&](int t) {
+    auto issue_k = [&](int t) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int key = min(t * kPfKeys + 16 * u + tid / 16, S - 1);
             kst[u] = ld16(kg + (int64_t)key * p.k_ss + 8 * (tid % 16));
+        }
+    };
+    auto issue_v = [&](int t) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int key = min(t * kPfKeys + 16 * u + tid / 16, S - 1);
             vst[u] = ld16(vg + (int64_t)key * p.v_ss + 8 * (tid % 16));
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](unsigned char *tile, const uint4 (&st)[2]) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int off = (16 * u + tid / 16) * kPfRowBytes + 16 * (tid % 16);
-            *reinterpret_cast<uint4 *>(ktile[buf] + off) = kst[u];
-            *reinterpret_cast<uint4 *>(vtile[buf] + off) = vst[u];
-        }
+        for (int u = 0; u < 2; ++u)
+            *reinterpret_cast<uint4 *>(tile + (16 * u + tid / 16) * kPfRowBytes + 16 * (tid % 16)) =
+                st[u];
     };
 
-    issue(0);
+    issue_k(0);
+    issue_v(0);
 
     // ---- query-side operands: column block cb < 2 holds q rows r0 + 16cb + c,
     // cb >= 2 the rho rows of the same queries; head-dim value 32g + 8ks + i
@@ -124,120 +142,151 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
             xop[cb][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + 32 * g + 8 * ks));
     }
 
-    f32x4_t acc[DB][4];  // [d block][column block: E rows 0-15, 16-31, E*T rows 0-15, 16-31]
+    // Value sums: acc[db][cb] = D2 rows d = 16db + 4g + j, column c of block
+    // cb (E rows 0-15, 16-31, E*T rows 0-15, 16-31).  Block db = DB multiplies
+    // a tile of ones, so its rows carry Z (cb < 2) and R (cb >= 2).
+    f32x4_t acc[DB + 1][4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db <= DB; ++db)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) acc[db][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mref[2] = {-INFINITY, -INFINITY};  // per query row (this lane's column)
-    float zs[2] = {0.f, 0.f}, rs[2] = {0.f, 0.f};
+    float mref[2] = {-INFINITY, -INFINITY};  // base-2 reference max per query row
 
-    store(0);
-    if (ntiles > 1) issue(1);
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t < wave_tiles) {
-            const unsigned char *kt = ktile[buf];
-            const unsigned char *vt = vtile[buf];
-            // scores and probe projections: d1[rb][cb] lane (c, g) = column c of
-            // block cb, keys 32t + 16rb + 4g + j
-            f32x4_t d1[2][4];
+    auto scores = [&](int t, f32x4_t (&d1)[2][4]) {
+        const unsigned char *kt = ktile[t & 1];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8_t kop = __builtin_bit_cast(
-                        bf16x8_t, ld16(kt + (16 * rb + c) * kPfRowBytes + 64 * g + 16 * ks));
-#pragma unroll
-                    for (int cb = 0; cb < 4; ++cb)
-                        d1[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, xop[cb][ks],
-                                                                             d1[rb][cb], 0, 0, 0);
-                }
-            }
-            // softmax numerators of the two query blocks; k-slot r of the value
-            // MFMA holds key 4g + r (r < 4) or 16 + 4g + r - 4 of the tile
-            bf16x8_t pop[4];
-#pragma unroll
-            for (int qc = 0; qc < 2; ++qc) {
-                const int qi = r0 + 16 * qc + c;
-                float s2[8], tt[8];
-                float tmax = -INFINITY;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int key = t * kPfKeys + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4);
-                    const float sv = (r < 4 ? d1[0][qc][r] : d1[1][qc][r - 4]) * p.scale_log2;
-                    tt[r] = r < 4 ? d1[0][qc + 2][r] : d1[1][qc + 2][r - 4];
-                    s2[r] = key <= qi && key < S ? sv : -INFINITY;
-                    tmax = fmaxf(tmax, s2[r]);
-                }
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                if (tmax > mref[qc] + kSlack) {  // rare: move this row's reference max
-                    const float al = __builtin_amdgcn_exp2f(mref[qc] - tmax);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        acc[db][qc] *= al;
-                        acc[db][qc + 2] *= al;
-                    }
-                    zs[qc] *= al;
-                    rs[qc] *= al;
-                    mref[qc] = tmax;
-                }
-                uint32_t ew[4], etw[4];
-#pragma unroll
-                for (int r = 0; r < 8; r += 2) {
-                    const float e0 = __builtin_amdgcn_exp2f(s2[r] - mref[qc]);
-                    const float e1 = __builtin_amdgcn_exp2f(s2[r + 1] - mref[qc]);
-                    ew[r / 2] = pack_bf16x2(e0, e1);
-                    etw[r / 2] = pack_bf16x2(e0 * tt[r], e1 * tt[r + 1]);
-                    zs[qc] += lo_f(ew[r / 2]) + hi_f(ew[r / 2]);
-                    rs[qc] += lo_f(etw[r / 2]) + hi_f(etw[r / 2]);
-                }
-                pop[qc] = __builtin_bit_cast(bf16x8_t, uint4{ew[0], ew[1], ew[2], ew[3]});
-                pop[qc + 2] = __builtin_bit_cast(bf16x8_t, uint4{etw[0], etw[1], etw[2], etw[3]});
-            }
-            // value sums: V^T operand rows d = 16db + c, read transposed from LDS
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-                const int col = 16 * db + 4 * (c % 4);
-                const unsigned char *a0 = vt + (4 * g + c / 4) * kPfRowBytes + 2 * col;
-                const unsigned char *a1 = vt + (16 + 4 * g + c / 4) * kPfRowBytes + 2 * col;
-                const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a0);
-                const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a1);
-                const bf16x8_t vop = __builtin_bit_cast(
-                    bf16x8_t, i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t kop = __builtin_bit_cast(
+                    bf16x8_t, ld16(kt + (16 * rb + c) * kPfRowBytes + 64 * g + 16 * ks));
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb)
-                    acc[db][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[cb], acc[db][cb],
-                                                                          0, 0, 0);
+                    d1[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, xop[cb][ks],
+                                                                         d1[rb][cb], 0, 0, 0);
             }
         }
-        if (t + 1 < ntiles) {
-            store(buf ^ 1);  // tile t+1; its buffer held tile t-1, finished before the last barrier
-            if (t + 2 < ntiles) issue(t + 2);
+    };
+
+    // Softmax numerators of tile t: E = 2^(c2 s - m) and E*T in bf16, as the
+    // B operands of the value MFMAs; k-slot r holds key 4g + r (r < 4) or
+    // 16 + 4g + r - 4 of the tile.  MASK: the tile crosses the diagonal or S.
+    auto numerators = [&](int t, const f32x4_t (&d1)[2][4], bf16x8_t (&pop)[4], auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+            const int qi = r0 + 16 * qc + c;
+            float sv[8];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                sv[r] = r < 4 ? d1[0][qc][r] : d1[1][qc][r - 4];
+                if constexpr (MASK) {
+                    const int key = t * kPfKeys + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4);
+                    sv[r] = key <= qi && key < S ? sv[r] : -INFINITY;
+                }
+                tmax = fmaxf(tmax, sv[r]);
+            }
+            const float tm2 = group_max(tmax) * c2;
+            if (tm2 > mref[qc] + kSlack) {  // rare: move this row's reference max
+                const float al = __builtin_amdgcn_exp2f(mref[qc] - tm2);
+#pragma unroll
+                for (int db = 0; db <= DB; ++db) {
+                    acc[db][qc] *= al;
+                    acc[db][qc + 2] *= al;
+                }
+                mref[qc] = tm2;
+            }
+            uint32_t ew[4], etw[4];
+#pragma unroll
+            for (int r = 0; r < 8; r += 2) {
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[r], c2, -mref[qc]));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, -mref[qc]));
+                const float t0 = r < 4 ? d1[0][qc + 2][r] : d1[1][qc + 2][r - 4];
+                const float t1 = r < 4 ? d1[0][qc + 2][r + 1] : d1[1][qc + 2][r - 3];
+                ew[r / 2] = pack_bf16x2(e0, e1);
+                etw[r / 2] = pack_bf16x2(e0 * t0, e1 * t1);
+            }
+            pop[qc] = __builtin_bit_cast(bf16x8_t, uint4{ew[0], ew[1], ew[2], ew[3]});
+            pop[qc + 2] = __builtin_bit_cast(bf16x8_t, uint4{etw[0], etw[1], etw[2], etw[3]});
         }
+    };
+
+    auto value_sums = [&](int t, const bf16x8_t (&pop)[4]) {
+        const unsigned char *vt = vtile[t & 1];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+            const int col = 16 * db + 4 * (c % 4);
+            const unsigned char *a0 = vt + (4 * g + c / 4) * kPfRowBytes + 2 * col;
+            const unsigned char *a1 = vt + (16 + 4 * g + c / 4) * kPfRowBytes + 2 * col;
+            const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a0);
+            const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a1);
+            const bf16x8_t vop = __builtin_bit_cast(
+                bf16x8_t, i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                acc[db][cb] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[cb], acc[db][cb], 0, 0, 0);
+        }
+        const bf16x8_t ones = __builtin_bit_cast(
+            bf16x8_t, uint4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+            acc[DB][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[cb], acc[DB][cb], 0, 0, 0);
+    };
+
+    // prologue: K tiles 0 and 1 and V tile 0 in LDS, K tile 2 and V tile 1 in flight
+    store(ktile[0], kst);
+    store(vtile[0], vst);
+    if (ntiles > 1) {
+        issue_k(1);
+        store(ktile[1], kst);
+    }
+    if (ntiles > 2) issue_k(2);
+    if (ntiles > 1) issue_v(1);
+    __syncthreads();
+
+    f32x4_t d1[2][4];
+    if (wave_tiles > 0) scores(0, d1);
+    for (int t = 0; t < ntiles; ++t) {
+        if (t < wave_tiles) {
+            f32x4_t d1n[2][4];
+            if (t + 1 < wave_tiles) scores(t + 1, d1n);  // overlaps the softmax below
+            bf16x8_t pop[4];
+            const bool full = t * kPfKeys + kPfKeys - 1 <= r0 && t * kPfKeys + kPfKeys <= S;
+            if (full)
+                numerators(t, d1, pop, std::false_type{});
+            else
+                numerators(t, d1, pop, std::true_type{});
+            value_sums(t, pop);
+            if (t + 1 < wave_tiles) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = d1n[rb][cb];
+            }
+        }
+        // K tile t+2 replaces tile t (last read by scores(t) one iteration ago);
+        // V tile t+1 replaces tile t-1 (last read by value_sums(t-1))
+        if (t + 2 < ntiles) store(ktile[t & 1], kst);
+        if (t + 1 < ntiles) store(vtile[(t + 1) & 1], vst);
+        if (t + 3 < ntiles) issue_k(t + 3);
+        if (t + 2 < ntiles) issue_v(t + 2);
         __syncthreads();
     }
 
     // ---- o = a - (b - a r) per query row; lane (c, g) holds d = 16db + 4g + j
 #pragma unroll
     for (int qc = 0; qc < 2; ++qc) {
-        float Z = zs[qc], R = rs[qc];
-        Z += __shfl_xor(Z, 16);
-        Z += __shfl_xor(Z, 32);
-        R += __shfl_xor(R, 16);
-        R += __shfl_xor(R, 32);
         const int qi = r0 + 16 * qc + c;
         if (qi >= S) continue;
-        const float inv = 1.0f / Z;
-        const float r = R * inv;
+        const float inv = 1.0f / acc[DB][qc][0];
+        const float r = acc[DB][qc + 2][0] * inv;
         float *orow = p.out + (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)head * p.o_sh;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
