@@ -21,10 +21,13 @@
 // Workgroup: 4 waves (one per SIMD; each holds 32 query rows, its Q / rho
 // operands and 128 accumulators) covering 128/G rows of each of the G query
 // heads of one KV head, so every K/V tile in LDS serves the whole GQA group.
-// K/V tiles of 32 keys are double-buffered in LDS (one barrier per tile, the
-// next tile's global loads in flight during the current tile's math).  V
-// reaches the MFMA through ds_read_b64_tr_b16.  Query blocks are scheduled
-// longest (highest causal row) first; tiles past a wave's last row are skipped.
+// K/V tiles of 32 keys are double-buffered in LDS (one barrier per tile; K
+// is two tiles and V one tile ahead of the math, their global loads in
+// flight during the current tile's math).  The next tile's score MFMAs are
+// interleaved with the current tile's softmax VALU work (one wave per SIMD
+// has nothing else to overlap them with).  V reaches the MFMA through
+// ds_read_b64_tr_b16.  Query blocks are scheduled longest (highest causal
+// row) first; tiles past a wave's last row are skipped.
 #include "kernels.hpp"
 
 #include <math.h>
@@ -173,7 +176,11 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
     // Softmax numerators of tile t: E = 2^(c2 s - m) and E*T in bf16, as the
     // B operands of the value MFMAs; k-slot r holds key 4g + r (r < 4) or
     // 16 + 4g + r - 4 of the tile.  MASK: the tile crosses the diagonal or S.
-    auto numerators = [&](int t, const f32x4_t (&d1)[2][4], bf16x8_t (&pop)[4], auto mask_tag) {
+    // Branch-free: a row's reference max moves (by select) only when the
+    // tile's max exceeds it by more than kSlack; alpha[qc] < 1 then tells the
+    // caller to rescale that row's sums before this tile's value MFMAs.
+    auto numerators = [&](int t, const f32x4_t (&d1)[2][4], bf16x8_t (&pop)[4],
+                          float (&alpha)[2], auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
         for (int qc = 0; qc < 2; ++qc) {
@@ -187,23 +194,17 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
                     const int key = t * kPfKeys + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4);
                     sv[r] = key <= qi && key < S ? sv[r] : -INFINITY;
                 }
-                tmax = fmaxf(tmax, sv[r]);
+                tmax = __builtin_fmaxf(tmax, sv[r]);
             }
             const float tm2 = group_max(tmax) * c2;
-            if (tm2 > mref[qc] + kSlack) {  // rare: move this row's reference max
-                const float al = __builtin_amdgcn_exp2f(mref[qc] - tm2);
-#pragma unroll
-                for (int db = 0; db <= DB; ++db) {
-                    acc[db][qc] *= al;
-                    acc[db][qc + 2] *= al;
-                }
-                mref[qc] = tm2;
-            }
+            const float mnew = tm2 > mref[qc] + kSlack ? tm2 : mref[qc];
+            alpha[qc] = __builtin_amdgcn_exp2f(mref[qc] - mnew);  // 1 unless moved; 0 at start
+            mref[qc] = mnew;
             uint32_t ew[4], etw[4];
 #pragma unroll
             for (int r = 0; r < 8; r += 2) {
-                const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[r], c2, -mref[qc]));
-                const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, -mref[qc]));
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[r], c2, -mnew));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, -mnew));
                 const float t0 = r < 4 ? d1[0][qc + 2][r] : d1[1][qc + 2][r - 4];
                 const float t1 = r < 4 ? d1[0][qc + 2][r + 1] : d1[1][qc + 2][r - 3];
                 ew[r / 2] = pack_bf16x2(e0, e1);
@@ -211,6 +212,19 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
             }
             pop[qc] = __builtin_bit_cast(bf16x8_t, uint4{ew[0], ew[1], ew[2], ew[3]});
             pop[qc + 2] = __builtin_bit_cast(bf16x8_t, uint4{etw[0], etw[1], etw[2], etw[3]});
+        }
+    };
+
+    // Rows whose reference max moved: scale their sums (rare after tile 0).
+    auto rescale = [&](const float (&alpha)[2]) {
+        if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f)) {
+#pragma unroll
+            for (int db = 0; db <= DB; ++db)
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc) {
+                    acc[db][qc] *= alpha[qc];
+                    acc[db][qc + 2] *= alpha[qc];
+                }
         }
     };
 
@@ -251,25 +265,30 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
     if (ntiles > 1) issue_v(1);
     __syncthreads();
 
-    f32x4_t d1[2][4];
-    if (wave_tiles > 0) scores(0, d1);
-    for (int t = 0; t < ntiles; ++t) {
+    // One tile of math.  The next tile's score MFMAs (independent of this
+    // tile's softmax) are interleaved with the softmax VALU work; the tile's
+    // value MFMAs follow.  The scores of the tile after the wave's last one
+    // read a stale (in-bounds) LDS tile and are never used.
+    auto tile = [&](int t, const f32x4_t (&d1)[2][4], f32x4_t (&d1n)[2][4], auto mask_tag) {
+        bf16x8_t pop[4];
+        float alpha[2];
+        scores(t + 1, d1n);
+        numerators(t, d1, pop, alpha, mask_tag);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one score MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then softmax VALU
+        }
+        rescale(alpha);
+        value_sums(t, pop);
+    };
+    auto step = [&](int t, const f32x4_t (&d1)[2][4], f32x4_t (&d1n)[2][4]) {
         if (t < wave_tiles) {
-            f32x4_t d1n[2][4];
-            if (t + 1 < wave_tiles) scores(t + 1, d1n);  // overlaps the softmax below
-            bf16x8_t pop[4];
             const bool full = t * kPfKeys + kPfKeys - 1 <= r0 && t * kPfKeys + kPfKeys <= S;
             if (full)
-                numerators(t, d1, pop, std::false_type{});
+                tile(t, d1, d1n, std::false_type{});
             else
-                numerators(t, d1, pop, std::true_type{});
-            value_sums(t, pop);
-            if (t + 1 < wave_tiles) {
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = d1n[rb][cb];
-            }
+                tile(t, d1, d1n, std::true_type{});
         }
         // K tile t+2 replaces tile t (last read by scores(t) one iteration ago);
         // V tile t+1 replaces tile t-1 (last read by value_sums(t-1))
@@ -278,6 +297,13 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillParams p)
         if (t + 3 < ntiles) issue_k(t + 3);
         if (t + 2 < ntiles) issue_v(t + 2);
         __syncthreads();
+    };
+
+    f32x4_t d1a[2][4], d1b[2][4];
+    scores(0, d1a);
+    for (int t = 0; t < ntiles; t += 2) {  // two tiles per trip: score buffers swap roles
+        step(t, d1a, d1b);
+        if (t + 1 < ntiles) step(t + 1, d1b, d1a);
     }
 
     // ---- o = a - (b - a r) per query row; lane (c, g) holds d = 16db + 4g + j
