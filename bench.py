@@ -30,13 +30,13 @@ METRIC = "Parallax decode KV GB/s (% of HBM peak) + tokens/s over batch×ctx swe
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {
-    "decode": ["parallax_local_linear_decode_amd/csrc/decode.hip",
-               "parallax_local_linear_decode_amd/csrc/kernels.hpp"],
-    "paged": ["parallax_local_linear_decode_amd/csrc/decode.hip",
-              "parallax_local_linear_decode_amd/csrc/kernels.hpp"],
-    "prefill": ["parallax_local_linear_decode_amd/csrc/prefill.hip",
-                "parallax_local_linear_decode_amd/csrc/kernels.hpp"],
+_COMMON = ["parallax_local_linear_decode_amd/csrc/kernels.hpp",
+           "parallax_local_linear_decode_amd/csrc/api.hip",
+           "parallax_local_linear_decode_amd/build.py"]
+KERNEL_SOURCES = {  # what the kernels of a workload are built from
+    "decode": ["parallax_local_linear_decode_amd/csrc/decode.hip"] + _COMMON,
+    "paged": ["parallax_local_linear_decode_amd/csrc/decode.hip"] + _COMMON,
+    "prefill": ["parallax_local_linear_decode_amd/csrc/prefill.hip"] + _COMMON,
 }
 
 
@@ -53,8 +53,9 @@ def kernel_sha(workload):
 
 
 def traffic_for(workload):
-    """HBM bytes per launch from committed counter runs, if they were taken on
-    the current kernel source; else None."""
+    """HBM bytes per step (FETCH_SIZE + WRITE_SIZE of every kernel the step
+    launches, calibrated against a plain copy) from committed counter runs,
+    if they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)[workload]
@@ -113,9 +114,9 @@ def make_decode_launcher(torch, plx, sets, out, split):
     return launch
 
 
-def cpu_baseline_decode(inp, nbytes, budget_s=12.0):
+def cpu_baseline_decode(inp, nbytes, budget_s=10.0):
     """The oracle (fp64 C, all host cores) on the same workload; repeated until
-    about budget_s of CPU time has passed."""
+    about budget_s of wall time has passed."""
     import oracle
     from parallax_local_linear_decode_amd.workloads import host_array
     import numpy as np
@@ -125,7 +126,7 @@ def cpu_baseline_decode(inp, nbytes, budget_s=12.0):
     bt = None if inp.block_table is None else host_array(inp.block_table)
     threads = oracle.default_threads()
     reps, elapsed, ref = 0, 0.0, None
-    while elapsed < budget_s and reps < 50:
+    while elapsed < budget_s and reps < 100000:
         t = time.perf_counter()
         ref = oracle.decode(args["q"], args["rho"], args["k"], args["v"], inp.scale,
                             seq_lens=sl, block_table=bt, threads=threads)
@@ -296,12 +297,20 @@ def run_prefill(args, torch, plx):
         # sampled query rows of every (batch, head); their causal pairs scale
         # the oracle's time to the whole workload
         rng = np.random.default_rng(0)
-        rows = np.sort(rng.choice(S, 24, replace=False)).astype(np.int32)
+        order = rng.permutation(S).astype(np.int32)
         hq, hr, hk, hv = (host_array(t) for t in (q, rho, k, v))
         threads = oracle.default_threads()
-        t0 = time.perf_counter()
-        ref = oracle.prefill(hq, hr, hk, hv, scale, rows=rows, threads=threads)
-        secs = time.perf_counter() - t0
+        secs, n, refs, done = 0.0, 24, [], 0
+        while secs < 10.0 and done < S:  # grow the row sample to ~10 s of oracle time
+            batch = np.sort(order[done:done + n])
+            t0 = time.perf_counter()
+            refs.append((batch, oracle.prefill(hq, hr, hk, hv, scale, rows=batch,
+                                               threads=threads)))
+            secs += time.perf_counter() - t0
+            done += n
+            n *= 2
+        rows = np.concatenate([r for r, _ in refs])
+        ref = np.concatenate([o for _, o in refs], axis=1)
         gate(out[:, rows.tolist()].double().cpu().numpy(), ref, 2e-2, 1e-2)
         frac = float(np.sum(rows + 1)) / (S * (S + 1) / 2)
         full = secs / frac
