@@ -157,6 +157,17 @@ def test_deterministic(gpu):
         assert torch.equal(run(inp), first)
 
 
+@pytest.mark.slow
+def test_full_size_deterministic(gpu):
+    """Batch 8, 16/8 heads, 4096 and 32768 tokens: repeated launches (split
+    kernel plus merge) return identical bits under a full-chip load."""
+    for L in (4096, 32768):
+        inp = decode_inputs(8, 16, 8, 128, L, seed=9, device=gpu)
+        first = run(inp).clone()
+        for i in range(50):
+            assert torch.equal(run(inp), first), f"L={L} launch {i} differs"
+
+
 def test_workspace_reuse_across_shapes(gpu):
     """One workspace, filled with garbage first, serves calls of different
     shapes back to back (arrival words from other calls count as zero)."""
