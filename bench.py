@@ -30,6 +30,9 @@ METRIC = "Parallax decode KV GB/s (% of HBM peak) + tokens/s over batch×ctx swe
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Decode over a bf16 cache runs on bf16 matrix cores (q, rho and the softmax
+# weights enter as two-term bf16 splits; sums accumulate in fp32).
+DECODE_DTYPE = "bf16"
 _COMMON = ["parallax_local_linear_decode_amd/csrc/kernels.hpp",
            "parallax_local_linear_decode_amd/csrc/api.hip",
            "parallax_local_linear_decode_amd/build.py"]
@@ -165,7 +168,7 @@ def run_decode(args, torch, plx):
     traffic = traffic_for("decode")
     return {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s",
-        "ms_per_step": per * 1e3, "dtype": "f32",
+        "ms_per_step": per * 1e3, "dtype": DECODE_DTYPE,
         "config": {"workload": f"decode: batch {B}, 16 query / 8 KV heads, d 128, ctx {L}, "
                                "contiguous bf16 KV cache, fp32 q/rho/out",
                    "batch": B, "ctx": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
@@ -199,7 +202,7 @@ def run_paged(args, torch, plx):
     gbps = nbytes / per / 1e9
     return {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": per * 1e3,
-        "dtype": "f32",
+        "dtype": DECODE_DTYPE,
         "config": {"workload": "paged decode: batch 256, 16 query / 8 KV heads, d 128, "
                                "ctx U[128, 32768], 16-token pages, shuffled block table, bf16",
                    "batch": 256, "total_tokens": int(sum(lens)), "kv_gb": nbytes / 1e9},
@@ -240,7 +243,7 @@ def run_sweep(args, torch, plx):
             torch.cuda.empty_cache()
     best = max((p["gbps"] for p in points if "gbps" in p), default=0.0)
     return {"metric": METRIC, "value": best, "unit": "GB/s", "ms_per_step": None,
-            "dtype": "f32", "config": {"workload": "decode sweep: batch x ctx grid, 16/8 heads, "
+            "dtype": DECODE_DTYPE, "config": {"workload": "decode sweep: batch x ctx grid, 16/8 heads, "
                                                    "d 128, bf16 KV", "points": points},
             "roofline": None, "cpu_baseline": None}
 

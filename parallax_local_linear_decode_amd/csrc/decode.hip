@@ -12,11 +12,13 @@
 //
 // which equals o_SA - S_KV rho for the softmax-weighted covariance S_KV.
 //
-// Common structure: grid = (batch x KV head) units x context splits.  A
-// workgroup reads each key/value row of its split once and serves all G
-// query heads of its KV head.  Logits are kept in base 2 (scale * log2 e
-// folded into q).  The running reference max only moves when a logit exceeds
-// it by more than 8, so rescaling is rare and every weight stays below 2^8.
+// Common structure: grid = context splits x (batch x KV head) units, split
+// major, so consecutive workgroups (dealt round-robin to the XCDs) belong to
+// different units and every XCD gets a like share of work.  A workgroup
+// reads each key/value row of its split once and serves all G query heads of
+// its KV head.  Logits are kept in base 2 (scale * log2 e folded into q).
+// The running reference max only moves when a logit exceeds it by more than
+// 8, so rescaling is rare and every weight stays below 2^8.
 // Each split leaves a partial record (m, Z, R, A, B) per query head; with
 // more than one split a small merge kernel combines them.  Every launch is
 // self-contained: no cross-workgroup fences, atomics or counters.
@@ -169,8 +171,9 @@ __global__ __launch_bounds__((64 * mfma_waves<D, G>())) void decode_mfma_kernel(
     const int c = lane & 15;  // MFMA column (scores/sums) or row (V^T) index
     const int g = lane >> 4;  // lane group: which 8 k-slots of an MFMA operand
 
-    const int split_idx = blockIdx.x % p.nsplit;
-    const int unit = blockIdx.x / p.nsplit;
+    const int units = gridDim.x / p.nsplit;
+    const int split_idx = blockIdx.x / units;  // split-major order
+    const int unit = blockIdx.x % units;
     const int b = unit / p.num_kv_heads;
     const int hk = unit % p.num_kv_heads;
     int L, nsp;
@@ -465,8 +468,9 @@ __global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePara
     const int row = lane / LPT;
     const int sub = lane % LPT;
 
-    const int split_idx = blockIdx.x % p.nsplit;
-    const int unit = blockIdx.x / p.nsplit;
+    const int units = gridDim.x / p.nsplit;
+    const int split_idx = blockIdx.x / units;  // split-major order
+    const int unit = blockIdx.x % units;
     const int b = unit / p.num_kv_heads;
     const int hk = unit % p.num_kv_heads;
     int L, nsp;
@@ -643,6 +647,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 
 template <int D, int G, bool PAGED>
 hipError_t launch_all(const DecodeParams &p, bool bf16, int batch, hipStream_t stream) {
+    // Workgroup w takes split w / units of unit w % units.  Consecutive
+    // workgroups are dealt round-robin to the eight XCDs, so in this order
+    // every XCD gets every eighth unit with all of its splits; in unit-major
+    // order each XCD would get fixed split indices, and with ragged rows the
+    // high ones are mostly empty, leaving XCDs idle.
     const unsigned units = (unsigned)((int64_t)batch * p.num_kv_heads);
     const dim3 grid((unsigned)((int64_t)units * p.nsplit));
     if (bf16)
