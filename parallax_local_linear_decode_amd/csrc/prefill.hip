@@ -201,29 +201,41 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
         // crosses the diagonal or S.
         auto numerators = [&](int t, const f32x4_t (&d1)[2][4], auto mask_tag) {
             constexpr bool MASK = decltype(mask_tag)::value;
+            // The two 16-row halves (qc) run side by side, phase by phase, so
+            // their dependency chains (max, cross-group max, exp) overlap.
+            float sv[2][8], gm[2];
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc) {
                 const int qi = r0 + 16 * qc + c;
-                float sv[8];
                 float tmax = -INFINITY;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    sv[r] = r < 4 ? d1[0][qc][r] : d1[1][qc][r - 4];
+                    sv[qc][r] = r < 4 ? d1[0][qc][r] : d1[1][qc][r - 4];
                     if constexpr (MASK) {
                         const int key = t * kPfKeys + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4);
-                        sv[r] = key <= qi && key < S ? sv[r] : -INFINITY;
+                        sv[qc][r] = key <= qi && key < S ? sv[qc][r] : -INFINITY;
                     }
-                    tmax = __builtin_fmaxf(tmax, sv[r]);
+                    tmax = __builtin_fmaxf(tmax, sv[qc][r]);
                 }
-                const float tm2 = group_max(tmax) * c2;
-                const float mnew = tm2 > mref[qc] + kSlack ? tm2 : mref[qc];
-                const float alpha = __builtin_amdgcn_exp2f(mref[qc] - mnew);  // 1 unless moved
-                mref[qc] = mnew;
+                gm[qc] = tmax;
+            }
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc) gm[qc] = group_max(gm[qc]);
+            float mnew[2], alpha[2];
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc) {
+                const float tm2 = gm[qc] * c2;
+                mnew[qc] = tm2 > mref[qc] + kSlack ? tm2 : mref[qc];
+                alpha[qc] = __builtin_amdgcn_exp2f(mref[qc] - mnew[qc]);  // 1 unless moved
+                mref[qc] = mnew[qc];
+            }
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc) {
                 uint32_t ew[4], etw[4];
 #pragma unroll
                 for (int r = 0; r < 8; r += 2) {
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[r], c2, -mnew));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[r + 1], c2, -mnew));
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[qc][r], c2, -mnew[qc]));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[qc][r + 1], c2, -mnew[qc]));
                     const float t0 = r < 4 ? d1[0][qc + 2][r] : d1[1][qc + 2][r - 4];
                     const float t1 = r < 4 ? d1[0][qc + 2][r + 1] : d1[1][qc + 2][r - 3];
                     ew[r / 2] = pack_bf16x2(e0, e1);
@@ -231,7 +243,9 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
                 }
                 pbuf[t & 1][pair][qc][lane] = uint4{ew[0], ew[1], ew[2], ew[3]};
                 pbuf[t & 1][pair][qc + 2][lane] = uint4{etw[0], etw[1], etw[2], etw[3]};
-                if (g == 0) abuf[t & 1][pair][qc][c] = alpha;
+                // every lane group holds the row's factor; all four write the
+                // same value (no lane condition, so no branch splits the code)
+                abuf[t & 1][pair][qc][c] = alpha[qc];
             }
         };
         auto score_step = [&](int t) {
