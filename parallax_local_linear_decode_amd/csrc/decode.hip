@@ -144,14 +144,22 @@ __device__ void finish_block(const DecodeParams &p, float (*red)[G][partial_floa
 
 constexpr int kMfmaStep = 32;  // tokens per wave step (two 16-token MFMA row blocks)
 
-// Waves per workgroup: 8 (two per SIMD), or 4 when eight query heads per KV
-// head at d = 128 need more than the 256 registers two waves can each hold.
+// Waves per workgroup: 8 (two per SIMD) or 4 (one per SIMD; at most 168
+// registers, so three such workgroups share a CU).  4 when eight query heads
+// per KV head at d = 128 need more than the 256 registers two waves can each
+// hold; else 4 when a workgroup's split has at most four 32-token steps (no
+// wave idles) or when the grid has more workgroups than the 256 CUs (three
+// workgroups per CU keep more loads in flight than one); 8 otherwise, where
+// one workgroup per CU is all there is.
 template <int D, int G>
-constexpr int mfma_waves() { return (D == 128 && G == 8) ? 4 : 8; }
+constexpr int mfma_waves_max() { return (D == 128 && G == 8) ? 4 : 8; }
+constexpr int kShortSteps = 4;    // steps per workgroup up to which 4 waves are used
+constexpr int kDeviceCUs = 256;   // compute units of an MI355X
 
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__((64 * mfma_waves<D, G>())) void decode_mfma_kernel(DecodeParams p) {
-    constexpr int kMfmaWaves = mfma_waves<D, G>();
+template <int D, int G, bool PAGED, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 && !(D == 128 && G == 8) ? 3 : 2) void
+decode_mfma_kernel(DecodeParams p) {
+    constexpr int kMfmaWaves = NW;
     constexpr int HS = G < 4 ? G : 4;     // query heads per 16-column set
     constexpr int NCS = G / HS;           // column sets (2 when G = 8)
     constexpr int KS = D / 32;            // score MFMAs per row block (K = 32 each)
@@ -654,10 +662,16 @@ hipError_t launch_all(const DecodeParams &p, bool bf16, int batch, hipStream_t s
     // high ones are mostly empty, leaving XCDs idle.
     const unsigned units = (unsigned)((int64_t)batch * p.num_kv_heads);
     const dim3 grid((unsigned)((int64_t)units * p.nsplit));
-    if (bf16)
-        hipLaunchKernelGGL((decode_mfma_kernel<D, G, PAGED>), grid, dim3(64 * mfma_waves<D, G>()), 0,
-                           stream, p);
-    else
+    if (bf16) {
+        constexpr int NWMAX = mfma_waves_max<D, G>();
+        const int steps = (min(p.split, p.max_seq_len) + kMfmaStep - 1) / kMfmaStep;
+        if (NWMAX == 8 && steps > kShortSteps && grid.x <= (unsigned)kDeviceCUs)
+            hipLaunchKernelGGL((decode_mfma_kernel<D, G, PAGED, NWMAX>), grid, dim3(64 * NWMAX), 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<D, G, PAGED, 4>), grid, dim3(64 * 4), 0, stream,
+                               p);
+    } else
         hipLaunchKernelGGL((decode_valu_kernel<D, G, PAGED>), grid, dim3(64 * kValuWaves), 0,
                            stream, p);
     hipError_t e = hipGetLastError();

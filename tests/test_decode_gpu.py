@@ -138,6 +138,25 @@ def test_ragged_lengths(gpu, kv_dtype, d, G):
         assert torch.all(out[lens.index(0)] == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_short_rows(gpu, d, G):
+    """A cache of at most 128 tokens gives workgroups of at most four 32-token
+    steps, which run with four waves; ragged lengths, NaN past each."""
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 96, 127, 128, 0, 100]
+    B, Hkv, Lcap = len(lens), 2, 128
+    inp = decode_inputs(B, Hkv * G, Hkv, d, Lcap, seed=G * 10 + d)
+    inp.seq_lens = torch.tensor(lens, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        inp.k[b, :, L:] = float("nan")
+        inp.v[b, :, L:] = float("nan")
+    ref = oracle_decode(inp)
+    inp = to(inp, gpu)
+    out = run(inp)
+    assert_parity(out, ref, TAU_BF16, RMS_DECODE_BF16, what=f"short rows G={G} d={d}")
+    assert torch.all(out[lens.index(0)] == 0)
+
+
 def test_split_choices_agree(gpu):
     inp = to(decode_inputs(3, 16, 8, 128, 3000, seed=7), gpu)
     ref = oracle_decode(inp)
@@ -210,6 +229,15 @@ def test_paged_small(gpu):
     for split in (0, 256, 512):
         assert_parity(run(inp, split_tokens=split), ref, TAU_BF16, RMS_DECODE_BF16,
                       what=f"paged split={split}")
+
+
+def test_paged_short_rows(gpu):
+    """Paged rows of 1-128 tokens (the four-wave workgroups), NaN-poisoned
+    tails and unused block-table entries, rho = 0 for two rows."""
+    inp = paged_inputs(24, 16, 8, 128, ctx_lo=1, ctx_hi=128, seed=3, rho_zero_rows=2)
+    ref = oracle_decode(inp)
+    inp = to(inp, gpu)
+    assert_parity(run(inp), ref, TAU_BF16, RMS_DECODE_BF16, what="paged short rows")
 
 
 def test_paged_equals_contiguous(gpu):
