@@ -10,6 +10,11 @@ last-level cache from serving it, R copies of the inputs (R * KV >= 1 GiB)
 are rotated, step i using copy i % R.  Steps are timed with HIP events on the
 stream the kernels are launched on.
 
+Decode and paged lines also carry `read_stream`: a plain read-only streaming
+kernel (libparallax_probe.so, built beside the library) timed over the same
+bytes per step and the same cold-copy rotation, the practical HBM ceiling on
+this GPU, and `frac_of_read_stream` = value / that rate.
+
 Prints ONE JSON line.  Other workloads: --workload paged (256 sequences, ctx
 U[128, 32768], 16-token pages), prefill (batch 4, seq 8192, 16/8 heads),
 sweep (batch x ctx grid), copy (a plain device copy used to calibrate the
@@ -141,6 +146,35 @@ def cpu_baseline_decode(inp, nbytes, budget_s=10.0):
                  "sample": f"the full workload, {reps} repetition(s), fp64 streaming form"}
 
 
+def read_stream(torch, plx, nbytes, n_bufs, steps, warmup):
+    """The HBM reference: a plain read-only streaming kernel (its own library,
+    libparallax_probe.so) over the same bytes per step and the same number of
+    rotating cold copies as the workload; GB/s."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(plx.__file__)), "libparallax_probe.so")
+    if not os.path.exists(path):
+        log(f"read stream: {path} missing (run the build); not reported")
+        return None
+    lib = ctypes.CDLL(path)
+    lib.parallax_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    size = (nbytes + 15) // 16 * 16
+    bufs = [torch.randint(0, 1 << 30, (size // 4,), dtype=torch.int32, device="cuda:0")
+            for _ in range(n_bufs)]
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(i):
+        if lib.parallax_probe_read(ctypes.c_void_p(bufs[i].data_ptr()), size,
+                                   ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+            raise SystemExit("read stream probe failed to launch")
+    per = time_launches(torch, launch, n_bufs, steps, warmup) / steps
+    del bufs
+    torch.cuda.empty_cache()
+    return {"gbps": round(size / per / 1e9, 2), "bytes": size, "cold_copies": n_bufs,
+            "kernel": "grid-stride 16-byte loads, 2048 x 256 threads (libparallax_probe)"}
+
+
 def run_decode(args, torch, plx):
     from parallax_local_linear_decode_amd.workloads import decode_inputs
     B, Hq, Hkv, d, L = args.batch, 16, 8, 128, args.ctx
@@ -166,6 +200,7 @@ def run_decode(args, torch, plx):
     warm = time_launches(torch, launch, 1, args.steps, args.warmup) / args.steps
     gbps = nbytes / per / 1e9
     traffic = traffic_for("decode")
+    stream_ref = read_stream(torch, plx, kv_bytes, n_bufs, args.steps, args.warmup)
     return {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s",
         "ms_per_step": per * 1e3, "dtype": DECODE_DTYPE,
@@ -177,6 +212,8 @@ def run_decode(args, torch, plx):
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s": B / per, "kv_tokens_per_s": B * L / per,
         "warm_cache_gbps": round(nbytes / warm / 1e9, 2),
+        "read_stream": stream_ref,
+        "frac_of_read_stream": None if not stream_ref else round(gbps / stream_ref["gbps"], 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
@@ -200,6 +237,9 @@ def run_paged(args, torch, plx):
     secs = time_launches(torch, launch, 1, args.steps, args.warmup)
     per = secs / args.steps
     gbps = nbytes / per / 1e9
+    del inp, launch
+    torch.cuda.empty_cache()
+    stream_ref = read_stream(torch, plx, nbytes, 1, min(args.steps, 50), 3)
     return {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": per * 1e3,
         "dtype": DECODE_DTYPE,
@@ -208,6 +248,8 @@ def run_paged(args, torch, plx):
                    "batch": 256, "total_tokens": int(sum(lens)), "kv_gb": nbytes / 1e9},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s": 256 / per, "kv_tokens_per_s": sum(lens) / per,
+        "read_stream": stream_ref,
+        "frac_of_read_stream": None if not stream_ref else round(gbps / stream_ref["gbps"], 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic_for("paged")},
@@ -385,7 +427,7 @@ def main():
             "dtype": rec["dtype"], "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1^2) rho)",
             "config": rec["config"]}
     for k in ("pct_hbm_peak", "tokens_per_s", "kv_tokens_per_s", "warm_cache_gbps",
-              "mfma_util"):
+              "read_stream", "frac_of_read_stream", "mfma_util"):
         if k in rec:
             line[k] = rec[k]
     line["roofline"] = rec["roofline"]

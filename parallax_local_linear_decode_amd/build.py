@@ -16,6 +16,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libparallax.so")
 SOURCES = ["api.hip", "decode.hip", "prefill.hip"]
+# A plain read-stream kernel the benchmark times as the HBM reference; its
+# own library, not part of libparallax.
+PROBE_LIB = os.path.join(PKG, "libparallax_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the generated code.  MFMA
@@ -52,14 +56,19 @@ def build(verbose: bool = False) -> str:
             print(r.stderr, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+
+    def link(target, target_objs):
+        tmp = target + ".tmp"
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *target_objs, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link of {os.path.basename(target)} failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, target)
+
+    link(LIB, objs[:len(SOURCES)])
+    link(PROBE_LIB, objs[len(SOURCES):])
     return LIB
 
 
