@@ -56,11 +56,11 @@ def _load():
     lib.orc_decode.argtypes = [i32, i32, i32, i32, i32, i32, dbl,
                                vp, i32, vp, i32, vp, vp, i32,
                                i64, i64, i64, i64, i64, i64,
-                               vp, i32, vp, i32, i32, vp, i32]
+                               vp, i32, vp, i32, i32, i32, vp, i32]
     lib.orc_prefill.restype = i32
     lib.orc_prefill.argtypes = [i32, i32, i32, i32, i32, i32, i32, dbl,
                                 vp, i32, vp, i32, vp, vp, i32,
-                                vp, i32, vp, i32]
+                                vp, i32, i32, vp, i32]
     _lib = lib
     return lib
 
@@ -84,7 +84,7 @@ def default_threads() -> int:
 
 
 def decode(q, rho, k, v, scale, *, seq_lens=None, block_table=None, form="streaming",
-           threads=None):
+           window=0, threads=None):
     """Decode attention rows, one per (batch, query head).
 
     q, rho : [B, Hq, dk]
@@ -94,6 +94,7 @@ def decode(q, rho, k, v, scale, *, seq_lens=None, block_table=None, form="stream
     paged cache:
         k [NB, Hkv, P, dk], v [NB, Hkv, P, dv] (P tokens per page),
         block_table [B, max_blocks] int32 of page ids, seq_lens [B] int32
+    window : 0 (every cached token) or W >= 1 (each row's last W tokens)
     Returns out [B, Hq, dv] float64.
     """
     lib = _load()
@@ -143,14 +144,15 @@ def decode(q, rho, k, v, scale, *, seq_lens=None, block_table=None, form="stream
                         *k_str, *v_str,
                         _ptr(seq_lens), L_all,
                         _ptr(block_table), P if block_table is not None else 0, max_blocks,
-                        _ptr(out), int(threads or default_threads()))
+                        int(window), _ptr(out), int(threads or default_threads()))
     if rc != 0:
         raise ValueError("oracle: orc_decode rejected its arguments")
     return out
 
 
-def prefill(q, rho, k, v, scale, *, rows=None, form="streaming", threads=None):
-    """Causal prefill rows: row i of (b, h) attends to keys 0..i.
+def prefill(q, rho, k, v, scale, *, rows=None, form="streaming", window=0, threads=None):
+    """Causal prefill rows: row i of (b, h) attends to keys 0..i (with window
+    W >= 1: keys max(0, i-W+1)..i).
 
     q, rho : [B, S, Hq, dk];  k : [B, S, Hkv, dk];  v : [B, S, Hkv, dv]
     rows   : query positions to evaluate (default: all S)
@@ -175,7 +177,7 @@ def prefill(q, rho, k, v, scale, *, rows=None, form="streaming", threads=None):
     rc = lib.orc_prefill(_FORMS[form], B, S, Hq, Hkv, dk, dv, float(scale),
                          _ptr(q), _dtype_code(q), _ptr(rho), _dtype_code(rho),
                          _ptr(k), _ptr(v), _dtype_code(k),
-                         _ptr(rows), int(rows.size), _ptr(out),
+                         _ptr(rows), int(rows.size), int(window), _ptr(out),
                          int(threads or default_threads()))
     if rc != 0:
         raise ValueError("oracle: orc_prefill rejected its arguments")

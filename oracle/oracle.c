@@ -25,6 +25,11 @@
  * only; query head h reads KV head h / (Hq/Hkv); an empty row (L = 0) gives
  * o = 0; prefill row i sees keys 0..i.
  *
+ * Local window (the "local window" the same page leaves open, section 3.1):
+ * with window W >= 1 a row keeps only its W most recent keys -- a decode row
+ * over L cached tokens uses keys max(0, L-W) .. L-1, prefill row i uses keys
+ * max(0, i-W+1) .. i; W = 0 means every key (full attention).
+ *
  * Two independent forms are provided:
  *   ORC_FORM_EXPLICIT  -- the definition above written out: logits, max,
  *                         normalised weights, weighted means, the explicit
@@ -90,44 +95,47 @@ typedef struct {
     double *s, *kbar, *kc, *vbar, *cov, *A, *Bm, *qd, *rd;
 } orc_scratch;
 
-/* The definition written out (explicit covariance matrix). */
+/* The definition written out (explicit covariance matrix), over the keys
+ * j0 .. j1-1; logits of key j are kept in s[j - j0]. */
 static void row_explicit(const double *q, const double *rho, int dk, int dv, double scale,
-                         int L, const orc_kv *kv, int b, int hk, double *o, orc_scratch *w) {
-    if (L <= 0) {
+                         int j0, int j1, const orc_kv *kv, int b, int hk, double *o,
+                         orc_scratch *w) {
+    if (j1 <= j0) {
         for (int c = 0; c < dv; ++c) o[c] = 0.0;
         return;
     }
+    double *p = w->s - j0;
     /* logits and their maximum */
     double smax = -INFINITY;
-    for (int j = 0; j < L; ++j) {
+    for (int j = j0; j < j1; ++j) {
         int64_t ko = kv_off(kv, 0, b, hk, j);
         double dot = 0.0;
         for (int e = 0; e < dk; ++e) dot += q[e] * orc_get(kv->k, kv->dtype, ko + e);
-        w->s[j] = scale * dot;
-        if (w->s[j] > smax) smax = w->s[j];
+        p[j] = scale * dot;
+        if (p[j] > smax) smax = p[j];
     }
-    /* softmax weights p_j (stored over s) */
+    /* softmax weights p_j (stored over the logits) */
     double den = 0.0;
-    for (int j = 0; j < L; ++j) {
-        w->s[j] = exp(w->s[j] - smax);
-        den += w->s[j];
+    for (int j = j0; j < j1; ++j) {
+        p[j] = exp(p[j] - smax);
+        den += p[j];
     }
-    for (int j = 0; j < L; ++j) w->s[j] /= den;
+    for (int j = j0; j < j1; ++j) p[j] /= den;
     /* weighted means kbar, vbar (vbar is the softmax output o_SA) */
     for (int e = 0; e < dk; ++e) w->kbar[e] = 0.0;
     for (int c = 0; c < dv; ++c) w->vbar[c] = 0.0;
-    for (int j = 0; j < L; ++j) {
+    for (int j = j0; j < j1; ++j) {
         int64_t ko = kv_off(kv, 0, b, hk, j), vo = kv_off(kv, 1, b, hk, j);
-        for (int e = 0; e < dk; ++e) w->kbar[e] += w->s[j] * orc_get(kv->k, kv->dtype, ko + e);
-        for (int c = 0; c < dv; ++c) w->vbar[c] += w->s[j] * orc_get(kv->v, kv->dtype, vo + c);
+        for (int e = 0; e < dk; ++e) w->kbar[e] += p[j] * orc_get(kv->k, kv->dtype, ko + e);
+        for (int c = 0; c < dv; ++c) w->vbar[c] += p[j] * orc_get(kv->v, kv->dtype, vo + c);
     }
     /* S_KV[c][e] = sum_j p_j (v_jc - vbar_c)(k_je - kbar_e) */
     memset(w->cov, 0, sizeof(double) * (size_t)dv * (size_t)dk);
-    for (int j = 0; j < L; ++j) {
+    for (int j = j0; j < j1; ++j) {
         int64_t ko = kv_off(kv, 0, b, hk, j), vo = kv_off(kv, 1, b, hk, j);
         for (int e = 0; e < dk; ++e) w->kc[e] = orc_get(kv->k, kv->dtype, ko + e) - w->kbar[e];
         for (int c = 0; c < dv; ++c) {
-            double dvc = w->s[j] * (orc_get(kv->v, kv->dtype, vo + c) - w->vbar[c]);
+            double dvc = p[j] * (orc_get(kv->v, kv->dtype, vo + c) - w->vbar[c]);
             double *row = w->cov + (size_t)c * (size_t)dk;
             for (int e = 0; e < dk; ++e) row[e] += dvc * w->kc[e];
         }
@@ -141,16 +149,17 @@ static void row_explicit(const double *q, const double *rho, int dk, int dv, dou
     }
 }
 
-/* The one-pass moment form (running max, Z, R, A, B). */
+/* The one-pass moment form (running max, Z, R, A, B) over keys j0 .. j1-1. */
 static void row_streaming(const double *q, const double *rho, int dk, int dv, double scale,
-                          int L, const orc_kv *kv, int b, int hk, double *o, orc_scratch *w) {
-    if (L <= 0) {
+                          int j0, int j1, const orc_kv *kv, int b, int hk, double *o,
+                          orc_scratch *w) {
+    if (j1 <= j0) {
         for (int c = 0; c < dv; ++c) o[c] = 0.0;
         return;
     }
     double m = -INFINITY, Z = 0.0, R = 0.0;
     for (int c = 0; c < dv; ++c) w->A[c] = w->Bm[c] = 0.0;
-    for (int j = 0; j < L; ++j) {
+    for (int j = j0; j < j1; ++j) {
         int64_t ko = kv_off(kv, 0, b, hk, j), vo = kv_off(kv, 1, b, hk, j);
         double qk = 0.0, t = 0.0;
         for (int e = 0; e < dk; ++e) {
@@ -194,6 +203,7 @@ typedef struct {
     int L_all;
     /* prefill: rows are (b, row_sel[r], h) over S tokens; n_rows == 0 => decode */
     int S, n_rows;
+    int window; /* 0: every key; W >= 1: the W most recent keys of each row */
     const int32_t *row_sel;
     int64_t n_units;
     int maxL;
@@ -242,15 +252,19 @@ static void *orc_worker(void *argp) {
             qoff = (((int64_t)b * J->S + i) * J->Hq + h) * J->dk;
             ooff = u * J->dv;
         }
+        /* keys j0 .. L-1: all of them, or the window's most recent ones */
+        int j0 = (J->window > 0 && L > J->window) ? L - J->window : 0;
         for (int e = 0; e < J->dk; ++e) {
             w.qd[e] = orc_get(J->q, J->q_dtype, qoff + e);
             w.rd[e] = orc_get(J->rho, J->rho_dtype, qoff + e);
         }
         int hk = h / G;
         if (J->form == ORC_FORM_EXPLICIT)
-            row_explicit(w.qd, w.rd, J->dk, J->dv, J->scale, L, &J->kv, b, hk, J->out + ooff, &w);
+            row_explicit(w.qd, w.rd, J->dk, J->dv, J->scale, j0, L, &J->kv, b, hk, J->out + ooff,
+                         &w);
         else
-            row_streaming(w.qd, w.rd, J->dk, J->dv, J->scale, L, &J->kv, b, hk, J->out + ooff, &w);
+            row_streaming(w.qd, w.rd, J->dk, J->dv, J->scale, j0, L, &J->kv, b, hk, J->out + ooff,
+                          &w);
     }
     free(w.s); free(w.kbar); free(w.kc); free(w.vbar); free(w.A); free(w.Bm); free(w.qd); free(w.rd);
     free(w.cov);
@@ -284,6 +298,7 @@ static int orc_run(orc_job *J, int nthreads) {
  *   k, v   : strided  -> element offset b*s0 + hk*sh + j*st (+ e)
  *            paged    -> page*s0 + hk*sh + slot*st (+ e), page from block_table
  *   seq_lens : [B] or NULL (then every row sees L_all tokens)
+ *   window : 0 (every cached token) or W >= 1 (the last W of each row)
  *   out    : [B, Hq, dv] fp64
  * Returns 0 on success, -1 on bad arguments or thread failure.
  */
@@ -294,8 +309,8 @@ int orc_decode(int form, int B, int Hq, int Hkv, int dk, int dv, double scale,
                int64_t v_s0, int64_t v_sh, int64_t v_st,
                const int32_t *seq_lens, int L_all,
                const int32_t *block_table, int page_size, int max_blocks,
-               double *out, int nthreads) {
-    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || dk < 1 || dv < 1) return -1;
+               int window, double *out, int nthreads) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || dk < 1 || dv < 1 || window < 0) return -1;
     if (block_table != NULL && page_size < 1) return -1;
     orc_job J;
     memset(&J, 0, sizeof J);
@@ -306,6 +321,7 @@ int orc_decode(int form, int B, int Hq, int Hkv, int dk, int dv, double scale,
     J.kv.v_s0 = v_s0; J.kv.v_sh = v_sh; J.kv.v_st = v_st;
     J.kv.block_table = block_table; J.kv.page_size = page_size; J.kv.max_blocks = max_blocks;
     J.out = out; J.seq_lens = seq_lens; J.L_all = L_all;
+    J.window = window;
     J.n_rows = 0;
     J.n_units = (int64_t)B * Hq;
     J.maxL = L_all;
@@ -315,7 +331,8 @@ int orc_decode(int form, int B, int Hq, int Hkv, int dk, int dv, double scale,
 }
 
 /*
- * Causal prefill: row i of (b, h) attends to keys 0..i of KV head h/(Hq/Hkv).
+ * Causal prefill: row i of (b, h) attends to keys 0..i of KV head h/(Hq/Hkv)
+ * (with window W >= 1: keys max(0, i-W+1)..i).
  *   q, rho : [B, S, Hq, dk];  k: [B, S, Hkv, dk];  v: [B, S, Hkv, dv]
  *   rows   : n_rows query positions evaluated for every (b, h)
  *   out    : [B, n_rows, Hq, dv] fp64
@@ -323,8 +340,9 @@ int orc_decode(int form, int B, int Hq, int Hkv, int dk, int dv, double scale,
 int orc_prefill(int form, int B, int S, int Hq, int Hkv, int dk, int dv, double scale,
                 const void *q, int q_dtype, const void *rho, int rho_dtype,
                 const void *k, const void *v, int kv_dtype,
-                const int32_t *rows, int n_rows, double *out, int nthreads) {
-    if (B < 0 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || dk < 1 || dv < 1 || n_rows < 1)
+                const int32_t *rows, int n_rows, int window, double *out, int nthreads) {
+    if (B < 0 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || dk < 1 || dv < 1 || n_rows < 1 ||
+        window < 0)
         return -1;
     int maxL = 0;
     for (int r = 0; r < n_rows; ++r) {
@@ -342,6 +360,7 @@ int orc_prefill(int form, int B, int S, int Hq, int Hkv, int dk, int dv, double 
     J.kv.block_table = NULL;
     J.out = out;
     J.S = S; J.n_rows = n_rows; J.row_sel = rows;
+    J.window = window;
     J.n_units = (int64_t)B * n_rows * Hq;
     J.maxL = maxL;
     return orc_run(&J, nthreads);

@@ -416,3 +416,139 @@ def test_prefill_uniform_limit():
             K, V = k[0, :i + 1, h // G], v[0, :i + 1, h // G]
             C = np.cov(np.vstack([V.T, K.T]), bias=True)[:8, 8:]
             assert rel_err(o[0, ri, h], V.mean(0) - C @ rho[0, i, h]) < 1e-12
+
+
+# ---------------------------------------------------------------- window ---
+# Local window W (the "local window" the Parallax page leaves open, section
+# 3.1): a row keeps only its W most recent keys -- decode over L cached
+# tokens uses keys L-W .. L-1, prefill row i uses keys i-W+1 .. i.
+
+def _np_parallax(q, rho, K, V, scale):
+    """The definition in numpy/scipy: softmax weights, numpy's weighted
+    (biased) cross-covariance."""
+    dv = V.shape[1]
+    p = scipy.special.softmax(scale * (K @ q))
+    if K.shape[0] == 1:
+        return V[0].copy()
+    C = np.cov(np.vstack([V.T, K.T]), aweights=p, bias=True)[:dv, dv:]
+    return p @ V - C @ rho
+
+
+def _two_token(q, rho, K, V, scale):
+    """Closed form for two keys: S_KV = p1 p2 (v1 - v2)(k1 - k2)^T."""
+    s1, s2 = scale * K[0] @ q, scale * K[1] @ q
+    p1 = 1.0 / (1.0 + math.exp(s2 - s1))
+    p2 = 1.0 - p1
+    return p1 * V[0] + p2 * V[1] - p1 * p2 * (V[0] - V[1]) * ((K[0] - K[1]) @ rho)
+
+
+def _window_decode_case(seed, lens=(5, 37, 64, 1), Hq=4, Hkv=2, d=6):
+    rng = np.random.default_rng(seed)
+    B, Lcap = len(lens), max(lens)
+    q = rng.standard_normal((B, Hq, d))
+    rho = 0.4 * rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, Lcap, d))
+    v = rng.standard_normal((B, Hkv, Lcap, d))
+    return q, rho, k, v, np.array(lens, dtype=np.int32)
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("W", [1, 2, 3, 16, 37, 100])
+def test_window_decode_against_numpy(form, W):
+    q, rho, k, v, lens = _window_decode_case(30)
+    B, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    o = oracle.decode(q, rho, k, v, 0.45, seq_lens=lens, window=W, form=form)
+    for b in range(B):
+        L = int(lens[b])
+        j0 = max(0, L - W)
+        for h in range(Hq):
+            K, V = k[b, h // G, j0:L], v[b, h // G, j0:L]
+            if K.shape[0] == 1:
+                want = V[0]                   # one key: o = v
+            elif K.shape[0] == 2:
+                want = _two_token(q[b, h], rho[b, h], K, V, 0.45)
+            else:
+                want = _np_parallax(q[b, h], rho[b, h], K, V, 0.45)
+            assert rel_err(o[b, h], want) < 1e-12, (b, h, W)
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_window_at_least_the_row_is_full_attention(form):
+    q, rho, k, v, lens = _window_decode_case(31)
+    full = oracle.decode(q, rho, k, v, 0.45, seq_lens=lens, form=form)
+    for W in (64, 65, 1000):
+        assert np.array_equal(oracle.decode(q, rho, k, v, 0.45, seq_lens=lens, window=W,
+                                            form=form), full)
+
+
+def test_window_paged_equals_contiguous_gather():
+    """Windowed paged decode against numpy indexing of the same pages."""
+    rng = np.random.default_rng(32)
+    B, Hq, Hkv, d, P = 3, 4, 2, 6, 4
+    lens = np.array([9, 14, 3], dtype=np.int32)
+    nblk = (lens + P - 1) // P
+    NB = int(nblk.sum())
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.zeros((B, int(nblk.max())), dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+    k = rng.standard_normal((NB, Hkv, P, d))
+    v = rng.standard_normal((NB, Hkv, P, d))
+    q = rng.standard_normal((B, Hq, d))
+    rho = 0.4 * rng.standard_normal((B, Hq, d))
+    G = Hq // Hkv
+    for W in (1, 5, 10):
+        o = oracle.decode(q, rho, k, v, 0.5, seq_lens=lens, block_table=table, window=W)
+        for b in range(B):
+            L = int(lens[b])
+            j = np.arange(max(0, L - W), L)
+            for h in range(Hq):
+                K = k[table[b, j // P], h // G, j % P]
+                V = v[table[b, j // P], h // G, j % P]
+                assert rel_err(o[b, h], _np_parallax(q[b, h], rho[b, h], K, V, 0.5)) < 1e-12
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("W", [1, 2, 5, 36])
+def test_window_prefill_against_numpy(form, W):
+    q, rho, k, v = _prefill_case(33)
+    B, S, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    rows = np.array([0, 1, 4, 5, 17, 36], dtype=np.int32)
+    o = oracle.prefill(q, rho, k, v, 0.4, rows=rows, form=form, window=W)
+    for ri, i in enumerate(rows):
+        j0 = max(0, int(i) - W + 1)
+        for b in range(B):
+            for h in range(Hq):
+                K, V = k[b, j0:i + 1, h // G], v[b, j0:i + 1, h // G]
+                assert rel_err(o[b, ri, h], _np_parallax(q[b, i, h], rho[b, i, h], K, V, 0.4)) \
+                    < 1e-12, (i, b, h, W)
+
+
+def test_window_mutants_are_caught():
+    """A window one key too wide, or counted from the oldest key, fails the
+    numpy pin."""
+    q, rho, k, v, lens = _window_decode_case(34)
+    G = q.shape[1] // k.shape[1]
+    W = 3
+    wrong = {
+        "one key too many": lambda L: (max(0, L - W - 1), L),
+        "oldest keys": lambda L: (0, min(L, W)),
+    }
+    for name, rng_of in wrong.items():
+        worst = 0.0
+        for b in range(q.shape[0]):
+            L = int(lens[b])
+            j0, j1 = rng_of(L)
+            for h in range(q.shape[1]):
+                got = oracle.decode(q[b:b + 1, h:h + 1], rho[b:b + 1, h:h + 1],
+                                    k[b:b + 1, h // G:h // G + 1, j0:j1],
+                                    v[b:b + 1, h // G:h // G + 1, j0:j1], 0.45)[0, 0]
+                lo = max(0, L - W)
+                want = _np_parallax(q[b, h], rho[b, h], k[b, h // G, lo:L], v[b, h // G, lo:L],
+                                    0.45)
+                worst = max(worst, rel_err(got, want))
+        assert worst > 1e-6, name
