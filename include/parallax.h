@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 1
+#define PARALLAX_ABI_VERSION 2
 
 typedef enum {
     PARALLAX_OK = 0,
@@ -65,6 +65,13 @@ typedef enum { PARALLAX_F32 = 0, PARALLAX_BF16 = 1 } parallax_dtype_t;
  * cached token 0 .. L_b-1 of its KV head (the cache already holds the
  * current token).  L_b = seq_lens[b] if seq_lens is given, else max_seq_len.
  * A row with L_b = 0 yields o = 0.
+ *
+ * Local window (window >= 1): the row attends to its last `window` cached
+ * tokens only, max(0, L_b - window) .. L_b-1 -- the local window that the
+ * same page leaves open (section 3.1); window = 0 is full attention.  Tokens
+ * before the window are never read, nor is any address formed from the page
+ * id of a page that holds only such tokens (its block-table entry may be
+ * read), so they may hold anything.
  *
  * Cache layouts (`kv_dtype` elements; k and v each have their own strides):
  *   contiguous (block_table == NULL): token j of (b, hk) at
@@ -114,6 +121,8 @@ typedef struct {
 
     int32_t split_tokens; /* tokens per context split; 0 = chosen by the library,
                              else a positive multiple of 256 */
+    int32_t window;       /* 0 = every cached token; W >= 1 = each row's last W tokens;
+                             < 0 is PARALLAX_ERR_INVALID_ARG (added in ABI version 2) */
 } parallax_decode_args_t;
 
 /*
@@ -134,7 +143,8 @@ parallax_status_t parallax_decode(const parallax_decode_args_t *args, void *work
 /* ------------------------------------------------------------ prefill --- */
 /*
  * Causal prefill: row i of (b, h) attends to keys 0..i of KV head
- * h / (Hq/Hkv).  q, rho bf16 [B, S, Hq, d]; k, v bf16 [B, S, Hkv, d];
+ * h / (Hq/Hkv) -- with a local window W >= 1 (see decode) to keys
+ * max(0, i-W+1) .. i only.  q, rho bf16 [B, S, Hq, d]; k, v bf16 [B, S, Hkv, d];
  * out fp32 [B, S, Hq, d].  causal must be 1; head_dim must be 128; the GQA
  * group Hq/Hkv must be 1, 2 or 4 (else PARALLAX_ERR_UNSUPPORTED).  Products
  * run on the bf16 matrix cores with fp32 accumulation; the softmax
@@ -160,6 +170,8 @@ typedef struct {
     int64_t v_stride_b, v_stride_s, v_stride_h;
     float *out;
     int64_t out_stride_b, out_stride_s, out_stride_h;
+    int32_t window; /* 0 = keys 0..i; W >= 1 = keys max(0, i-W+1)..i; < 0 is
+                       PARALLAX_ERR_INVALID_ARG (added in ABI version 2) */
 } parallax_prefill_args_t;
 
 parallax_status_t parallax_prefill(const parallax_prefill_args_t *args, void *hip_stream);

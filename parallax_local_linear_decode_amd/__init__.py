@@ -30,7 +30,7 @@ PARALLAX_ERR_WORKSPACE = 3
 PARALLAX_ERR_HIP = 4
 PARALLAX_F32 = 0
 PARALLAX_BF16 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _i32, _i64, _u32, _f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float,
                                ctypes.c_void_p)
@@ -50,6 +50,7 @@ class DecodeArgs(ctypes.Structure):
         ("seq_lens", _vp), ("max_seq_len", _i32),
         ("block_table", _vp), ("block_size", _i32), ("max_blocks_per_seq", _i32),
         ("split_tokens", _i32),
+        ("window", _i32),
     ]
 
 
@@ -63,6 +64,7 @@ class PrefillArgs(ctypes.Structure):
         ("k", _vp), ("k_stride_b", _i64), ("k_stride_s", _i64), ("k_stride_h", _i64),
         ("v", _vp), ("v_stride_b", _i64), ("v_stride_s", _i64), ("v_stride_h", _i64),
         ("out", _vp), ("out_stride_b", _i64), ("out_stride_s", _i64), ("out_stride_h", _i64),
+        ("window", _i32),
     ]
 
 
@@ -130,7 +132,8 @@ def _stream_handle(t: torch.Tensor, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _decode_args(q, rho, k, v, out, scale, seq_lens, block_table, max_seq_len, split_tokens):
+def _decode_args(q, rho, k, v, out, scale, seq_lens, block_table, max_seq_len, split_tokens,
+                 window=0):
     if q.dim() != 3 or rho.shape != q.shape:
         raise ValueError("q and rho must be [B, Hq, d] of the same shape")
     if q.dtype != torch.float32 or rho.dtype != torch.float32 or out.dtype != torch.float32:
@@ -172,6 +175,7 @@ def _decode_args(q, rho, k, v, out, scale, seq_lens, block_table, max_seq_len, s
         a.block_size = k.shape[2]
         a.max_blocks_per_seq = block_table.shape[1]
     a.split_tokens = int(split_tokens)
+    a.window = int(window)
     return a
 
 
@@ -190,11 +194,12 @@ def _workspace(device, stream, nbytes):
 
 
 def parallax_decode_workspace_size(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None,
-                                   max_seq_len=None, split_tokens=0) -> int:
+                                   max_seq_len=None, split_tokens=0, window=0) -> int:
     """Bytes of workspace parallax_decode needs for these tensors."""
     lib = load_library()
     # The size depends on shapes only; q stands in for the output tensor.
-    a = _decode_args(q, rho, k, v, q, scale, seq_lens, block_table, max_seq_len, split_tokens)
+    a = _decode_args(q, rho, k, v, q, scale, seq_lens, block_table, max_seq_len, split_tokens,
+                     window)
     nbytes = ctypes.c_size_t(0)
     st = lib.parallax_decode_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
     if st != PARALLAX_OK:
@@ -203,19 +208,22 @@ def parallax_decode_workspace_size(q, rho, k, v, *, scale=None, seq_lens=None, b
 
 
 def parallax_decode(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None,
-                    max_seq_len=None, out=None, workspace=None, split_tokens=0, stream=None):
+                    max_seq_len=None, out=None, workspace=None, split_tokens=0, window=0,
+                    stream=None):
     """Parallax decode over a contiguous ([B, Hkv, L, d]) or paged
     ([pages, Hkv, 16, d] + block_table [B, max_blocks]) KV cache.
 
     q, rho: float32 [B, Hq, d]; k, v: bfloat16 or float32; seq_lens int32 [B]
-    (required when paged).  Returns out float32 [B, Hq, d].  `workspace`, if
+    (required when paged).  window: 0 for every cached token, W >= 1 for each
+    row's last W tokens.  Returns out float32 [B, Hq, d].  `workspace`, if
     given, is a uint8 device tensor of at least
     parallax_decode_workspace_size(...) bytes (any contents).
     """
     lib = load_library()
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    a = _decode_args(q, rho, k, v, out, scale, seq_lens, block_table, max_seq_len, split_tokens)
+    a = _decode_args(q, rho, k, v, out, scale, seq_lens, block_table, max_seq_len, split_tokens,
+                     window)
     nbytes = ctypes.c_size_t(0)
     st = lib.parallax_decode_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
     if st != PARALLAX_OK:
@@ -231,9 +239,11 @@ def parallax_decode(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None
     return out
 
 
-def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, stream=None):
+def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, window=0,
+                     stream=None):
     """Causal Parallax prefill.  q, rho bf16 [B, S, Hq, d]; k, v bf16
-    [B, S, Hkv, d].  Returns out float32 [B, S, Hq, d]."""
+    [B, S, Hkv, d].  window: 0 for keys 0..i, W >= 1 for keys i-W+1..i.
+    Returns out float32 [B, S, Hq, d]."""
     lib = load_library()
     for name, t in (("q", q), ("rho", rho), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(-1) != 1:
@@ -253,6 +263,7 @@ def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, stream=
     a.k, a.k_stride_b, a.k_stride_s, a.k_stride_h = _ptr(k), *k.stride()[:3]
     a.v, a.v_stride_b, a.v_stride_s, a.v_stride_h = _ptr(v), *v.stride()[:3]
     a.out, a.out_stride_b, a.out_stride_s, a.out_stride_h = _ptr(out), *out.stride()[:3]
+    a.window = int(window)
     st = lib.parallax_prefill(ctypes.byref(a), _stream_handle(q, stream))
     if st != PARALLAX_OK:
         _raise(st, lib)

@@ -82,6 +82,7 @@ parallax_status_t plan_decode(const parallax_decode_args_t *a, DecodePlan *pl) {
     if (a->split_tokens < 0 || (a->split_tokens > 0 && a->split_tokens % kSplitQuantum != 0))
         return fail(PARALLAX_ERR_INVALID_ARG, "decode: split_tokens must be 0 or a multiple of %d",
                     kSplitQuantum);
+    if (a->window < 0) return fail(PARALLAX_ERR_INVALID_ARG, "decode: window must be >= 0");
     const bool paged = a->block_table != nullptr;
     if (paged) {
         if (a->seq_lens == nullptr)
@@ -114,8 +115,13 @@ parallax_status_t plan_decode(const parallax_decode_args_t *a, DecodePlan *pl) {
         return fail(PARALLAX_ERR_UNSUPPORTED, "decode: every stride must span a multiple of 16 bytes");
 
     const int64_t units = (int64_t)a->batch * a->num_kv_heads;
-    int split = a->split_tokens > 0 ? a->split_tokens : choose_split(units, a->max_seq_len);
-    int nsplit = (a->max_seq_len + split - 1) / split;
+    // tokens a row's splits cover at most: every cached token, or the window
+    // plus its start rounded down to a 32-token step
+    const int span = a->window > 0 && a->window < a->max_seq_len - 31
+                         ? a->window + 31
+                         : a->max_seq_len;
+    int split = a->split_tokens > 0 ? a->split_tokens : choose_split(units, span);
+    int nsplit = (span + split - 1) / split;
     if (units * nsplit > 0x7fffffffLL)
         return fail(PARALLAX_ERR_UNSUPPORTED, "decode: grid too large (%lld workgroups)",
                     (long long)(units * nsplit));
@@ -148,6 +154,7 @@ parallax_status_t check_prefill(const parallax_prefill_args_t *a) {
         if (s < 0) return fail(PARALLAX_ERR_INVALID_ARG, "prefill: strides must be non-negative");
     if (a->causal != 1)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: only causal = 1 is supported");
+    if (a->window < 0) return fail(PARALLAX_ERR_INVALID_ARG, "prefill: window must be >= 0");
     if (a->head_dim != 128)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 128)", a->head_dim);
     const int group = a->num_q_heads / a->num_kv_heads;
@@ -238,6 +245,7 @@ PLX_EXPORT parallax_status_t parallax_decode(const parallax_decode_args_t *a, vo
     p.nsplit = pl.nsplit;
     p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
     p.partials = pl.workspace_bytes > 0 ? static_cast<float *>(workspace) : nullptr;
+    p.window = a->window;
     return hip_status(plx::launch_decode(p, a->kv_dtype, a->head_dim, pl.group, pl.paged, a->batch,
                                          static_cast<hipStream_t>(hip_stream)),
                       "decode launch");
@@ -272,6 +280,7 @@ PLX_EXPORT parallax_status_t parallax_prefill(const parallax_prefill_args_t *a, 
     p.num_q_heads = a->num_q_heads;
     p.num_kv_heads = a->num_kv_heads;
     p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
+    p.window = a->window;
     return hip_status(plx::launch_prefill(p, a->head_dim, static_cast<hipStream_t>(hip_stream)),
                       "prefill launch");
 }

@@ -88,14 +88,23 @@ __device__ __forceinline__ uint4 load16(const void *p) {
     return *reinterpret_cast<const uint4 *>(p);
 }
 
-// Sequence length of batch row b, clamped to what the cache can hold, and
-// the number of splits that row uses (at least one, so an empty row still
-// gets its zero output written).
+// Window starts are rounded down to whole 32-token steps, so a step never
+// straddles more than two 16-token pages.
+constexpr int kWindowAlign = 32;
+
+// Sequence length L of batch row b, clamped to what the cache can hold; the
+// first token tb the row attends to (0, or L - window for the local-window
+// variant); tbase, tb rounded down to a step boundary, where split 0 starts
+// (tokens tbase .. tb-1 are masked); and the number of splits the row uses
+// (at least one, so an empty row still gets its zero output written).
 template <bool PAGED>
-__device__ __forceinline__ void row_extent(const DecodeParams &p, int b, int &L, int &nsp) {
+__device__ __forceinline__ void row_extent(const DecodeParams &p, int b, int &L, int &tb,
+                                           int &tbase, int &nsp) {
     L = p.seq_lens ? p.seq_lens[b] : p.max_seq_len;
     L = max(0, min(L, PAGED ? p.max_blocks * kDecodeStepTokens : p.max_seq_len));
-    nsp = max(1, min(p.nsplit, (L + p.split - 1) / p.split));
+    tb = p.window > 0 ? max(0, L - p.window) : 0;
+    tbase = tb & ~(kWindowAlign - 1);
+    nsp = max(1, min(p.nsplit, (L - tbase + p.split - 1) / p.split));
 }
 
 __device__ __forceinline__ float finish(float A, float B, float Z, float R) {
@@ -184,10 +193,10 @@ decode_mfma_kernel(DecodeParams p) {
     const int unit = blockIdx.x % units;
     const int b = unit / p.num_kv_heads;
     const int hk = unit % p.num_kv_heads;
-    int L, nsp;
-    row_extent<PAGED>(p, b, L, nsp);
+    int L, tb, tbase, nsp;
+    row_extent<PAGED>(p, b, L, tb, tbase, nsp);
     if (split_idx >= nsp) return;
-    const int t0 = split_idx * p.split;
+    const int t0 = tbase + split_idx * p.split;
     const int t1 = min(L, t0 + p.split);
     const int nsteps = (t1 - t0 + kMfmaStep - 1) / kMfmaStep;
 
@@ -234,12 +243,15 @@ decode_mfma_kernel(DecodeParams p) {
 
     // Loads of one step: K straight into score-operand layout (lane c, g of
     // row block rb holds token 16*rb + c, head-dim values DQ*g + 8*ks ..),
-    // V as coalesced 16-byte row pieces.  Tokens past t1 re-read token t1-1.
+    // V as coalesced 16-byte row pieces.  Tokens past t1 re-read token t1-1
+    // and tokens before the window start tb re-read token tb, so nothing
+    // outside the row's window is read (a page that lies wholly before the
+    // window supplies no address).
     auto issue_k = [&](int st, const Pages &pg, uint4 (&kr)[2][KS]) {
         const int base = t0 + st * kMfmaStep;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            const int j = min(base + 16 * rb + c, t1 - 1);
+            const int j = max(tb, min(base + 16 * rb + c, t1 - 1));
             const int64_t off = tok_off(j, base, pg, p.k_s0, p.k_sh, p.k_st) + DQ * g;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) kr[rb][ks] = load16(kc + off + 8 * ks);
@@ -249,7 +261,7 @@ decode_mfma_kernel(DecodeParams p) {
         const int base = t0 + st * kMfmaStep;
 #pragma unroll
         for (int u = 0; u < VLD; ++u) {
-            const int j = min(base + RPL * u + lane / LPR, t1 - 1);
+            const int j = max(tb, min(base + RPL * u + lane / LPR, t1 - 1));
             vr[u] = load16(vc + tok_off(j, base, pg, p.v_s0, p.v_sh, p.v_st) + 8 * (lane % LPR));
         }
     };
@@ -327,8 +339,10 @@ decode_mfma_kernel(DecodeParams p) {
         // k-slot r (0..7) of this lane's group <-> token of the step
         bool valid[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            valid[r] = base + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4) < t1;
+        for (int r = 0; r < 8; ++r) {
+            const int tok = base + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4);
+            valid[r] = tok < t1 && tok >= tb;
+        }
 
         bf16x8_t pw[NCS];
 #pragma unroll
@@ -481,10 +495,10 @@ __global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePara
     const int unit = blockIdx.x % units;
     const int b = unit / p.num_kv_heads;
     const int hk = unit % p.num_kv_heads;
-    int L, nsp;
-    row_extent<PAGED>(p, b, L, nsp);
+    int L, tb, tbase, nsp;
+    row_extent<PAGED>(p, b, L, tb, tbase, nsp);
     if (split_idx >= nsp) return;
-    const int t0 = split_idx * p.split;
+    const int t0 = tbase + split_idx * p.split;
     const int t1 = min(L, t0 + p.split);
     const int nsteps = (t1 - t0 + kDecodeStepTokens - 1) / kDecodeStepTokens;
 
@@ -509,6 +523,7 @@ __global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePara
     const float *vc = static_cast<const float *>(p.v);
     for (int st = wave; st < nsteps; st += kValuWaves) {
         const int base = t0 + st * kDecodeStepTokens;
+        if (base + kDecodeStepTokens <= tb) continue;  // step wholly before the window
         int64_t kb, vb;
         if constexpr (PAGED) {
             const int pg = p.block_table[(int64_t)b * p.max_blocks + base / kDecodeStepTokens];
@@ -521,13 +536,15 @@ __global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePara
         uint4 kw[U], vw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int j = min(base + u * TPL + row, t1 - 1);  // rows past t1 re-read t1-1
+            // rows past t1 re-read t1-1, rows before the window re-read tb
+            const int j = max(tb, min(base + u * TPL + row, t1 - 1));
             kw[u] = load16(kc + kb + (int64_t)j * p.k_st + sub * VEC);
             vw[u] = load16(vc + vb + (int64_t)j * p.v_st + sub * VEC);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool valid = base + u * TPL + row < t1;
+            const int tok = base + u * TPL + row;
+            const bool valid = tok < t1 && tok >= tb;
             const float kf[4] = {__uint_as_float(kw[u].x), __uint_as_float(kw[u].y),
                                  __uint_as_float(kw[u].z), __uint_as_float(kw[u].w)};
             const float vf[4] = {__uint_as_float(vw[u].x), __uint_as_float(vw[u].y),
@@ -614,8 +631,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const int unit = blockIdx.x;
     const int b = unit / p.num_kv_heads;
     const int hk = unit % p.num_kv_heads;
-    int L, nsp;
-    row_extent<PAGED>(p, b, L, nsp);
+    int L, tb, tbase, nsp;
+    row_extent<PAGED>(p, b, L, tb, tbase, nsp);
     if (nsp <= 1) return;  // written by the split kernel
     const float *recs = p.partials + (int64_t)unit * p.nsplit * G * REC;
     for (int idx = threadIdx.x; idx < G * D; idx += 256) {
@@ -664,7 +681,11 @@ hipError_t launch_all(const DecodeParams &p, bool bf16, int batch, hipStream_t s
     const dim3 grid((unsigned)((int64_t)units * p.nsplit));
     if (bf16) {
         constexpr int NWMAX = mfma_waves_max<D, G>();
-        const int steps = (min(p.split, p.max_seq_len) + kMfmaStep - 1) / kMfmaStep;
+        // tokens a row's splits cover at most (as the host sized the split)
+        const int span = p.window > 0 && p.window < p.max_seq_len - (kWindowAlign - 1)
+                             ? p.window + kWindowAlign - 1
+                             : p.max_seq_len;
+        const int steps = (min(p.split, span) + kMfmaStep - 1) / kMfmaStep;
         if (NWMAX == 8 && steps > kShortSteps && grid.x <= (unsigned)kDeviceCUs)
             hipLaunchKernelGGL((decode_mfma_kernel<D, G, PAGED, NWMAX>), grid, dim3(64 * NWMAX), 0,
                                stream, p);

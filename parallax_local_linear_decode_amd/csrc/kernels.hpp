@@ -33,6 +33,7 @@ struct DecodeParams {
     int32_t nsplit;     // splits per (batch, kv head) in the grid
     float scale_log2;   // logit scale times log2(e): logits are kept in base 2
     float *partials;    // [B*Hkv*nsplit][G][partial_floats(d)] or null when nsplit == 1
+    int32_t window;     // 0: every cached token; W >= 1: each row's last W tokens
 };
 
 struct PrefillParams {
@@ -48,6 +49,7 @@ struct PrefillParams {
     int64_t o_sb, o_ss, o_sh;
     int32_t batch, seq_len, num_q_heads, num_kv_heads;
     float scale_log2;
+    int32_t window;  // 0: keys 0..i; W >= 1: keys max(0, i-W+1)..i
 };
 
 // Launchers (defined next to their kernels).  They return the HIP status of

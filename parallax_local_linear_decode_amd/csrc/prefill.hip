@@ -72,7 +72,9 @@ __device__ __forceinline__ float group_max(float x) {
     return fmaxf(__builtin_bit_cast(float, (int)b2[0]), __builtin_bit_cast(float, (int)b2[1]));
 }
 
-template <int G>
+// WIN: the local-window form (instantiated separately, so full causal
+// attention carries none of its index arithmetic).
+template <int G, bool WIN>
 __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p) {
     constexpr int D = kPfD;
     constexpr int KS = D / 32;                      // score MFMAs per 16-key block
@@ -107,6 +109,12 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
     const int key_end = min(S, (qb + 1) * QB);        // keys this workgroup needs
     const int ntiles = (key_end + kPfKeys - 1) / kPfKeys;
     const int pair_tiles = min(ntiles, (min(S, r0 + kPfRows) + kPfKeys - 1) / kPfKeys);
+    // Local window W >= 1: row i keeps keys i-W+1 .. i.  Tiles below the
+    // workgroup's first needed key are skipped; the loop starts on an even
+    // tile (the LDS buffer of tile t is t & 1, fixed at compile time).
+    const int W = WIN ? p.window : 0;
+    const int t_first = (W > 0 ? max(0, qb * QB - W + 1) / kPfKeys : 0) & ~1;
+    const int pair_lo = W > 0 ? max(0, r0 - W + 1) / kPfKeys : 0;  // first tile of this pair
 
     // ---- cooperative tile loads: thread t moves 16 bytes (chunk t%16) of key
     // t/16.  Tiles travel through two register stages per operand, so a K or V
@@ -146,12 +154,12 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
     // K tile 0 into LDS; K tiles 1, 2 and V tiles 0, 1 in flight, in the
     // order the loop keeps them.
     auto prologue = [&] {
-        issue_k(0, kst[0]);
+        issue_k(t_first, kst[0]);
         store(ktile[0], kst[0]);
-        issue_k(1, kst[1]);
-        issue_v(0, vst[0]);
-        issue_k(2, kst[0]);
-        issue_v(1, vst[1]);
+        issue_k(t_first + 1, kst[1]);
+        issue_v(t_first, vst[0]);
+        issue_k(t_first + 2, kst[0]);
+        issue_v(t_first + 1, vst[1]);
         __syncthreads();
     };
 
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
         // wave through LDS.  A row's reference max moves (by select) only when
         // the tile's max exceeds it by more than kSlack; alpha < 1 then tells
         // the value wave to rescale that row's sums first.  MASK: the tile
-        // crosses the diagonal or S.
+        // crosses the diagonal, S or (local window) a row's window start.
         auto numerators = [&](int t, const f32x4_t (&d1)[2][4], auto mask_tag) {
             constexpr bool MASK = decltype(mask_tag)::value;
             // The two 16-row halves (qc) run side by side, phase by phase, so
@@ -213,7 +221,9 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
                     sv[qc][r] = r < 4 ? d1[0][qc][r] : d1[1][qc][r - 4];
                     if constexpr (MASK) {
                         const int key = t * kPfKeys + (r < 4 ? 4 * g + r : 16 + 4 * g + r - 4);
-                        sv[qc][r] = key <= qi && key < S ? sv[qc][r] : -INFINITY;
+                        sv[qc][r] = key <= qi && key < S && (W == 0 || key > qi - W)
+                                        ? sv[qc][r]
+                                        : -INFINITY;
                     }
                     tmax = __builtin_fmaxf(tmax, sv[qc][r]);
                 }
@@ -227,7 +237,15 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
                 const float tm2 = gm[qc] * c2;
                 mnew[qc] = tm2 > mref[qc] + kSlack ? tm2 : mref[qc];
                 alpha[qc] = __builtin_amdgcn_exp2f(mref[qc] - mnew[qc]);  // 1 unless moved
+                if constexpr (MASK && WIN) {
+                    // a row that has met no key yet (its window starts past
+                    // this tile) keeps m = -inf: weights 0, factor 1
+                    if (mnew[qc] == -INFINITY) alpha[qc] = 1.0f;
+                }
                 mref[qc] = mnew[qc];
+                if constexpr (MASK && WIN) {
+                    if (mnew[qc] == -INFINITY) mnew[qc] = 0.0f;  // exp2(-inf - 0) = 0 below
+                }
             }
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc) {
@@ -249,10 +267,12 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
             }
         };
         auto score_step = [&](int t) {
-            if (t < pair_tiles) {
+            if (t >= pair_lo && t < pair_tiles) {
                 f32x4_t d1[2][4];
                 scores(t, d1);
-                if (t * kPfKeys + kPfKeys - 1 <= r0 && t * kPfKeys + kPfKeys <= S)
+                // no masking when every key of the tile is in every row's range
+                if (t * kPfKeys + kPfKeys - 1 <= r0 && t * kPfKeys + kPfKeys <= S &&
+                    (W == 0 || t * kPfKeys > r0 + kPfRows - 1 - W))
                     numerators(t, d1, std::false_type{});
                 else
                     numerators(t, d1, std::true_type{});
@@ -262,7 +282,7 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
         // time.  Both halves always run (iterations past the last tile do no
         // math), so the two roles pass the same number of barriers.
         prologue();
-        for (int t = 0; t <= ntiles; t += 2) {
+        for (int t = t_first; t <= ntiles; t += 2) {
             score_step(t);
             advance(t, std::integral_constant<int, 0>{});
             score_step(t + 1);
@@ -320,10 +340,10 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
         };
 
         prologue();
-        for (int t = 0; t <= ntiles; t += 2) {
-            if (t >= 1 && t - 1 < pair_tiles) value_tile(t - 1);
+        for (int t = t_first; t <= ntiles; t += 2) {
+            if (t - 1 >= pair_lo && t - 1 < pair_tiles) value_tile(t - 1);
             advance(t, std::integral_constant<int, 0>{});
-            if (t < pair_tiles) value_tile(t);
+            if (t >= pair_lo && t < pair_tiles) value_tile(t);
             advance(t + 1, std::integral_constant<int, 1>{});
         }
 
@@ -360,10 +380,14 @@ hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream) {
     const int qb_rows = kPfRows * kPfPairs / G;
     const dim3 grid((unsigned)(units * ((p.seq_len + qb_rows - 1) / qb_rows)));
     const dim3 block(128 * kPfPairs);
-    switch (G) {
-        case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, block, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, block, 0, stream, p); break;
-        case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, block, 0, stream, p); break;
+    const bool win = p.window > 0 && p.window < p.seq_len;  // else every key 0..i is in range
+    switch (G * 2 + (win ? 1 : 0)) {
+        case 2: hipLaunchKernelGGL((prefill_kernel<1, false>), grid, block, 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((prefill_kernel<1, true>), grid, block, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<2, false>), grid, block, 0, stream, p); break;
+        case 5: hipLaunchKernelGGL((prefill_kernel<2, true>), grid, block, 0, stream, p); break;
+        case 8: hipLaunchKernelGGL((prefill_kernel<4, false>), grid, block, 0, stream, p); break;
+        case 9: hipLaunchKernelGGL((prefill_kernel<4, true>), grid, block, 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -35,13 +35,14 @@ def assert_parity(gpu, ref, tau, rms_gate=None, what=""):
     return ratio, rms
 
 
-def oracle_decode(inp, *, form="streaming", seq_lens=None, rows=None):
+def oracle_decode(inp, *, form="streaming", seq_lens=None, rows=None, window=0):
     """Run the oracle on a DecodeInputs (torch tensors, any device)."""
     sl = inp.seq_lens if seq_lens is None else seq_lens
     sl = None if sl is None else host_array(sl).astype(np.int32)
     bt = None if inp.block_table is None else host_array(inp.block_table)
     return oracle.decode(host_array(inp.q), host_array(inp.rho), host_array(inp.k),
-                         host_array(inp.v), inp.scale, seq_lens=sl, block_table=bt, form=form)
+                         host_array(inp.v), inp.scale, seq_lens=sl, block_table=bt, form=form,
+                         window=window)
 
 
 def gather_sequences(inp, batch_ids):

@@ -94,6 +94,7 @@ UNSUPP = plx.PARALLAX_ERR_UNSUPPORTED
     (dict(split_tokens=100), INVALID, "split_tokens"),
     (dict(split_tokens=64), INVALID, "split_tokens"),
     (dict(split_tokens=-256), INVALID, "split_tokens"),
+    (dict(window=-1), INVALID, "window"),
     (dict(block_table=FAKE, block_size=16, max_blocks_per_seq=256), INVALID, "seq_lens"),
     (dict(block_table=FAKE, seq_lens=FAKE, block_size=32, max_blocks_per_seq=256), UNSUPP,
      "block_size"),
@@ -159,9 +160,35 @@ def good_prefill(**over):
     (dict(v=FAKE + 2), UNSUPP, "aligned"),
     (dict(q_stride_s=2052), UNSUPP, "16 bytes"),
     (dict(out_stride_h=130), UNSUPP, "16 bytes"),
+    (dict(window=-5), INVALID, "window"),
 ])
 def test_prefill_rejects(lib, over, status, needle):
     a = good_prefill(**over)
     assert lib.parallax_prefill(ctypes.byref(a), None) == status
     assert needle in plx.parallax_last_error()
     assert lib.parallax_prefill(None, None) == INVALID
+
+
+def test_version_1_structs_are_rejected(lib):
+    """ABI version 2 appended `window` to both argument structs; a caller
+    built against version 1 passes the old, smaller struct_size."""
+    old_decode = ctypes.sizeof(plx.DecodeArgs) - 8
+    old_prefill = ctypes.sizeof(plx.PrefillArgs) - 8
+    st, _ = ws_size(lib, good_decode(struct_size=old_decode))
+    assert st == INVALID and "struct_size" in plx.parallax_last_error()
+    assert lib.parallax_prefill(ctypes.byref(good_prefill(struct_size=old_prefill)), None) == INVALID
+
+
+def test_window_shrinks_the_split_plan(lib):
+    """A local window bounds the tokens a row's splits cover (window + 31), so
+    fewer splits and less workspace than full attention over the cache."""
+    full = good_decode(batch=1, max_seq_len=32768,
+                       k_stride_0=8 * 32768 * 128, k_stride_h=32768 * 128,
+                       v_stride_0=8 * 32768 * 128, v_stride_h=32768 * 128)
+    st, n_full = ws_size(lib, full)
+    assert st == plx.PARALLAX_OK and n_full > 0
+    full.window = 100
+    st, n_win = ws_size(lib, full)
+    assert st == plx.PARALLAX_OK and n_win == 0
+    full.window = 40000  # at least the cache: same plan as full attention
+    assert ws_size(lib, full) == (plx.PARALLAX_OK, n_full)
