@@ -96,7 +96,7 @@ def time_launches(torch, launch, n_bufs, steps, warmup):
     return start.elapsed_time(end) / 1000.0  # seconds
 
 
-def make_decode_launcher(torch, plx, sets, out, split):
+def make_decode_launcher(torch, plx, sets, out, split, window=0):
     """Pre-marshalled C-ABI calls, one per input copy, so the host loop is a
     single ctypes call per step."""
     import ctypes
@@ -105,7 +105,7 @@ def make_decode_launcher(torch, plx, sets, out, split):
     calls = []
     for inp in sets:
         a = plx._decode_args(inp.q, inp.rho, inp.k, inp.v, out, inp.scale, inp.seq_lens,
-                             inp.block_table, None, split)
+                             inp.block_table, None, split, window)
         n = ctypes.c_size_t(0)
         st = lib.parallax_decode_workspace_size(ctypes.byref(a), ctypes.byref(n))
         if st != 0:
@@ -122,7 +122,7 @@ def make_decode_launcher(torch, plx, sets, out, split):
     return launch
 
 
-def cpu_baseline_decode(inp, nbytes, budget_s=10.0):
+def cpu_baseline_decode(inp, nbytes, budget_s=10.0, window=0):
     """The oracle (fp64 C, all host cores) on the same workload; repeated until
     about budget_s of wall time has passed."""
     import oracle
@@ -137,7 +137,7 @@ def cpu_baseline_decode(inp, nbytes, budget_s=10.0):
     while elapsed < budget_s and reps < 100000:
         t = time.perf_counter()
         ref = oracle.decode(args["q"], args["rho"], args["k"], args["v"], inp.scale,
-                            seq_lens=sl, block_table=bt, threads=threads)
+                            seq_lens=sl, block_table=bt, window=window, threads=threads)
         elapsed += time.perf_counter() - t
         reps += 1
     per = elapsed / reps
@@ -177,14 +177,15 @@ def read_stream(torch, plx, nbytes, n_bufs, steps, warmup):
 
 def run_decode(args, torch, plx):
     from parallax_local_linear_decode_amd.workloads import decode_inputs
-    B, Hq, Hkv, d, L = args.batch, 16, 8, 128, args.ctx
+    B, Hq, Hkv, d, L, W = args.batch, 16, 8, 128, args.ctx, args.window
+    Lw = min(L, W) if W > 0 else L  # tokens each row reads
     dev = torch.device("cuda:0")
-    kv_bytes = B * Hkv * L * d * 2 * 2
-    n_bufs = max(1, math.ceil(args.cold_bytes / kv_bytes))
+    kv_bytes = B * Hkv * Lw * d * 2 * 2
+    n_bufs = max(1, math.ceil(args.cold_bytes / kv_bytes))  # rotation over the bytes read
     sets = [decode_inputs(B, Hq, Hkv, d, L, seed=i, device=dev) for i in range(n_bufs)]
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-    launch = make_decode_launcher(torch, plx, sets, out, args.split)
-    nbytes = decode_bytes(B, Hq, Hkv, d, [L] * B)
+    launch = make_decode_launcher(torch, plx, sets, out, args.split, W)
+    nbytes = decode_bytes(B, Hq, Hkv, d, [Lw] * B)
 
     # parity gate on the data being timed (copy 0) before any number is reported
     launch(0)
@@ -192,25 +193,26 @@ def run_decode(args, torch, plx):
     gpu0 = out.double().cpu().numpy()
     cpu = None
     if args.cpu_baseline:
-        ref, cpu = cpu_baseline_decode(sets[0], nbytes)
+        ref, cpu = cpu_baseline_decode(sets[0], nbytes, window=W)
         gate(gpu0, ref, 2e-2, 1e-3)
 
     secs = time_launches(torch, launch, n_bufs, args.steps, args.warmup)
     per = secs / args.steps
     warm = time_launches(torch, launch, 1, args.steps, args.warmup) / args.steps
     gbps = nbytes / per / 1e9
-    traffic = traffic_for("decode")
+    traffic = traffic_for("decode") if W <= 0 else None
     stream_ref = read_stream(torch, plx, kv_bytes, n_bufs, args.steps, args.warmup)
     return {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s",
         "ms_per_step": per * 1e3, "dtype": DECODE_DTYPE,
         "config": {"workload": f"decode: batch {B}, 16 query / 8 KV heads, d 128, ctx {L}, "
-                               "contiguous bf16 KV cache, fp32 q/rho/out",
+                               "contiguous bf16 KV cache, fp32 q/rho/out"
+                               + (f", local window {W} (bytes of the window)" if W > 0 else ""),
                    "batch": B, "ctx": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": d, "kv_dtype": "bf16", "cold_copies": n_bufs,
-                   "split_tokens": args.split},
+                   "split_tokens": args.split, "window": W},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "tokens_per_s": B / per, "kv_tokens_per_s": B * L / per,
+        "tokens_per_s": B / per, "kv_tokens_per_s": B * Lw / per,
         "warm_cache_gbps": round(nbytes / warm / 1e9, 2),
         "read_stream": stream_ref,
         "frac_of_read_stream": None if not stream_ref else round(gbps / stream_ref["gbps"], 4),
@@ -302,11 +304,19 @@ def run_copy(args, torch, plx):
             "config": {"workload": f"copy {n} bytes"}, "roofline": None, "cpu_baseline": None}
 
 
-def prefill_flops(B, S, Hq, d):
+def causal_pairs(S, window=0):
+    """(query, key) pairs of one causal sequence: row i sees i+1 keys, or
+    min(i+1, window) with a local window."""
+    if window <= 0 or window >= S:
+        return S * (S + 1) // 2
+    return window * (window + 1) // 2 + (S - window) * window
+
+
+def prefill_flops(B, S, Hq, d, window=0):
     """Algorithmic flops: per causal (query, key) pair and query head, the two
     score products (q.k, rho.k) and the two value products (E v, E t v), each
     2*d flops."""
-    return 4 * 2 * d * (S * (S + 1) // 2) * B * Hq
+    return 4 * 2 * d * causal_pairs(S, window) * B * Hq
 
 
 def run_prefill(args, torch, plx):
@@ -328,6 +338,7 @@ def run_prefill(args, torch, plx):
     a.k, a.k_stride_b, a.k_stride_s, a.k_stride_h = k.data_ptr(), *k.stride()[:3]
     a.v, a.v_stride_b, a.v_stride_s, a.v_stride_h = v.data_ptr(), *v.stride()[:3]
     a.out, a.out_stride_b, a.out_stride_s, a.out_stride_h = out.data_ptr(), *out.stride()[:3]
+    a.window = W = args.window
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def launch(i):
@@ -350,32 +361,35 @@ def run_prefill(args, torch, plx):
             batch = np.sort(order[done:done + n])
             t0 = time.perf_counter()
             refs.append((batch, oracle.prefill(hq, hr, hk, hv, scale, rows=batch,
-                                               threads=threads)))
+                                               window=W, threads=threads)))
             secs += time.perf_counter() - t0
             done += n
             n *= 2
         rows = np.concatenate([r for r, _ in refs])
         ref = np.concatenate([o for _, o in refs], axis=1)
         gate(out[:, rows.tolist()].double().cpu().numpy(), ref, 2e-2, 1e-2)
-        frac = float(np.sum(rows + 1)) / (S * (S + 1) / 2)
+        seen = rows + 1 if W <= 0 else np.minimum(rows + 1, W)
+        frac = float(np.sum(seen)) / causal_pairs(S, W)
         full = secs / frac
-        cpu = {"value": prefill_flops(B, S, Hq, d) / full / 1e12, "unit": "TFLOP/s",
+        cpu = {"value": prefill_flops(B, S, Hq, d, W) / full / 1e12, "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle", "seconds_per_step": full,
                "sample": f"{rows.size} query rows x all (batch, head), fp64 streaming form; "
                          f"time scaled by causal pairs ({secs:.1f} s measured)"}
     secs = time_launches(torch, launch, 1, args.steps, args.warmup)
     per = secs / args.steps
-    tflops = prefill_flops(B, S, Hq, d) / per / 1e12
+    tflops = prefill_flops(B, S, Hq, d, W) / per / 1e12
+    wtxt = f", local window {W}" if W > 0 else ""
     return {
         "metric": "Parallax causal prefill TFLOP/s (% of bf16 MFMA peak)", "value": round(tflops, 1),
         "unit": "TFLOP/s", "ms_per_step": per * 1e3, "dtype": "bf16",
         "config": {"workload": "causal prefill: batch 4, seq 8192, 16 query / 8 KV heads, d 128, "
-                               "bf16 q/rho/k/v, fp32 out", "batch": B, "seq_len": S},
+                               f"bf16 q/rho/k/v, fp32 out{wtxt}", "batch": B, "seq_len": S,
+                   "window": W},
         "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "tokens_per_s": B * S / per,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_for("prefill")},
+                     "traffic": traffic_for("prefill") if W <= 0 else None},
         "cpu_baseline": cpu,
     }
 
@@ -399,6 +413,8 @@ def main():
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--ctx", type=int, default=4096)
     ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="local window for decode / prefill (0 = full attention)")
     ap.add_argument("--cold-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
