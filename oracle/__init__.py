@@ -11,6 +11,12 @@ Transformers a 'Second Eye'", section 1.3): for each query row,
 ``o = o_SA - S_KV @ rho`` with ``o_SA`` the softmax attention output and
 ``S_KV`` the softmax-weighted, centred covariance of values against keys.
 
+The training side (same page, section 2.2 trains the layer end to end):
+``prefill_stats`` gives the per-row quantities a forward pass keeps (log of
+the softmax denominator, ``r``, ``o_SA``) and ``prefill_backward`` the
+gradients of ``sum(dout * out)`` with respect to q, rho, k and v, by the chain
+rule through the forward steps.
+
 Array conventions (numpy):
   * float64 / float32 arrays are read as such;
   * uint16 arrays are raw bfloat16 bit patterns (widened exactly).
@@ -61,6 +67,14 @@ def _load():
     lib.orc_prefill.argtypes = [i32, i32, i32, i32, i32, i32, i32, dbl,
                                 vp, i32, vp, i32, vp, vp, i32,
                                 vp, i32, i32, vp, i32]
+    lib.orc_prefill_stats.restype = i32
+    lib.orc_prefill_stats.argtypes = [i32, i32, i32, i32, i32, i32, dbl,
+                                      vp, i32, vp, i32, vp, vp, i32,
+                                      vp, i32, i32, vp, vp, vp, i32]
+    lib.orc_prefill_backward.restype = i32
+    lib.orc_prefill_backward.argtypes = [i32, i32, i32, i32, i32, i32, dbl,
+                                         vp, i32, vp, i32, vp, vp, i32, vp, i32,
+                                         vp, i32, i32, vp, vp, vp, vp, i32]
     _lib = lib
     return lib
 
@@ -182,3 +196,80 @@ def prefill(q, rho, k, v, scale, *, rows=None, form="streaming", window=0, threa
     if rc != 0:
         raise ValueError("oracle: orc_prefill rejected its arguments")
     return out
+
+
+def _prefill_common(q, rho, k, v):
+    q = np.ascontiguousarray(q)
+    rho = np.ascontiguousarray(rho)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    B, S, Hq, dk = q.shape
+    Hkv = k.shape[2]
+    dv = v.shape[3]
+    if rho.shape != q.shape or k.shape != (B, S, Hkv, dk) or v.shape[:3] != (B, S, Hkv):
+        raise ValueError("inconsistent prefill shapes")
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
+    return q, rho, k, v, (B, S, Hq, Hkv, dk, dv)
+
+
+def _rows(rows, S):
+    if rows is None:
+        rows = np.arange(S, dtype=np.int32)
+    return np.ascontiguousarray(rows, dtype=np.int32)
+
+
+def prefill_stats(q, rho, k, v, scale, *, rows=None, window=0, threads=None):
+    """What a causal prefill forward pass keeps for its backward pass, per
+    (batch, row, query head): ``lse`` = natural log of sum_j exp(scale q.k_j)
+    over the row's keys, ``r`` = sum_j p_j (rho . k_j), ``a`` = o_SA.
+
+    Shapes as ``prefill``.  Returns lse [B, R, Hq], r [B, R, Hq],
+    a [B, R, Hq, dv] (float64; R = len(rows)).
+    """
+    lib = _load()
+    q, rho, k, v, (B, S, Hq, Hkv, dk, dv) = _prefill_common(q, rho, k, v)
+    rows = _rows(rows, S)
+    lse = np.empty((B, rows.size, Hq), dtype=np.float64)
+    r = np.empty((B, rows.size, Hq), dtype=np.float64)
+    a = np.empty((B, rows.size, Hq, dv), dtype=np.float64)
+    rc = lib.orc_prefill_stats(B, S, Hq, Hkv, dk, dv, float(scale),
+                               _ptr(q), _dtype_code(q), _ptr(rho), _dtype_code(rho),
+                               _ptr(k), _ptr(v), _dtype_code(k),
+                               _ptr(rows), int(rows.size), int(window),
+                               _ptr(lse), _ptr(r), _ptr(a), int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle: orc_prefill_stats rejected its arguments")
+    return lse, r, a
+
+
+def prefill_backward(q, rho, k, v, dout, scale, *, rows=None, window=0, threads=None):
+    """Gradients of sum(dout * prefill(q, rho, k, v)) (causal, optional window).
+
+    dout : [B, S, Hq, dv]
+    rows : query rows whose terms are included (default all).  dq and drho are
+           returned for these rows; dk and dv sum these rows' contributions
+           only, so they are exact for key j when every row that sees key j
+           is included.
+    Returns dq [B, R, Hq, dk], drho [B, R, Hq, dk], dk [B, S, Hkv, dk],
+    dv [B, S, Hkv, dv] (float64).
+    """
+    lib = _load()
+    q, rho, k, v, (B, S, Hq, Hkv, dk, dv) = _prefill_common(q, rho, k, v)
+    dout = np.ascontiguousarray(dout)
+    if dout.shape != (B, S, Hq, dv):
+        raise ValueError("dout must be [B, S, Hq, dv]")
+    rows = _rows(rows, S)
+    dq = np.empty((B, rows.size, Hq, dk), dtype=np.float64)
+    drho = np.empty_like(dq)
+    dkk = np.empty((B, S, Hkv, dk), dtype=np.float64)
+    dvv = np.empty((B, S, Hkv, dv), dtype=np.float64)
+    rc = lib.orc_prefill_backward(B, S, Hq, Hkv, dk, dv, float(scale),
+                                  _ptr(q), _dtype_code(q), _ptr(rho), _dtype_code(rho),
+                                  _ptr(k), _ptr(v), _dtype_code(k), _ptr(dout), _dtype_code(dout),
+                                  _ptr(rows), int(rows.size), int(window),
+                                  _ptr(dq), _ptr(drho), _ptr(dkk), _ptr(dvv),
+                                  int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle: orc_prefill_backward rejected its arguments")
+    return dq, drho, dkk, dvv

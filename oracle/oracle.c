@@ -43,6 +43,12 @@
  *   The second follows from the first because sum_j p_j (v_j - vbar) = 0, so
  *   S_KV rho = sum_j p_j t_j v_j - vbar (sum_j p_j t_j).
  *
+ * Training side (causal prefill): orc_prefill_stats gives the per-row
+ * quantities a forward pass keeps for its backward pass (log of the softmax
+ * denominator, r, o_SA) and orc_prefill_backward the gradients of
+ * sum(dout * out) with respect to q, rho, k and v, by the chain rule through
+ * the forward steps (written out above the two functions).
+ *
  * Arithmetic: fp64, libm exp, sequential sums in index order.  Build with
  * -ffp-contract=off so results do not depend on FMA contraction.
  */
@@ -364,4 +370,287 @@ int orc_prefill(int form, int B, int S, int Hq, int Hkv, int dk, int dv, double 
     J.n_units = (int64_t)B * n_rows * Hq;
     J.maxL = maxL;
     return orc_run(&J, nthreads);
+}
+
+/* ------------------------------------------------------------ training --- */
+/*
+ * Causal prefill, training side: the statistics a forward pass keeps for the
+ * backward pass, and the gradients.  Both are written from the definition:
+ * each query row recomputes its logits, weights and moments over its keys
+ * (row i sees keys j0 .. i, j0 = max(0, i-W+1) with a window W >= 1, else 0).
+ *
+ * The gradient follows the chain rule through the steps of the forward pass
+ * (page "Parallax: Parameterized Local Linear Attention Gives Transformers a
+ * 'Second Eye'", section 1.3 for the forward; section 2.2 for training the
+ * layer), for the scalar loss sum(dout * out):
+ *
+ *   o = a - b + a r        a = sum_j p_j v_j,  r = sum_j p_j t_j,
+ *                          b = sum_j p_j t_j v_j
+ *   gA = (1 + r) g,  gB = -g,  gR = a . g                    (g = dout row)
+ *   dp_j = gA . v_j + gR t_j + t_j (gB . v_j)
+ *   dt_j = p_j (gR + gB . v_j)
+ *   dv_j += p_j (gA + t_j gB)
+ *   ds_j = p_j (dp_j - sum_l p_l dp_l)                        (softmax)
+ *   dq   = scale sum_j ds_j k_j,  dk_j += scale ds_j q        (s = scale q.k)
+ *   drho = sum_j dt_j k_j,        dk_j += dt_j rho            (t = rho.k)
+ */
+
+typedef void (*orc_unit_fn)(const void *ctx, int64_t u, double *scratch);
+
+typedef struct {
+    const void *ctx;
+    orc_unit_fn fn;
+    int64_t n_units;
+    size_t scratch_doubles;
+    int nthreads, tid;
+    int failed;
+} orc_par_arg;
+
+static void *orc_par_worker(void *argp) {
+    orc_par_arg *a = (orc_par_arg *)argp;
+    double *scratch = (double *)malloc(sizeof(double) * (a->scratch_doubles ? a->scratch_doubles : 1));
+    if (scratch == NULL) {
+        a->failed = 1;
+        return NULL;
+    }
+    for (int64_t u = a->tid; u < a->n_units; u += a->nthreads) a->fn(a->ctx, u, scratch);
+    free(scratch);
+    return NULL;
+}
+
+/* Runs fn(ctx, u, scratch) for u = 0 .. n_units-1 on nthreads threads. */
+static int orc_parallel(const void *ctx, orc_unit_fn fn, int64_t n_units, size_t scratch_doubles,
+                        int nthreads) {
+    if (n_units <= 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if ((int64_t)nthreads > n_units) nthreads = (int)n_units;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    orc_par_arg *ta = (orc_par_arg *)calloc((size_t)nthreads, sizeof(orc_par_arg));
+    if (th == NULL || ta == NULL) {
+        free(th);
+        free(ta);
+        return -1;
+    }
+    int started = 0, rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        ta[i].ctx = ctx; ta[i].fn = fn; ta[i].n_units = n_units;
+        ta[i].scratch_doubles = scratch_doubles; ta[i].nthreads = nthreads; ta[i].tid = i;
+        if (i == 0) continue;
+        if (pthread_create(&th[i], NULL, orc_par_worker, &ta[i]) != 0) { rc = -1; break; }
+        started = i;
+    }
+    if (rc == 0) orc_par_worker(&ta[0]);
+    for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; ++i) rc |= ta[i].failed ? -1 : 0;
+    free(th);
+    free(ta);
+    return rc;
+}
+
+typedef struct {
+    int B, S, Hq, Hkv, dk, dv, window;
+    double scale;
+    const void *q, *rho, *k, *v, *dout;
+    int q_dtype, rho_dtype, kv_dtype, dout_dtype;
+    const int32_t *rows;
+    int n_rows;
+    /* stats outputs, [B, n_rows, Hq] (+ dv) */
+    double *lse, *rmean, *osa;
+    /* gradient outputs */
+    double *dq, *drho; /* [B, n_rows, Hq, dk] */
+    double *dkk, *dvv; /* [B, S, Hkv, dk] / [B, S, Hkv, dv] */
+} orc_train;
+
+static double orc_k(const orc_train *T, int b, int j, int hk, int e) {
+    return orc_get(T->k, T->kv_dtype, (((int64_t)b * T->S + j) * T->Hkv + hk) * T->dk + e);
+}
+
+static double orc_v(const orc_train *T, int b, int j, int hk, int c) {
+    return orc_get(T->v, T->kv_dtype, (((int64_t)b * T->S + j) * T->Hkv + hk) * T->dv + c);
+}
+
+/* One row's forward quantities over keys j0..i: weights p (normalised), probe
+ * projections t, the log of the softmax denominator (natural log, of the
+ * unshifted logits), r = sum p t and a = sum p v (o_SA).  Returns j0. */
+static int orc_row_forward(const orc_train *T, int b, int h, int i, const double *qd,
+                           const double *rd, double *p, double *t, double *lse, double *r,
+                           double *a) {
+    int hk = h / (T->Hq / T->Hkv);
+    int j0 = (T->window > 0 && i + 1 > T->window) ? i + 1 - T->window : 0;
+    double smax = -INFINITY;
+    for (int j = j0; j <= i; ++j) {
+        double qk = 0.0, tj = 0.0;
+        for (int e = 0; e < T->dk; ++e) {
+            double kje = orc_k(T, b, j, hk, e);
+            qk += qd[e] * kje;
+            tj += rd[e] * kje;
+        }
+        p[j - j0] = T->scale * qk;
+        t[j - j0] = tj;
+        if (p[j - j0] > smax) smax = p[j - j0];
+    }
+    double den = 0.0;
+    for (int j = j0; j <= i; ++j) {
+        p[j - j0] = exp(p[j - j0] - smax);
+        den += p[j - j0];
+    }
+    for (int j = j0; j <= i; ++j) p[j - j0] /= den;
+    *lse = smax + log(den);
+    double rr = 0.0;
+    for (int j = j0; j <= i; ++j) rr += p[j - j0] * t[j - j0];
+    *r = rr;
+    for (int c = 0; c < T->dv; ++c) a[c] = 0.0;
+    for (int j = j0; j <= i; ++j)
+        for (int c = 0; c < T->dv; ++c) a[c] += p[j - j0] * orc_v(T, b, j, hk, c);
+    return j0;
+}
+
+static void orc_load_row(const orc_train *T, int b, int h, int i, double *qd, double *rd) {
+    int64_t off = (((int64_t)b * T->S + i) * T->Hq + h) * T->dk;
+    for (int e = 0; e < T->dk; ++e) {
+        qd[e] = orc_get(T->q, T->q_dtype, off + e);
+        rd[e] = orc_get(T->rho, T->rho_dtype, off + e);
+    }
+}
+
+/* unit = (b, selected row, h) */
+static void orc_stats_unit(const void *ctx, int64_t u, double *w) {
+    const orc_train *T = (const orc_train *)ctx;
+    int64_t per_b = (int64_t)T->n_rows * T->Hq;
+    int b = (int)(u / per_b), ri = (int)((u % per_b) / T->Hq), h = (int)(u % T->Hq);
+    int i = T->rows[ri];
+    double *qd = w, *rd = qd + T->dk, *p = rd + T->dk, *t = p + T->S;
+    orc_load_row(T, b, h, i, qd, rd);
+    orc_row_forward(T, b, h, i, qd, rd, p, t, &T->lse[u], &T->rmean[u], T->osa + u * T->dv);
+}
+
+/* unit = (b, kv head): every selected row of the G query heads that read it,
+ * so the key/value gradients of this unit are summed by one thread in a
+ * fixed order. */
+static void orc_backward_unit(const void *ctx, int64_t u, double *w) {
+    const orc_train *T = (const orc_train *)ctx;
+    int b = (int)(u / T->Hkv), hk = (int)(u % T->Hkv);
+    int G = T->Hq / T->Hkv, dk = T->dk, dv = T->dv;
+    double *qd = w, *rd = qd + dk, *p = rd + dk, *t = p + T->S, *dp = t + T->S, *dt = dp + T->S;
+    double *a = dt + T->S, *bv = a + dv, *g = bv + dv, *gA = g + dv, *gB = gA + dv;
+    for (int h = hk * G; h < (hk + 1) * G; ++h) {
+        for (int ri = 0; ri < T->n_rows; ++ri) {
+            int i = T->rows[ri];
+            orc_load_row(T, b, h, i, qd, rd);
+            double lse, r;
+            int j0 = orc_row_forward(T, b, h, i, qd, rd, p, t, &lse, &r, a);
+            int n = i + 1 - j0;
+            /* b = sum_j p_j t_j v_j */
+            for (int c = 0; c < dv; ++c) bv[c] = 0.0;
+            for (int jj = 0; jj < n; ++jj)
+                for (int c = 0; c < dv; ++c) bv[c] += p[jj] * t[jj] * orc_v(T, b, j0 + jj, hk, c);
+            /* o = a - b + a r  ->  gA = (1 + r) g, gB = -g, gR = a . g */
+            int64_t go = (((int64_t)b * T->S + i) * T->Hq + h) * dv;
+            double gR = 0.0;
+            for (int c = 0; c < dv; ++c) {
+                g[c] = orc_get(T->dout, T->dout_dtype, go + c);
+                gA[c] = (1.0 + r) * g[c];
+                gB[c] = -g[c];
+                gR += a[c] * g[c];
+            }
+            /* a, r, b as sums over the keys -> gradients of p_j, t_j, v_j */
+            for (int jj = 0; jj < n; ++jj) {
+                int j = j0 + jj;
+                double gAv = 0.0, gBv = 0.0;
+                for (int c = 0; c < dv; ++c) {
+                    double vjc = orc_v(T, b, j, hk, c);
+                    gAv += gA[c] * vjc;
+                    gBv += gB[c] * vjc;
+                }
+                dp[jj] = gAv + gR * t[jj] + t[jj] * gBv;
+                dt[jj] = p[jj] * (gR + gBv);
+                double *dvo = T->dvv + (((int64_t)b * T->S + j) * T->Hkv + hk) * dv;
+                for (int c = 0; c < dv; ++c) dvo[c] += p[jj] * (gA[c] + t[jj] * gB[c]);
+            }
+            /* softmax: ds_j = p_j (dp_j - sum_l p_l dp_l); ds is kept in dp */
+            double pdp = 0.0;
+            for (int jj = 0; jj < n; ++jj) pdp += p[jj] * dp[jj];
+            for (int jj = 0; jj < n; ++jj) dp[jj] = p[jj] * (dp[jj] - pdp);
+            /* s_j = scale q . k_j and t_j = rho . k_j */
+            int64_t qo = (((int64_t)b * T->n_rows + ri) * T->Hq + h) * dk;
+            for (int e = 0; e < dk; ++e) T->dq[qo + e] = T->drho[qo + e] = 0.0;
+            for (int jj = 0; jj < n; ++jj) {
+                int j = j0 + jj;
+                double *dko = T->dkk + (((int64_t)b * T->S + j) * T->Hkv + hk) * dk;
+                for (int e = 0; e < dk; ++e) {
+                    double kje = orc_k(T, b, j, hk, e);
+                    T->dq[qo + e] += T->scale * dp[jj] * kje;
+                    T->drho[qo + e] += dt[jj] * kje;
+                    dko[e] += T->scale * dp[jj] * qd[e] + dt[jj] * rd[e];
+                }
+            }
+        }
+    }
+}
+
+static int orc_train_check(int B, int S, int Hq, int Hkv, int dk, int dv, int window,
+                           const int32_t *rows, int n_rows) {
+    if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || dk < 1 || dv < 1 || window < 0 ||
+        n_rows < 1 || rows == NULL)
+        return -1;
+    for (int r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= S) return -1;
+    return 0;
+}
+
+/*
+ * Forward statistics of causal prefill rows (what a forward pass keeps for
+ * the backward pass):
+ *   lse   [B, n_rows, Hq]      natural log of sum_j exp(scale q.k_j)
+ *   rmean [B, n_rows, Hq]      r = sum_j p_j (rho . k_j)
+ *   osa   [B, n_rows, Hq, dv]  a = o_SA = sum_j p_j v_j
+ * Shapes as orc_prefill.
+ */
+int orc_prefill_stats(int B, int S, int Hq, int Hkv, int dk, int dv, double scale,
+                      const void *q, int q_dtype, const void *rho, int rho_dtype,
+                      const void *k, const void *v, int kv_dtype,
+                      const int32_t *rows, int n_rows, int window,
+                      double *lse, double *rmean, double *osa, int nthreads) {
+    if (orc_train_check(B, S, Hq, Hkv, dk, dv, window, rows, n_rows) != 0) return -1;
+    orc_train T;
+    memset(&T, 0, sizeof T);
+    T.B = B; T.S = S; T.Hq = Hq; T.Hkv = Hkv; T.dk = dk; T.dv = dv; T.window = window;
+    T.scale = scale;
+    T.q = q; T.rho = rho; T.k = k; T.v = v;
+    T.q_dtype = q_dtype; T.rho_dtype = rho_dtype; T.kv_dtype = kv_dtype;
+    T.rows = rows; T.n_rows = n_rows;
+    T.lse = lse; T.rmean = rmean; T.osa = osa;
+    return orc_parallel(&T, orc_stats_unit, (int64_t)B * n_rows * Hq,
+                        (size_t)2 * dk + (size_t)2 * S, nthreads);
+}
+
+/*
+ * Gradients of sum(dout * out) for causal prefill, out as orc_prefill.
+ *   dout       [B, S, Hq, dv]
+ *   rows       the query rows whose terms are included; dq, drho are given
+ *              for them, and dk, dv sum the contributions of these rows only
+ *              (so they are exact for key j when every row that sees key j
+ *              is in rows; all rows 0..S-1 give the full gradients)
+ *   dq, drho   [B, n_rows, Hq, dk]
+ *   dk         [B, S, Hkv, dk];  dv [B, S, Hkv, dv]  (zeroed here)
+ */
+int orc_prefill_backward(int B, int S, int Hq, int Hkv, int dk, int dv, double scale,
+                         const void *q, int q_dtype, const void *rho, int rho_dtype,
+                         const void *k, const void *v, int kv_dtype,
+                         const void *dout, int dout_dtype,
+                         const int32_t *rows, int n_rows, int window,
+                         double *dq, double *drho, double *dkk, double *dvv, int nthreads) {
+    if (orc_train_check(B, S, Hq, Hkv, dk, dv, window, rows, n_rows) != 0) return -1;
+    orc_train T;
+    memset(&T, 0, sizeof T);
+    T.B = B; T.S = S; T.Hq = Hq; T.Hkv = Hkv; T.dk = dk; T.dv = dv; T.window = window;
+    T.scale = scale;
+    T.q = q; T.rho = rho; T.k = k; T.v = v; T.dout = dout;
+    T.q_dtype = q_dtype; T.rho_dtype = rho_dtype; T.kv_dtype = kv_dtype; T.dout_dtype = dout_dtype;
+    T.rows = rows; T.n_rows = n_rows;
+    T.dq = dq; T.drho = drho; T.dkk = dkk; T.dvv = dvv;
+    memset(dkk, 0, sizeof(double) * (size_t)B * S * Hkv * dk);
+    memset(dvv, 0, sizeof(double) * (size_t)B * S * Hkv * dv);
+    return orc_parallel(&T, orc_backward_unit, (int64_t)B * Hkv,
+                        (size_t)2 * dk + (size_t)4 * S + (size_t)5 * dv, nthreads);
 }
