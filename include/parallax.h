@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 2
+#define PARALLAX_ABI_VERSION 3
 
 typedef enum {
     PARALLAX_OK = 0,
@@ -172,9 +172,86 @@ typedef struct {
     int64_t out_stride_b, out_stride_s, out_stride_h;
     int32_t window; /* 0 = keys 0..i; W >= 1 = keys max(0, i-W+1)..i; < 0 is
                        PARALLAX_ERR_INVALID_ARG (added in ABI version 2) */
+
+    /* Optional outputs for a backward pass (added in ABI version 3); each may
+     * be NULL, and is written when not.  With p_ij the softmax weights of
+     * row i:
+     *   lse   fp32 [B, Hq, S], contiguous: log of sum_j exp(scale q_i.k_j)
+     *         over the row's keys (natural log);
+     *   rmean fp32 [B, Hq, S], contiguous: r_i = sum_j p_ij (rho_i . k_j);
+     *   o_sa  fp32, the shape and strides of out: the softmax output
+     *         a_i = sum_j p_ij v_j.
+     * 16-byte aligned. */
+    float *lse;
+    float *rmean;
+    float *o_sa;
 } parallax_prefill_args_t;
 
 parallax_status_t parallax_prefill(const parallax_prefill_args_t *args, void *hip_stream);
+
+/* ---------------------------------------------------- prefill backward --- */
+/*
+ * Gradients of a causal prefill (same keys per row as parallax_prefill,
+ * window included) for the loss sum(dout * out): dq, drho [B, S, Hq, d] and
+ * dk, dv [B, S, Hkv, d], fp32, OVERWRITTEN (not accumulated).  Training the
+ * layer end to end is how the page "Parallax: Parameterized Local Linear
+ * Attention Gives Transformers a 'Second Eye'" (section 2.2) uses it; the
+ * derivation follows the forward formula above by the chain rule:
+ * with g = dout_i, c = a_i . g, u_j = g . v_j and D = g . o_i + r_i c,
+ *     dv_j += p_ij (1 + r_i - t_ij) g
+ *     ds_ij = p_ij (u_j (1 + r_i - t_ij) + c t_ij - D),  dt_ij = p_ij (c - u_j)
+ *     dq_i  = scale sum_j ds_ij k_j,   drho_i = sum_j dt_ij k_j,
+ *     dk_j += scale ds_ij q_i + dt_ij rho_i   (summed over rows and the GQA group)
+ * Inputs: q, rho, k, v as the forward (bf16); dout bf16 [B, S, Hq, d]; out,
+ * o_sa fp32 (the forward's output and its o_sa, sharing out's strides); lse
+ * and rmean fp32 [B, Hq, S] contiguous (the forward's optional outputs).  The
+ * products run on the bf16 matrix cores with fp32 accumulation; the weights
+ * (1 + r - t) p, ds and dt are rounded to bf16 before they meet dout, q, rho
+ * and k.  Deterministic: no atomics, fixed summation order.
+ * Supported: causal = 1, head_dim 128, GQA group 1, 2 or 4 (else
+ * PARALLAX_ERR_UNSUPPORTED).  Workspace: parallax_prefill_backward_workspace_size
+ * bytes (16 per query row), 16-byte aligned, owned by the caller; its
+ * contents on entry do not matter.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(parallax_prefill_backward_args_t) */
+    int32_t batch;
+    int32_t seq_len;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    float scale;
+    int32_t causal;
+    int32_t window; /* as parallax_prefill_args_t */
+
+    const void *q;
+    int64_t q_stride_b, q_stride_s, q_stride_h;
+    const void *rho;
+    int64_t rho_stride_b, rho_stride_s, rho_stride_h;
+    const void *k;
+    int64_t k_stride_b, k_stride_s, k_stride_h;
+    const void *v;
+    int64_t v_stride_b, v_stride_s, v_stride_h;
+    const void *dout;
+    int64_t dout_stride_b, dout_stride_s, dout_stride_h;
+    const float *out;  /* forward output */
+    const float *o_sa; /* forward o_sa, out's strides */
+    int64_t out_stride_b, out_stride_s, out_stride_h;
+    const float *lse;   /* [B, Hq, S] */
+    const float *rmean; /* [B, Hq, S] */
+    float *dq;
+    float *drho; /* dq's strides */
+    int64_t dq_stride_b, dq_stride_s, dq_stride_h;
+    float *dk;
+    float *dv; /* dk's strides */
+    int64_t dk_stride_b, dk_stride_s, dk_stride_h;
+} parallax_prefill_backward_args_t;
+
+parallax_status_t parallax_prefill_backward_workspace_size(
+    const parallax_prefill_backward_args_t *args, size_t *bytes);
+parallax_status_t parallax_prefill_backward(const parallax_prefill_backward_args_t *args,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *hip_stream);
 
 /* ------------------------------------------------------------- misc --- */
 const char *parallax_status_string(parallax_status_t status);

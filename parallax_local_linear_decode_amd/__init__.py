@@ -30,7 +30,7 @@ PARALLAX_ERR_WORKSPACE = 3
 PARALLAX_ERR_HIP = 4
 PARALLAX_F32 = 0
 PARALLAX_BF16 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _i32, _i64, _u32, _f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float,
                                ctypes.c_void_p)
@@ -65,6 +65,28 @@ class PrefillArgs(ctypes.Structure):
         ("v", _vp), ("v_stride_b", _i64), ("v_stride_s", _i64), ("v_stride_h", _i64),
         ("out", _vp), ("out_stride_b", _i64), ("out_stride_s", _i64), ("out_stride_h", _i64),
         ("window", _i32),
+        ("lse", _vp), ("rmean", _vp), ("o_sa", _vp),
+    ]
+
+
+class PrefillBackwardArgs(ctypes.Structure):
+    """Mirror of parallax_prefill_backward_args_t."""
+    _fields_ = [
+        ("struct_size", _u32), ("batch", _i32), ("seq_len", _i32), ("num_q_heads", _i32),
+        ("num_kv_heads", _i32), ("head_dim", _i32), ("scale", _f32), ("causal", _i32),
+        ("window", _i32),
+        ("q", _vp), ("q_stride_b", _i64), ("q_stride_s", _i64), ("q_stride_h", _i64),
+        ("rho", _vp), ("rho_stride_b", _i64), ("rho_stride_s", _i64), ("rho_stride_h", _i64),
+        ("k", _vp), ("k_stride_b", _i64), ("k_stride_s", _i64), ("k_stride_h", _i64),
+        ("v", _vp), ("v_stride_b", _i64), ("v_stride_s", _i64), ("v_stride_h", _i64),
+        ("dout", _vp), ("dout_stride_b", _i64), ("dout_stride_s", _i64), ("dout_stride_h", _i64),
+        ("out", _vp), ("o_sa", _vp),
+        ("out_stride_b", _i64), ("out_stride_s", _i64), ("out_stride_h", _i64),
+        ("lse", _vp), ("rmean", _vp),
+        ("dq", _vp), ("drho", _vp), ("dq_stride_b", _i64), ("dq_stride_s", _i64),
+        ("dq_stride_h", _i64),
+        ("dk", _vp), ("dv", _vp), ("dk_stride_b", _i64), ("dk_stride_s", _i64),
+        ("dk_stride_h", _i64),
     ]
 
 
@@ -91,6 +113,12 @@ def load_library():
     lib.parallax_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
     lib.parallax_prefill.restype = ctypes.c_int
     lib.parallax_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
+    lib.parallax_prefill_backward_workspace_size.restype = ctypes.c_int
+    lib.parallax_prefill_backward_workspace_size.argtypes = [
+        ctypes.POINTER(PrefillBackwardArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.parallax_prefill_backward.restype = ctypes.c_int
+    lib.parallax_prefill_backward.argtypes = [ctypes.POINTER(PrefillBackwardArgs), _vp,
+                                              ctypes.c_size_t, _vp]
     if lib.parallax_abi_version() != ABI_VERSION:
         raise RuntimeError("libparallax ABI version mismatch")
     _lib = lib
@@ -240,10 +268,12 @@ def parallax_decode(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None
 
 
 def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, window=0,
-                     stream=None):
+                     stream=None, return_stats=False):
     """Causal Parallax prefill.  q, rho bf16 [B, S, Hq, d]; k, v bf16
     [B, S, Hkv, d].  window: 0 for keys 0..i, W >= 1 for keys i-W+1..i.
-    Returns out float32 [B, S, Hq, d]."""
+    Returns out float32 [B, S, Hq, d]; with return_stats, (out, lse, rmean,
+    o_sa): what parallax_prefill_backward needs (lse, rmean float32
+    [B, Hq, S]; o_sa float32 like out)."""
     lib = load_library()
     for name, t in (("q", q), ("rho", rho), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(-1) != 1:
@@ -264,14 +294,90 @@ def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, window=
     a.v, a.v_stride_b, a.v_stride_s, a.v_stride_h = _ptr(v), *v.stride()[:3]
     a.out, a.out_stride_b, a.out_stride_s, a.out_stride_h = _ptr(out), *out.stride()[:3]
     a.window = int(window)
+    if return_stats:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+        rmean = torch.empty_like(lse)
+        o_sa = torch.empty_like(out)
+        a.lse, a.rmean, a.o_sa = _ptr(lse), _ptr(rmean), _ptr(o_sa)
     st = lib.parallax_prefill(ctypes.byref(a), _stream_handle(q, stream))
     if st != PARALLAX_OK:
         _raise(st, lib)
-    return out
+    return (out, lse, rmean, o_sa) if return_stats else out
+
+
+def _backward_args(q, rho, k, v, dout, out, o_sa, lse, rmean, dq, drho, dk, dv, scale, causal,
+                   window):
+    a = PrefillBackwardArgs()
+    a.struct_size = ctypes.sizeof(PrefillBackwardArgs)
+    B, S, Hq, d = q.shape
+    a.batch, a.seq_len, a.num_q_heads, a.num_kv_heads, a.head_dim = B, S, Hq, k.shape[2], d
+    a.scale = float(scale if scale is not None else 1.0 / math.sqrt(d))
+    a.causal = 1 if causal else 0
+    a.window = int(window)
+    a.q, a.q_stride_b, a.q_stride_s, a.q_stride_h = _ptr(q), *q.stride()[:3]
+    a.rho, a.rho_stride_b, a.rho_stride_s, a.rho_stride_h = _ptr(rho), *rho.stride()[:3]
+    a.k, a.k_stride_b, a.k_stride_s, a.k_stride_h = _ptr(k), *k.stride()[:3]
+    a.v, a.v_stride_b, a.v_stride_s, a.v_stride_h = _ptr(v), *v.stride()[:3]
+    a.dout, a.dout_stride_b, a.dout_stride_s, a.dout_stride_h = _ptr(dout), *dout.stride()[:3]
+    a.out, a.o_sa = _ptr(out), _ptr(o_sa)
+    a.out_stride_b, a.out_stride_s, a.out_stride_h = out.stride()[:3]
+    a.lse, a.rmean = _ptr(lse), _ptr(rmean)
+    a.dq, a.drho = _ptr(dq), _ptr(drho)
+    a.dq_stride_b, a.dq_stride_s, a.dq_stride_h = dq.stride()[:3]
+    a.dk, a.dv = _ptr(dk), _ptr(dv)
+    a.dk_stride_b, a.dk_stride_s, a.dk_stride_h = dk.stride()[:3]
+    return a
+
+
+def parallax_prefill_backward(q, rho, k, v, dout, out, o_sa, lse, rmean, *, scale=None,
+                              causal=True, window=0, dq=None, drho=None, dk=None, dv=None,
+                              workspace=None, stream=None):
+    """Gradients of sum(dout * out) of a causal Parallax prefill.
+
+    q, rho, k, v as parallax_prefill; dout bf16 [B, S, Hq, d]; out, o_sa,
+    lse, rmean from ``parallax_prefill(..., return_stats=True)``.  Returns
+    (dq, drho, dk, dv), float32, dq/drho [B, S, Hq, d] and dk/dv
+    [B, S, Hkv, d] (allocated when not given; overwritten when given).
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("rho", rho), ("k", k), ("v", v), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a 4-d bfloat16 tensor with contiguous head dim")
+    B, S, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if o_sa.stride() != out.stride():
+        raise ValueError("o_sa must share out's strides")
+    for name, t, shape in (("out", out, (B, S, Hq, d)), ("o_sa", o_sa, (B, S, Hq, d)),
+                           ("lse", lse, (B, Hq, S)), ("rmean", rmean, (B, Hq, S))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be float32 of shape {shape}")
+    if not (lse.is_contiguous() and rmean.is_contiguous()):
+        raise ValueError("lse and rmean must be contiguous")
+    dq = torch.empty((B, S, Hq, d), dtype=torch.float32, device=q.device) if dq is None else dq
+    drho = torch.empty_like(dq) if drho is None else drho
+    dk = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty_like(dk) if dv is None else dv
+    if drho.stride() != dq.stride() or dv.stride() != dk.stride():
+        raise ValueError("drho must share dq's strides and dv dk's")
+    a = _backward_args(q, rho, k, v, dout, out, o_sa, lse, rmean, dq, drho, dk, dv, scale,
+                       causal, window)
+    need = ctypes.c_size_t(0)
+    st = lib.parallax_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(need))
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 16), dtype=torch.uint8, device=q.device)
+    st = lib.parallax_prefill_backward(ctypes.byref(a), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream_handle(q, stream))
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    return dq, drho, dk, dv
 
 
 __all__ = [
     "parallax_decode", "parallax_decode_workspace_size", "parallax_prefill",
+    "parallax_prefill_backward", "PrefillBackwardArgs",
     "parallax_status_string", "parallax_last_error", "parallax_abi_version", "load_library",
     "DecodeArgs", "PrefillArgs", "ParallaxError",
 ]

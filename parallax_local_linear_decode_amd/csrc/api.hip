@@ -171,7 +171,71 @@ parallax_status_t check_prefill(const parallax_prefill_args_t *a) {
     for (int i = 12; i < 15; ++i)
         if (!bytes16(strides[i], 4))
             return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: strides must span multiples of 16 bytes");
+    if (!aligned16(a->lse) || !aligned16(a->rmean) || !aligned16(a->o_sa))
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: lse, rmean and o_sa must be 16-byte aligned");
     return PARALLAX_OK;
+}
+
+parallax_status_t check_prefill_backward(const parallax_prefill_backward_args_t *a) {
+    if (a == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "prefill backward: args is NULL");
+    if (a->struct_size != sizeof(parallax_prefill_backward_args_t))
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill backward: struct_size %u, expected %zu",
+                    a->struct_size, sizeof(parallax_prefill_backward_args_t));
+    if (a->batch < 1 || a->seq_len < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+        return fail(PARALLAX_ERR_INVALID_ARG,
+                    "prefill backward: batch, seq_len and head counts must be >= 1");
+    if (a->num_q_heads % a->num_kv_heads != 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill backward: num_q_heads %% num_kv_heads != 0");
+    if (!isfinite(a->scale))
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill backward: scale is not finite");
+    if (!a->q || !a->rho || !a->k || !a->v || !a->dout || !a->out || !a->o_sa || !a->lse ||
+        !a->rmean || !a->dq || !a->drho || !a->dk || !a->dv)
+        return fail(PARALLAX_ERR_INVALID_ARG,
+                    "prefill backward: every tensor pointer must be non-NULL");
+    const int64_t strides[] = {a->q_stride_b,    a->q_stride_s,    a->q_stride_h,
+                               a->rho_stride_b,  a->rho_stride_s,  a->rho_stride_h,
+                               a->k_stride_b,    a->k_stride_s,    a->k_stride_h,
+                               a->v_stride_b,    a->v_stride_s,    a->v_stride_h,
+                               a->dout_stride_b, a->dout_stride_s, a->dout_stride_h,
+                               a->out_stride_b,  a->out_stride_s,  a->out_stride_h,
+                               a->dq_stride_b,   a->dq_stride_s,   a->dq_stride_h,
+                               a->dk_stride_b,   a->dk_stride_s,   a->dk_stride_h};
+    for (int64_t s : strides)
+        if (s < 0)
+            return fail(PARALLAX_ERR_INVALID_ARG, "prefill backward: strides must be non-negative");
+    if (a->causal != 1)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill backward: only causal = 1 is supported");
+    if (a->window < 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill backward: window must be >= 0");
+    if (a->head_dim != 128)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill backward: head_dim %d (supported: 128)",
+                    a->head_dim);
+    const int group = a->num_q_heads / a->num_kv_heads;
+    if (group != 1 && group != 2 && group != 4)
+        return fail(PARALLAX_ERR_UNSUPPORTED,
+                    "prefill backward: GQA group %d (supported: 1, 2, 4)", group);
+    if ((int64_t)a->batch * a->num_kv_heads * ((a->seq_len + 31) / 32) > 0x7fffffffLL ||
+        (int64_t)a->batch * a->num_q_heads * a->seq_len > 0x7fffffffLL * 16LL)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill backward: grid too large");
+    const void *ptrs[] = {a->q,   a->rho, a->k,     a->v,  a->dout, a->out, a->o_sa,
+                          a->lse, a->rmean, a->dq, a->drho, a->dk, a->dv};
+    for (const void *ptr : ptrs)
+        if (!aligned16(ptr))
+            return fail(PARALLAX_ERR_UNSUPPORTED,
+                        "prefill backward: every pointer must be 16-byte aligned");
+    for (int i = 0; i < 15; ++i)
+        if (!bytes16(strides[i], 2))
+            return fail(PARALLAX_ERR_UNSUPPORTED,
+                        "prefill backward: strides must span multiples of 16 bytes");
+    for (int i = 15; i < 24; ++i)
+        if (!bytes16(strides[i], 4))
+            return fail(PARALLAX_ERR_UNSUPPORTED,
+                        "prefill backward: strides must span multiples of 16 bytes");
+    return PARALLAX_OK;
+}
+
+size_t prefill_backward_workspace(const parallax_prefill_backward_args_t *a) {
+    return (size_t)a->batch * a->num_q_heads * a->seq_len * 16;  // one float4 per query row
 }
 
 parallax_status_t hip_status(hipError_t e, const char *what) {
@@ -281,6 +345,81 @@ PLX_EXPORT parallax_status_t parallax_prefill(const parallax_prefill_args_t *a, 
     p.num_kv_heads = a->num_kv_heads;
     p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
     p.window = a->window;
+    p.lse = a->lse;
+    p.rmean = a->rmean;
+    p.o_sa = a->o_sa;
     return hip_status(plx::launch_prefill(p, a->head_dim, static_cast<hipStream_t>(hip_stream)),
                       "prefill launch");
+}
+
+PLX_EXPORT parallax_status_t parallax_prefill_backward_workspace_size(
+    const parallax_prefill_backward_args_t *args, size_t *bytes) {
+    if (bytes == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "prefill backward: bytes is NULL");
+    parallax_status_t s = check_prefill_backward(args);
+    if (s != PARALLAX_OK) return s;
+    *bytes = prefill_backward_workspace(args);
+    return PARALLAX_OK;
+}
+
+PLX_EXPORT parallax_status_t parallax_prefill_backward(const parallax_prefill_backward_args_t *a,
+                                                       void *workspace, size_t workspace_bytes,
+                                                       void *hip_stream) {
+    parallax_status_t s = check_prefill_backward(a);
+    if (s != PARALLAX_OK) return s;
+    const size_t need = prefill_backward_workspace(a);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(PARALLAX_ERR_WORKSPACE,
+                    "prefill backward: workspace of %zu bytes needed, %zu given", need,
+                    workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(PARALLAX_ERR_WORKSPACE, "prefill backward: workspace must be 16-byte aligned");
+    plx::PrefillBwdParams p;
+    p.q = static_cast<const uint16_t *>(a->q);
+    p.rho = static_cast<const uint16_t *>(a->rho);
+    p.k = static_cast<const uint16_t *>(a->k);
+    p.v = static_cast<const uint16_t *>(a->v);
+    p.dout = static_cast<const uint16_t *>(a->dout);
+    p.out = a->out;
+    p.o_sa = a->o_sa;
+    p.lse = a->lse;
+    p.rmean = a->rmean;
+    p.dq = a->dq;
+    p.drho = a->drho;
+    p.dk = a->dk;
+    p.dv = a->dv;
+    p.rowstat = static_cast<float4 *>(workspace);
+    p.q_sb = a->q_stride_b;
+    p.q_ss = a->q_stride_s;
+    p.q_sh = a->q_stride_h;
+    p.r_sb = a->rho_stride_b;
+    p.r_ss = a->rho_stride_s;
+    p.r_sh = a->rho_stride_h;
+    p.k_sb = a->k_stride_b;
+    p.k_ss = a->k_stride_s;
+    p.k_sh = a->k_stride_h;
+    p.v_sb = a->v_stride_b;
+    p.v_ss = a->v_stride_s;
+    p.v_sh = a->v_stride_h;
+    p.g_sb = a->dout_stride_b;
+    p.g_ss = a->dout_stride_s;
+    p.g_sh = a->dout_stride_h;
+    p.o_sb = a->out_stride_b;
+    p.o_ss = a->out_stride_s;
+    p.o_sh = a->out_stride_h;
+    p.dq_sb = a->dq_stride_b;
+    p.dq_ss = a->dq_stride_s;
+    p.dq_sh = a->dq_stride_h;
+    p.dk_sb = a->dk_stride_b;
+    p.dk_ss = a->dk_stride_s;
+    p.dk_sh = a->dk_stride_h;
+    p.batch = a->batch;
+    p.seq_len = a->seq_len;
+    p.num_q_heads = a->num_q_heads;
+    p.num_kv_heads = a->num_kv_heads;
+    p.scale = a->scale;
+    p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
+    p.window = a->window;
+    return hip_status(
+        plx::launch_prefill_backward(p, a->head_dim, static_cast<hipStream_t>(hip_stream)),
+        "prefill backward launch");
 }

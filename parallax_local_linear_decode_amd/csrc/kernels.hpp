@@ -1,5 +1,5 @@
 // Internal launch parameters shared by the host dispatcher (api.hip) and the
-// gfx950 kernels (decode.hip, prefill.hip).  Not part of the public ABI.
+// gfx950 kernels (decode.hip, prefill.hip, prefill_bwd.hip).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -50,6 +50,43 @@ struct PrefillParams {
     int32_t batch, seq_len, num_q_heads, num_kv_heads;
     float scale_log2;
     int32_t window;  // 0: keys 0..i; W >= 1: keys max(0, i-W+1)..i
+    // optional outputs for a backward pass (each may be null): natural-log
+    // softmax denominator and r per row, [B, Hq, S]; o_SA with out's strides
+    float *lse;
+    float *rmean;
+    float *o_sa;
+};
+
+// Causal prefill backward.  rowstat is the workspace: one float4 per row
+// (b, h, i) at ((b * Hq + h) * S + i), holding (lse * log2 e, r, c, D) with
+// c = o_SA . dout and D = dout . out + r c.
+struct PrefillBwdParams {
+    const uint16_t *q;
+    const uint16_t *rho;
+    const uint16_t *k;
+    const uint16_t *v;
+    const uint16_t *dout;
+    const float *out;
+    const float *o_sa;
+    const float *lse;
+    const float *rmean;
+    float *dq;
+    float *drho;
+    float *dk;
+    float *dv;
+    float4 *rowstat;
+    int64_t q_sb, q_ss, q_sh;
+    int64_t r_sb, r_ss, r_sh;
+    int64_t k_sb, k_ss, k_sh;
+    int64_t v_sb, v_ss, v_sh;
+    int64_t g_sb, g_ss, g_sh;    // dout
+    int64_t o_sb, o_ss, o_sh;    // out and o_sa
+    int64_t dq_sb, dq_ss, dq_sh; // dq and drho
+    int64_t dk_sb, dk_ss, dk_sh; // dk and dv
+    int32_t batch, seq_len, num_q_heads, num_kv_heads;
+    float scale;       // natural logit scale
+    float scale_log2;  // scale * log2(e)
+    int32_t window;
 };
 
 // Launchers (defined next to their kernels).  They return the HIP status of
@@ -57,5 +94,6 @@ struct PrefillParams {
 hipError_t launch_decode(const DecodeParams &p, int kv_dtype, int d, int group, bool paged,
                          int batch, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream);
+hipError_t launch_prefill_backward(const PrefillBwdParams &p, int d, hipStream_t stream);
 
 }  // namespace plx

@@ -87,6 +87,7 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
     __shared__ __attribute__((aligned(16))) unsigned char vtile[2][TILE];
     __shared__ uint4 pbuf[2][kPfPairs][4][64];     // P operands, in value-MFMA lane layout
     __shared__ float abuf[2][kPfPairs][2][16];      // per-row rescale factors
+    __shared__ float mfin[kPfPairs][2][16];         // final reference max per row
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -288,6 +289,11 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
             score_step(t + 1);
             advance(t + 1, std::integral_constant<int, 1>{});
         }
+        if (p.lse != nullptr) {  // the value wave turns its Z into log(sum e^s)
+            mfin[pair][0][c] = mref[0];
+            mfin[pair][1][c] = mref[1];
+            __syncthreads();
+        }
     } else {
         // Value sums: acc[db][cb] = D2 rows d = 16db + 4g + j, column c of block
         // cb (E rows 0-15, 16-31, E*T rows 0-15, 16-31).  Block db = DB
@@ -347,6 +353,8 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
             advance(t + 1, std::integral_constant<int, 1>{});
         }
 
+        if (p.lse != nullptr) __syncthreads();  // mfin written by the score waves
+
         // ---- o = a - (b - a r) per query row; lane (c, g) holds d = 16db + 4g + j
 #pragma unroll
         for (int qc = 0; qc < 2; ++qc) {
@@ -354,8 +362,8 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
             if (qi >= S) continue;
             const float inv = 1.0f / acc[DB][qc][0];
             const float r = acc[DB][qc + 2][0] * inv;
-            float *orow =
-                p.out + (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)head * p.o_sh;
+            const int64_t ooff = (int64_t)b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)head * p.o_sh;
+            float *orow = p.out + ooff;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 float o[4];
@@ -366,6 +374,20 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
                 }
                 *reinterpret_cast<float4 *>(orow + 16 * db + 4 * g) =
                     float4{o[0], o[1], o[2], o[3]};
+            }
+            // what a backward pass needs: log of the softmax denominator
+            // (natural log; Z is kept relative to 2^m), r and o_SA
+            const int64_t ri = ((int64_t)b * p.num_q_heads + head) * S + qi;
+            if (p.lse != nullptr && g == 0)
+                p.lse[ri] = (mfin[pair][qc][c] + __builtin_log2f(acc[DB][qc][0])) *
+                            0.6931471805599453f;
+            if (p.rmean != nullptr && g == 0) p.rmean[ri] = r;
+            if (p.o_sa != nullptr) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    *reinterpret_cast<float4 *>(p.o_sa + ooff + 16 * db + 4 * g) =
+                        float4{acc[db][qc][0] * inv, acc[db][qc][1] * inv, acc[db][qc][2] * inv,
+                               acc[db][qc][3] * inv};
             }
         }
     }

@@ -1,0 +1,666 @@
+// prefill_bwd.hip -- backward pass of causal Parallax prefill for gfx950
+// (CDNA4), bf16 matrix cores.
+//
+// Forward, per query row i (page "Parallax: Parameterized Local Linear
+// Attention Gives Transformers a 'Second Eye'", section 1.3):
+//   s_j = scale q.k_j, p = softmax(s), t_j = rho.k_j,
+//   a = sum p_j v_j, r = sum p_j t_j, b = sum p_j t_j v_j, o = a - b + a r.
+// With g = dL/do, c = a.g and u_j = g.v_j the chain rule gives
+//   dL/dv_j += p_j (1 + r - t_j) g
+//   dL/dp_j  = u_j (1 + r - t_j) + c t_j,   sum_j p_j dL/dp_j = g.o + r c =: D
+//   dL/ds_j  = p_j (dL/dp_j - D)            (softmax)
+//   dL/dt_j  = p_j (c - u_j)
+//   dq = scale sum_j ds_j k_j,  drho = sum_j dt_j k_j,
+//   dk_j += scale ds_j q + dt_j rho          (summed over rows and GQA heads)
+// The forward pass keeps, per row, lse = log sum_j e^{s_j}, r and a; then
+// p_j = e^{s_j - lse} is recomputed exactly, with no running max.
+//
+// Three kernels, all deterministic (fixed summation order, no atomics):
+//   prep  one 16-lane group per row: c = a.g and D = g.o + r c, stored with
+//         lse * log2(e) and r as one float4 per row (the workspace);
+//   dq    query-major, the forward's structure: a workgroup holds 128 query
+//         rows of the G heads of one KV head, 32-key K/V tiles stream through
+//         LDS.  Score wave p recomputes S^T = K Q^T, T^T = K rho^T and
+//         U^T = V dout^T (keys x queries) and forms dS^T, dT^T in bf16; value
+//         wave p + 4 accumulates dq^T += K^T dS^T and drho^T += K^T dT^T (K^T
+//         through ds_read_b64_tr_b16), one tile behind.
+//   dkv   key-major, the same pair structure with roles swapped: a workgroup
+//         holds 128 keys of one KV head (32 per pair, K and V resident in the
+//         score wave), and 32-row tiles of q, rho and dout of every query head
+//         of the group stream through LDS.  Score wave: S = Q K^T, T = rho K^T,
+//         U = dout V^T (queries x keys), then W = p (1 + r - t), scale dS and
+//         dT in bf16; value wave: dv^T += dout^T W, dk^T += q^T dS + rho^T dT.
+// Tiles read by both roles live two epochs (score wave in epoch t, value
+// wave in epoch t + 1), so they are triple-buffered in LDS; each epoch ends
+// with one barrier, and global loads run two tiles ahead through two register
+// stages, issued unconditionally so the compiler's wait counts stay exact.
+#include "kernels.hpp"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace plx {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBwPairs = 4;                 // score/value wave pairs per workgroup
+constexpr int kBwRows = 32;                 // query rows (dq) or keys (dkv) per pair
+constexpr int kBwTile = 32;                 // rows of a streamed tile
+constexpr int kBwD = 128;                   // head dim
+constexpr int kBwRowBytes = 2 * kBwD + 16;  // LDS bytes per tile row (16-byte pad)
+constexpr int kBwTileBytes = kBwTile * kBwRowBytes;
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+    return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// Byte offset of triple-buffer slot t % 3.  Passed through readfirstlane so
+// the loop optimizer treats it as an opaque value: otherwise it turns every
+// LDS address derived from it into an induction variable of its own, which
+// costs dozens of registers.
+__device__ __forceinline__ int slot3(int t) {
+    return __builtin_amdgcn_readfirstlane((t % 3) * kBwTileBytes);
+}
+
+__device__ __forceinline__ f32x4_t mfma(const bf16x8_t &a, const bf16x8_t &b, const f32x4_t &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A operand of a 16x16x32 MFMA holding the transpose of a 32-row LDS tile:
+// row 16db + (lane % 16) of the result is head-dim column 16db + lane % 16
+// of the tile, k-slot r is tile row 4g + r (r < 4) or 16 + 4g + r - 4.
+__device__ __forceinline__ bf16x8_t tr_operand(const unsigned char *tile, int db, int c, int g) {
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    const int col = 16 * db + 4 * (c % 4);
+    const unsigned char *a0 = tile + (4 * g + c / 4) * kBwRowBytes + 2 * col;
+    const unsigned char *a1 = tile + (16 + 4 * g + c / 4) * kBwRowBytes + 2 * col;
+    const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a0);
+    const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a1);
+    return __builtin_bit_cast(
+        bf16x8_t, i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]});
+}
+
+// ------------------------------------------------------------------ prep ---
+__global__ __launch_bounds__(256) void bwd_prep_kernel(PrefillBwdParams p) {
+    const int64_t rows = (int64_t)p.batch * p.num_q_heads * p.seq_len;
+    const int64_t u = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+    const int part = threadIdx.x % 16;
+    const int64_t uu = u < rows ? u : rows - 1;
+    const int i = (int)(uu % p.seq_len);
+    const int h = (int)((uu / p.seq_len) % p.num_q_heads);
+    const int b = (int)(uu / ((int64_t)p.seq_len * p.num_q_heads));
+    const uint4 gw = ld16(p.dout + (int64_t)b * p.g_sb + (int64_t)i * p.g_ss + (int64_t)h * p.g_sh +
+                          8 * part);
+    const int64_t ooff = (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh + 8 * part;
+    const float4 o0 = *reinterpret_cast<const float4 *>(p.out + ooff);
+    const float4 o1 = *reinterpret_cast<const float4 *>(p.out + ooff + 4);
+    const float4 a0 = *reinterpret_cast<const float4 *>(p.o_sa + ooff);
+    const float4 a1 = *reinterpret_cast<const float4 *>(p.o_sa + ooff + 4);
+    const float gv[8] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y),
+                         bf16_lo(gw.z), bf16_hi(gw.z), bf16_lo(gw.w), bf16_hi(gw.w)};
+    const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    float ca = 0.f, go = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        ca = fmaf(av[e], gv[e], ca);
+        go = fmaf(ov[e], gv[e], go);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) {
+        ca += __shfl_xor(ca, m, 16);
+        go += __shfl_xor(go, m, 16);
+    }
+    if (u < rows && part == 0) {
+        const float r = p.rmean[uu];
+        p.rowstat[uu] = float4{p.lse[uu] * 1.4426950408889634f, r, ca, fmaf(r, ca, go)};
+    }
+}
+
+// -------------------------------------------------------------------- dq ---
+template <int G, bool WIN>
+__global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams p) {
+    constexpr int KS = kBwD / 32;          // score MFMAs per 16-key block
+    constexpr int DB = kBwD / 16;          // 16-row blocks of the gradient sums
+    constexpr int PPH = kBwPairs / G;      // pairs per query head
+    constexpr int QB = kBwRows * PPH;      // query rows per head per workgroup
+
+    __shared__ __attribute__((aligned(16))) unsigned char ktile[3 * kBwTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char vtile[2][kBwTileBytes];
+    __shared__ uint4 pbuf[2][kBwPairs][4][64];  // dS^T (qc 0, 1), dT^T (qc 0, 1), B-operand layout
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int S = p.seq_len;
+    const float c2 = p.scale_log2;
+    const bool score_wave = wave < kBwPairs;
+    const int pair = wave % kBwPairs;
+
+    const int units = p.batch * p.num_kv_heads;
+    const int nqb = (S + QB - 1) / QB;
+    const int qb = nqb - 1 - (int)(blockIdx.x / units);  // longest causal rows first
+    const int unit = blockIdx.x % units;
+    const int b = unit / p.num_kv_heads;
+    const int hk = unit % p.num_kv_heads;
+    const int head = hk * G + pair / PPH;
+    const int r0 = qb * QB + (pair % PPH) * kBwRows;  // first query row of this pair
+    const int key_end = min(S, (qb + 1) * QB);
+    const int ntiles = (key_end + kBwTile - 1) / kBwTile;
+    const int pair_tiles = min(ntiles, (min(S, r0 + kBwRows) + kBwTile - 1) / kBwTile);
+    const int W = WIN ? p.window : 0;
+    const int t_first = (W > 0 ? max(0, qb * QB - W + 1) / kBwTile : 0) & ~1;
+    const int pair_lo = W > 0 ? max(0, r0 - W + 1) / kBwTile : 0;
+
+    const uint16_t *kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
+    const uint16_t *vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
+    uint4 kst[2], vst[2];  // tile j in stage j & 1
+    auto issue = [&](int t, uint4 &kd, uint4 &vd) {
+        const int key = min(t * kBwTile + tid / 16, S - 1);
+        kd = ld16(kg + (int64_t)key * p.k_ss + 8 * (tid % 16));
+        vd = ld16(vg + (int64_t)key * p.v_ss + 8 * (tid % 16));
+    };
+    auto store = [&](unsigned char *tile, const uint4 &st) {
+        *reinterpret_cast<uint4 *>(tile + (tid / 16) * kBwRowBytes + 16 * (tid % 16)) = st;
+    };
+    // End of epoch t: K and V tile t + 1 go to LDS (K buffer (t+1) % 3 last
+    // held tile t - 2, read by the value waves in epoch t - 1; V buffer
+    // (t+1) & 1 held tile t - 1, read by the score waves in epoch t - 1), and
+    // their register stage takes the loads of tile t + 3.
+    auto advance = [&](int t, auto par) {
+        constexpr int P = decltype(par)::value;
+        store(ktile + slot3(t + 1), kst[1 - P]);
+        store(vtile[1 - P], vst[1 - P]);
+        issue(t + 3, kst[1 - P], vst[1 - P]);
+        __syncthreads();
+    };
+    auto prologue = [&] {
+        issue(t_first, kst[0], vst[0]);
+        store(ktile + slot3(t_first), kst[0]);
+        store(vtile[0], vst[0]);
+        issue(t_first + 1, kst[1], vst[1]);
+        issue(t_first + 2, kst[0], vst[0]);
+        __syncthreads();
+    };
+
+    if (score_wave) {
+        // Query-side B operands: column c of block cb is q row r0 + 16cb + c
+        // (cb < 2) or the rho row of the same query (cb >= 2); gop[qc] holds
+        // the dout rows.  Head-dim value 32g + 8ks + i sits in k-slot 8g + i of
+        // MFMA ks, the slots the K and V A-operands use.
+        bf16x8_t xop[4][KS], gop[2][KS];
+        float4 st[2];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int row = min(r0 + 16 * (cb & 1) + c, S - 1);
+            const uint16_t *src = cb < 2 ? p.q + (int64_t)b * p.q_sb + (int64_t)row * p.q_ss +
+                                               (int64_t)head * p.q_sh
+                                         : p.rho + (int64_t)b * p.r_sb + (int64_t)row * p.r_ss +
+                                               (int64_t)head * p.r_sh;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                xop[cb][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + 32 * g + 8 * ks));
+        }
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+            const int row = min(r0 + 16 * qc + c, S - 1);
+            const uint16_t *src =
+                p.dout + (int64_t)b * p.g_sb + (int64_t)row * p.g_ss + (int64_t)head * p.g_sh;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                gop[qc][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + 32 * g + 8 * ks));
+            st[qc] = p.rowstat[((int64_t)b * p.num_q_heads + head) * S + row];
+        }
+
+        // d1[rb][cb]: lane (c, g) = query column c of block cb, keys
+        // 32t + 16rb + 4g + j; du[rb][qc] the same for U^T.
+        auto scores = [&](int t, f32x4_t (&d1)[2][4], f32x4_t (&du)[2][2]) {
+            const unsigned char *kt = ktile + slot3(t);
+            const unsigned char *vt = vtile[t & 1];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                du[rb][0] = du[rb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8_t kop = __builtin_bit_cast(
+                        bf16x8_t, ld16(kt + (16 * rb + c) * kBwRowBytes + 64 * g + 16 * ks));
+                    const bf16x8_t vop = __builtin_bit_cast(
+                        bf16x8_t, ld16(vt + (16 * rb + c) * kBwRowBytes + 64 * g + 16 * ks));
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = mfma(kop, xop[cb][ks], d1[rb][cb]);
+#pragma unroll
+                    for (int qc = 0; qc < 2; ++qc) du[rb][qc] = mfma(vop, gop[qc][ks], du[rb][qc]);
+                }
+            }
+        };
+        // dS^T and dT^T of tile t in bf16, as B operands of the value MFMAs
+        // (k-slot r holds key 4g + r for r < 4, else 16 + 4g + r - 4).
+        auto grads = [&](int t, const f32x4_t (&d1)[2][4], const f32x4_t (&du)[2][2],
+                         auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc) {
+                const int qi = r0 + 16 * qc + c;
+                const float lse2 = st[qc].x, r1 = 1.0f + st[qc].y, cc = st[qc].z, dd = st[qc].w;
+                uint32_t sw[4], tw[4];
+#pragma unroll
+                for (int r = 0; r < 8; r += 2) {
+                    float ds2[2], dt2[2];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int rr = r + h2;
+                        const float s = rr < 4 ? d1[0][qc][rr] : d1[1][qc][rr - 4];
+                        const float tt = rr < 4 ? d1[0][qc + 2][rr] : d1[1][qc + 2][rr - 4];
+                        const float uu = rr < 4 ? du[0][qc][rr] : du[1][qc][rr - 4];
+                        float pw = __builtin_amdgcn_exp2f(fmaf(s, c2, -lse2));
+                        if constexpr (MASK) {
+                            const int key = t * kBwTile + (rr < 4 ? 4 * g + rr : 16 + 4 * g + rr - 4);
+                            pw = key <= qi && key < S && (W == 0 || key > qi - W) ? pw : 0.0f;
+                        }
+                        const float dp = fmaf(uu, r1 - tt, cc * tt);
+                        ds2[h2] = pw * (dp - dd);
+                        dt2[h2] = pw * (cc - uu);
+                    }
+                    sw[r / 2] = pack_bf16x2(ds2[0], ds2[1]);
+                    tw[r / 2] = pack_bf16x2(dt2[0], dt2[1]);
+                }
+                pbuf[t & 1][pair][qc][lane] = uint4{sw[0], sw[1], sw[2], sw[3]};
+                pbuf[t & 1][pair][qc + 2][lane] = uint4{tw[0], tw[1], tw[2], tw[3]};
+            }
+        };
+        auto score_step = [&](int t) {
+            if (t >= pair_lo && t < pair_tiles) {
+                f32x4_t d1[2][4], du[2][2];
+                scores(t, d1, du);
+                if (t * kBwTile + kBwTile - 1 <= r0 && t * kBwTile + kBwTile <= S &&
+                    (W == 0 || t * kBwTile > r0 + kBwRows - 1 - W))
+                    grads(t, d1, du, std::false_type{});
+                else
+                    grads(t, d1, du, std::true_type{});
+            }
+        };
+        prologue();
+        for (int t = t_first; t <= ntiles; t += 2) {
+            score_step(t);
+            advance(t, std::integral_constant<int, 0>{});
+            score_step(t + 1);
+            advance(t + 1, std::integral_constant<int, 1>{});
+        }
+    } else {
+        // acc[db][cb]: rows d = 16db + 4g + j, column c of block cb (dS^T rows
+        // 0-15, 16-31, dT^T rows 0-15, 16-31) -> dq^T (cb < 2), drho^T (cb >= 2)
+        f32x4_t acc[DB][4];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) acc[db][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        auto value_tile = [&](int u) {
+            bf16x8_t pop[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                pop[cb] = __builtin_bit_cast(bf16x8_t, pbuf[u & 1][pair][cb][lane]);
+            const unsigned char *kt = ktile + slot3(u);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8_t kop = tr_operand(kt, db, c, g);
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) acc[db][cb] = mfma(kop, pop[cb], acc[db][cb]);
+            }
+        };
+
+        prologue();
+        for (int t = t_first; t <= ntiles; t += 2) {
+            if (t - 1 >= pair_lo && t - 1 < pair_tiles) value_tile(t - 1);
+            advance(t, std::integral_constant<int, 0>{});
+            if (t >= pair_lo && t < pair_tiles) value_tile(t);
+            advance(t + 1, std::integral_constant<int, 1>{});
+        }
+
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+            const int qi = r0 + 16 * qc + c;
+            if (qi >= S) continue;
+            const int64_t off = (int64_t)b * p.dq_sb + (int64_t)qi * p.dq_ss + (int64_t)head * p.dq_sh;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                *reinterpret_cast<float4 *>(p.dq + off + 16 * db + 4 * g) =
+                    float4{p.scale * acc[db][qc][0], p.scale * acc[db][qc][1],
+                           p.scale * acc[db][qc][2], p.scale * acc[db][qc][3]};
+                *reinterpret_cast<float4 *>(p.drho + off + 16 * db + 4 * g) =
+                    float4{acc[db][qc + 2][0], acc[db][qc + 2][1], acc[db][qc + 2][2],
+                           acc[db][qc + 2][3]};
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------- dkv ---
+template <int G, bool WIN>
+__global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParams p) {
+    constexpr int KS = kBwD / 32;
+    constexpr int DB = kBwD / 16;
+    constexpr int KB = kBwRows * kBwPairs;  // keys per workgroup
+
+    __shared__ __attribute__((aligned(16))) unsigned char qtile[3 * kBwTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char rtile[3 * kBwTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char gtile[3 * kBwTileBytes];
+    __shared__ float4 stile[3][kBwTile];          // row statistics of the tile's rows
+    __shared__ uint4 pbuf[2][kBwPairs][6][64];    // W, scale dS, dT (key blocks 0, 1)
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int S = p.seq_len;
+    const float c2 = p.scale_log2;
+    const bool score_wave = wave < kBwPairs;
+    const int pair = wave % kBwPairs;
+
+    const int units = p.batch * p.num_kv_heads;
+    const int kb = (int)(blockIdx.x / units);  // most query rows first
+    const int unit = blockIdx.x % units;
+    const int b = unit / p.num_kv_heads;
+    const int hk = unit % p.num_kv_heads;
+    const int k0 = kb * KB;
+    const int kp = k0 + pair * kBwRows;  // first key of this pair
+    const int W = WIN ? p.window : 0;
+    // Query tiles qt_lo .. qt_hi of every head of the group see some key of
+    // the workgroup; the stream visits them head by head.
+    const int ntq = (S + kBwTile - 1) / kBwTile;
+    const int qt_lo = k0 / kBwTile;
+    const int qt_hi = W > 0 ? min(ntq - 1, (k0 + KB - 1 + W - 1) / kBwTile) : ntq - 1;
+    const int nq = qt_hi - qt_lo + 1;
+    const int ntiles = G * nq;
+    // this pair's tiles within each head's run (none when its keys are past S)
+    const int pq_lo = kp < S ? kp / kBwTile : ntq;
+    const int pq_hi = W > 0 ? min(qt_hi, (kp + kBwRows - 1 + W - 1) / kBwTile) : qt_hi;
+
+    auto tile_head = [&](int t) { return hk * G + t / nq; };
+    auto tile_qt = [&](int t) { return qt_lo + t % nq; };
+
+    // Two register stages (named, not an array: the compiler may move an
+    // array it fails to keep in registers into LDS).
+    struct Stage {
+        uint4 q, r, g;
+        float4 s;
+    } stage0, stage1;
+    auto stage = [&](auto par) -> Stage & {
+        if constexpr (decltype(par)::value == 0) return stage0;
+        else return stage1;
+    };
+    // register stage P of tile t (P fixed at compile time: a runtime index
+    // into a register array would move it to scratch memory)
+    auto issue = [&](int t, auto par) {
+        Stage &st = stage(par);
+        const int tt = min(t, ntiles - 1);
+        const int h = tile_head(tt);
+        const int row = min(tile_qt(tt) * kBwTile + tid / 16, S - 1);
+        st.q = ld16(p.q + (int64_t)b * p.q_sb + (int64_t)row * p.q_ss + (int64_t)h * p.q_sh +
+                      8 * (tid % 16));
+        st.r = ld16(p.rho + (int64_t)b * p.r_sb + (int64_t)row * p.r_ss + (int64_t)h * p.r_sh +
+                      8 * (tid % 16));
+        st.g = ld16(p.dout + (int64_t)b * p.g_sb + (int64_t)row * p.g_ss + (int64_t)h * p.g_sh +
+                      8 * (tid % 16));
+        st.s = p.rowstat[((int64_t)b * p.num_q_heads + h) * S + row];
+    };
+    auto store = [&](int t, auto par) {
+        const Stage &st = stage(par);
+        const int off = slot3(t) + (tid / 16) * kBwRowBytes + 16 * (tid % 16);
+        *reinterpret_cast<uint4 *>(qtile + off) = st.q;
+        *reinterpret_cast<uint4 *>(rtile + off) = st.r;
+        *reinterpret_cast<uint4 *>(gtile + off) = st.g;
+        // the 16 threads of a row all store its statistics (same value): no
+        // lane condition, so no branch around a store that waits on a load
+        stile[t % 3][tid / 16] = st.s;
+    };
+    auto advance = [&](int t, auto par) {
+        constexpr int P = decltype(par)::value;
+        store(t + 1, std::integral_constant<int, 1 - P>{});
+        issue(t + 3, std::integral_constant<int, 1 - P>{});
+        __syncthreads();
+    };
+    auto prologue = [&] {
+        issue(0, std::integral_constant<int, 0>{});
+        store(0, std::integral_constant<int, 0>{});
+        issue(1, std::integral_constant<int, 1>{});
+        issue(2, std::integral_constant<int, 0>{});
+        __syncthreads();
+    };
+    auto active = [&](int t) {
+        if (t < 0 || t >= ntiles) return false;
+        const int qt = tile_qt(t);
+        return qt >= pq_lo && qt <= pq_hi;
+    };
+
+    if (score_wave) {
+        // Key-side B operands: column c of block kc is key kp + 16kc + c;
+        // head-dim value 32g + 8ks + i in k-slot 8g + i of MFMA ks.
+        bf16x8_t kop[2][KS], vop[2][KS];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const int key = min(kp + 16 * kc + c, S - 1);
+            const uint16_t *ks_ = p.k + (int64_t)b * p.k_sb + (int64_t)key * p.k_ss + (int64_t)hk * p.k_sh;
+            const uint16_t *vs_ = p.v + (int64_t)b * p.v_sb + (int64_t)key * p.v_ss + (int64_t)hk * p.v_sh;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                kop[kc][ks] = __builtin_bit_cast(bf16x8_t, ld16(ks_ + 32 * g + 8 * ks));
+                vop[kc][ks] = __builtin_bit_cast(bf16x8_t, ld16(vs_ + 32 * g + 8 * ks));
+            }
+        }
+
+        // sd/td/ud[rb][kc]: lane (c, g) = key column c of block kc, tile rows
+        // 16rb + 4g + j.
+        auto scores = [&](int t, f32x4_t (&sd)[2][2], f32x4_t (&td)[2][2], f32x4_t (&ud)[2][2]) {
+            const int buf = slot3(t);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+                    sd[rb][kc] = td[rb][kc] = ud[rb][kc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int off = (16 * rb + c) * kBwRowBytes + 64 * g + 16 * ks;
+                    const bf16x8_t qa = __builtin_bit_cast(bf16x8_t, ld16(qtile + buf + off));
+                    const bf16x8_t ra = __builtin_bit_cast(bf16x8_t, ld16(rtile + buf + off));
+                    const bf16x8_t ga = __builtin_bit_cast(bf16x8_t, ld16(gtile + buf + off));
+#pragma unroll
+                    for (int kc = 0; kc < 2; ++kc) {
+                        sd[rb][kc] = mfma(qa, kop[kc][ks], sd[rb][kc]);
+                        td[rb][kc] = mfma(ra, kop[kc][ks], td[rb][kc]);
+                        ud[rb][kc] = mfma(ga, vop[kc][ks], ud[rb][kc]);
+                    }
+                }
+            }
+        };
+        // W = p (1 + r - t), scale dS and dT of tile t in bf16, as B operands
+        // of the value MFMAs (column = key, k-slot r = tile row 4g + r for
+        // r < 4, else 16 + 4g + r - 4).
+        auto grads = [&](int t, const f32x4_t (&sd)[2][2], const f32x4_t (&td)[2][2],
+                         const f32x4_t (&ud)[2][2], auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            const int buf = t % 3;
+            const int row0 = tile_qt(t) * kBwTile;
+            uint32_t ww[8], sw[8], tw[8];  // [4 kc + k-slot pair]
+            // one 16-row half at a time: its four rows' statistics are live
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                float4 rs[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) rs[j] = stile[buf][16 * rb + 4 * g + j];
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const int key = kp + 16 * kc + c;
+#pragma unroll
+                    for (int j = 0; j < 4; j += 2) {
+                        float w2[2], ds2[2], dt2[2];
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            const float s = sd[rb][kc][j + h2];
+                            const float tt = td[rb][kc][j + h2];
+                            const float uu = ud[rb][kc][j + h2];
+                            const float4 st = rs[j + h2];
+                            float pw = __builtin_amdgcn_exp2f(fmaf(s, c2, -st.x));
+                            if constexpr (MASK) {
+                                const int qi = row0 + 16 * rb + 4 * g + j + h2;
+                                pw = key <= qi && qi < S && key < S && (W == 0 || key > qi - W)
+                                         ? pw
+                                         : 0.0f;
+                            }
+                            const float m1 = 1.0f + st.y - tt;
+                            w2[h2] = pw * m1;
+                            ds2[h2] = p.scale * pw * (fmaf(uu, m1, st.z * tt) - st.w);
+                            dt2[h2] = pw * (st.z - uu);
+                        }
+                        // k-slot 4rb + j of the value MFMAs' B operand
+                        ww[4 * kc + 2 * rb + j / 2] = pack_bf16x2(w2[0], w2[1]);
+                        sw[4 * kc + 2 * rb + j / 2] = pack_bf16x2(ds2[0], ds2[1]);
+                        tw[4 * kc + 2 * rb + j / 2] = pack_bf16x2(dt2[0], dt2[1]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                pbuf[t & 1][pair][kc][lane] =
+                    uint4{ww[4 * kc], ww[4 * kc + 1], ww[4 * kc + 2], ww[4 * kc + 3]};
+                pbuf[t & 1][pair][2 + kc][lane] =
+                    uint4{sw[4 * kc], sw[4 * kc + 1], sw[4 * kc + 2], sw[4 * kc + 3]};
+                pbuf[t & 1][pair][4 + kc][lane] =
+                    uint4{tw[4 * kc], tw[4 * kc + 1], tw[4 * kc + 2], tw[4 * kc + 3]};
+            }
+        };
+        auto score_step = [&](int t) {
+            if (active(t)) {
+                f32x4_t sd[2][2], td[2][2], ud[2][2];
+                scores(t, sd, td, ud);
+                const int row0 = tile_qt(t) * kBwTile;
+                // unmasked when every row of the tile sees every key of the pair
+                if (row0 >= kp + kBwRows - 1 && row0 + kBwTile <= S && kp + kBwRows <= S &&
+                    (W == 0 || row0 + kBwTile - 1 - W < kp))
+                    grads(t, sd, td, ud, std::false_type{});
+                else
+                    grads(t, sd, td, ud, std::true_type{});
+            }
+        };
+        prologue();
+        for (int t = 0; t <= ntiles; t += 2) {
+            score_step(t);
+            advance(t, std::integral_constant<int, 0>{});
+            score_step(t + 1);
+            advance(t + 1, std::integral_constant<int, 1>{});
+        }
+    } else {
+        // dvt[db][kc], dkt[db][kc]: rows d = 16db + 4g + j, key column c of
+        // block kc.
+        f32x4_t dvt[DB][2], dkt[DB][2];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) dvt[db][kc] = dkt[db][kc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        auto value_tile = [&](int u) {
+            bf16x8_t pw[2], ps[2], pt[2];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                pw[kc] = __builtin_bit_cast(bf16x8_t, pbuf[u & 1][pair][kc][lane]);
+                ps[kc] = __builtin_bit_cast(bf16x8_t, pbuf[u & 1][pair][2 + kc][lane]);
+                pt[kc] = __builtin_bit_cast(bf16x8_t, pbuf[u & 1][pair][4 + kc][lane]);
+            }
+            const int buf = slot3(u);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8_t ga = tr_operand(gtile + buf, db, c, g);
+                const bf16x8_t qa = tr_operand(qtile + buf, db, c, g);
+                const bf16x8_t ra = tr_operand(rtile + buf, db, c, g);
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    dvt[db][kc] = mfma(ga, pw[kc], dvt[db][kc]);
+                    dkt[db][kc] = mfma(qa, ps[kc], dkt[db][kc]);
+                    dkt[db][kc] = mfma(ra, pt[kc], dkt[db][kc]);
+                }
+                // keep the transposed reads of later blocks from being hoisted
+                // all at once (48 reads would need 96 registers)
+                if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+
+        prologue();
+        for (int t = 0; t <= ntiles; t += 2) {
+            if (active(t - 1)) value_tile(t - 1);
+            advance(t, std::integral_constant<int, 0>{});
+            if (active(t)) value_tile(t);
+            advance(t + 1, std::integral_constant<int, 1>{});
+        }
+
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            const int key = kp + 16 * kc + c;
+            if (key >= S) continue;
+            const int64_t off = (int64_t)b * p.dk_sb + (int64_t)key * p.dk_ss + (int64_t)hk * p.dk_sh;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                *reinterpret_cast<float4 *>(p.dk + off + 16 * db + 4 * g) =
+                    float4{dkt[db][kc][0], dkt[db][kc][1], dkt[db][kc][2], dkt[db][kc][3]};
+                *reinterpret_cast<float4 *>(p.dv + off + 16 * db + 4 * g) =
+                    float4{dvt[db][kc][0], dvt[db][kc][1], dvt[db][kc][2], dvt[db][kc][3]};
+            }
+        }
+    }
+}
+
+template <int G, bool WIN>
+hipError_t launch_bwd(const PrefillBwdParams &p, hipStream_t stream) {
+    const int units = p.batch * p.num_kv_heads;
+    const int qb_rows = kBwRows * kBwPairs / G;
+    const int nqb = (p.seq_len + qb_rows - 1) / qb_rows;
+    const int nkb = (p.seq_len + kBwRows * kBwPairs - 1) / (kBwRows * kBwPairs);
+    hipLaunchKernelGGL((bwd_dq_kernel<G, WIN>), dim3((unsigned)(units * nqb)), dim3(128 * kBwPairs),
+                       0, stream, p);
+    hipLaunchKernelGGL((bwd_dkv_kernel<G, WIN>), dim3((unsigned)(units * nkb)),
+                       dim3(128 * kBwPairs), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_backward(const PrefillBwdParams &p, int d, hipStream_t stream) {
+    if (d != kBwD) return hipErrorInvalidValue;
+    const int64_t rows = (int64_t)p.batch * p.num_q_heads * p.seq_len;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int G = p.num_q_heads / p.num_kv_heads;
+    const bool win = p.window > 0 && p.window < p.seq_len;
+    switch (G * 2 + (win ? 1 : 0)) {
+        case 2: return launch_bwd<1, false>(p, stream);
+        case 3: return launch_bwd<1, true>(p, stream);
+        case 4: return launch_bwd<2, false>(p, stream);
+        case 5: return launch_bwd<2, true>(p, stream);
+        case 8: return launch_bwd<4, false>(p, stream);
+        case 9: return launch_bwd<4, true>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace plx

@@ -140,6 +140,12 @@ def prefill_inputs(B, S, Hq, Hkv, d, *, dtype=torch.bfloat16, seed=0, rho_std=0.
     return q, rho, k, v, 1.0 / math.sqrt(d)
 
 
+def prefill_dout(B, S, Hq, d, *, dtype=torch.bfloat16, seed=0, std=1.0, device="cpu"):
+    """Upstream gradient of a prefill output, [B, S, Hq, d] ~ N(0, std^2),
+    drawn from its own generator (pass a seed different from the inputs')."""
+    return _randn((B, S, Hq, d), _gen(device, seed), device, dtype, std=std)
+
+
 def host_array(t: torch.Tensor):
     """A numpy view of a tensor's exact bits on the host (bf16 -> raw uint16)."""
     t = t.detach().contiguous().cpu()

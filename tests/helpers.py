@@ -12,6 +12,14 @@ TAU_F32 = 1e-5
 TAU_BF16 = 2e-2
 RMS_DECODE_BF16 = 1e-3
 RMS_PREFILL = 1e-2
+# Prefill backward: the kernels round the weights p (1 + r - t), ds and dt to
+# bf16 before the gradient products, and the forward's statistics carry its own
+# bf16 rounding.  dt_j = p_j (c - u_j) sums to zero over a row's keys, so drho
+# is a cancelling sum whose per-term rounding does not cancel: a simulation of
+# these rounding steps at the test shapes gives elementwise ratios up to
+# 8.8e-2 (drho) and relative RMS errors up to 2.1e-3 for all four gradients.
+TAU_BWD = 0.15
+RMS_BWD = 1e-2
 
 
 def parity(gpu, ref):

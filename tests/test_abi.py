@@ -23,6 +23,7 @@ def test_exports_every_declared_function(lib):
     text = open(HEADER).read()
     names = set(re.findall(r"\b(parallax_[a-z_]+)\s*\(", text))
     assert {"parallax_decode", "parallax_prefill", "parallax_decode_workspace_size",
+            "parallax_prefill_backward", "parallax_prefill_backward_workspace_size",
             "parallax_status_string", "parallax_last_error", "parallax_abi_version"} <= names
     for n in sorted(names):
         assert hasattr(lib, n), f"{n} is declared but not exported"
@@ -169,14 +170,96 @@ def test_prefill_rejects(lib, over, status, needle):
     assert lib.parallax_prefill(None, None) == INVALID
 
 
-def test_version_1_structs_are_rejected(lib):
-    """ABI version 2 appended `window` to both argument structs; a caller
-    built against version 1 passes the old, smaller struct_size."""
+def test_older_structs_are_rejected(lib):
+    """ABI version 2 appended `window` to both argument structs and version 3
+    the three optional statistics outputs to the prefill struct; a caller
+    built against an older header passes a smaller struct_size."""
     old_decode = ctypes.sizeof(plx.DecodeArgs) - 8
-    old_prefill = ctypes.sizeof(plx.PrefillArgs) - 8
     st, _ = ws_size(lib, good_decode(struct_size=old_decode))
     assert st == INVALID and "struct_size" in plx.parallax_last_error()
-    assert lib.parallax_prefill(ctypes.byref(good_prefill(struct_size=old_prefill)), None) == INVALID
+    for old_prefill in (ctypes.sizeof(plx.PrefillArgs) - 24, ctypes.sizeof(plx.PrefillArgs) - 32):
+        a = good_prefill(struct_size=old_prefill)
+        assert lib.parallax_prefill(ctypes.byref(a), None) == INVALID
+        assert "struct_size" in plx.parallax_last_error()
+
+
+def test_prefill_stats_outputs_must_be_aligned(lib):
+    for name in ("lse", "rmean", "o_sa"):
+        a = good_prefill(**{name: FAKE + 4})
+        assert lib.parallax_prefill(ctypes.byref(a), None) == UNSUPP
+        assert "aligned" in plx.parallax_last_error()
+
+
+def good_backward(**over):
+    a = plx.PrefillBackwardArgs()
+    a.struct_size = ctypes.sizeof(plx.PrefillBackwardArgs)
+    a.batch, a.seq_len, a.num_q_heads, a.num_kv_heads, a.head_dim = 4, 8192, 16, 8, 128
+    a.scale = 128 ** -0.5
+    a.causal = 1
+    for n in ("q", "rho", "k", "v", "dout", "out", "o_sa", "lse", "rmean", "dq", "drho", "dk",
+              "dv"):
+        setattr(a, n, FAKE)
+    qs = (8192 * 16 * 128, 16 * 128, 128)
+    ks = (8192 * 8 * 128, 8 * 128, 128)
+    for pre, st in (("q", qs), ("rho", qs), ("dout", qs), ("out", qs), ("dq", qs), ("k", ks),
+                    ("v", ks), ("dk", ks)):
+        setattr(a, pre + "_stride_b", st[0])
+        setattr(a, pre + "_stride_s", st[1])
+        setattr(a, pre + "_stride_h", st[2])
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def bw_size(lib, a):
+    n = ctypes.c_size_t(123)
+    st = lib.parallax_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_backward_workspace_size(lib):
+    """One float4 of row statistics per (batch, query head, row)."""
+    assert bw_size(lib, good_backward()) == (plx.PARALLAX_OK, 4 * 16 * 8192 * 16)
+    assert bw_size(lib, good_backward(seq_len=5, batch=1)) == (plx.PARALLAX_OK, 16 * 5 * 16)
+    assert lib.parallax_prefill_backward_workspace_size(ctypes.byref(good_backward()), None) == \
+        INVALID
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(struct_size=8), INVALID, "struct_size"),
+    (dict(batch=0), INVALID, "batch"),
+    (dict(num_kv_heads=3), INVALID, "num_q_heads"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(dout=None), INVALID, "non-NULL"),
+    (dict(lse=None), INVALID, "non-NULL"),
+    (dict(dv=None), INVALID, "non-NULL"),
+    (dict(dk_stride_s=-4), INVALID, "non-negative"),
+    (dict(window=-1), INVALID, "window"),
+    (dict(causal=0), UNSUPP, "causal"),
+    (dict(head_dim=64), UNSUPP, "head_dim"),
+    (dict(num_q_heads=64), UNSUPP, "GQA group"),
+    (dict(rmean=FAKE + 8), UNSUPP, "aligned"),
+    (dict(dout_stride_h=132), UNSUPP, "16 bytes"),
+    (dict(dq_stride_s=2050), UNSUPP, "16 bytes"),
+])
+def test_backward_rejects(lib, over, status, needle):
+    a = good_backward(**over)
+    assert bw_size(lib, a)[0] == status
+    assert needle in plx.parallax_last_error()
+    assert lib.parallax_prefill_backward(ctypes.byref(a), FAKE, 1 << 30, None) == status
+    assert lib.parallax_prefill_backward(None, FAKE, 1 << 30, None) == INVALID
+
+
+def test_backward_workspace_checks(lib):
+    a = good_backward()
+    _, need = bw_size(lib, a)
+    assert lib.parallax_prefill_backward(ctypes.byref(a), None, need, None) == \
+        plx.PARALLAX_ERR_WORKSPACE
+    assert lib.parallax_prefill_backward(ctypes.byref(a), FAKE, need - 16, None) == \
+        plx.PARALLAX_ERR_WORKSPACE
+    assert lib.parallax_prefill_backward(ctypes.byref(a), FAKE + 8, need, None) == \
+        plx.PARALLAX_ERR_WORKSPACE
+    assert "workspace" in plx.parallax_last_error()
 
 
 def test_window_shrinks_the_split_plan(lib):

@@ -1,0 +1,200 @@
+"""GPU parity of the causal prefill backward pass (parallax_prefill_backward)
+and of the statistics the forward pass keeps for it, against the fp64 oracle,
+through the C ABI.
+
+The GPU backward consumes the GPU forward's own outputs (out, o_sa, lse, r);
+the oracle recomputes everything from the inputs, so these tests check the
+whole training step.  Small cases compare every element (ragged lengths
+around the 32-row tiles and 128-row blocks, GQA groups 1/2/4, local windows);
+the full-size workload (batch 4 x 8192 tokens, 16 query / 8 KV heads, d 128)
+compares sampled rows of dq and drho, the last 64 keys' dk and dv (exact for
+them: no earlier row sees those keys), and two properties that hold at any
+size: per (batch, KV head) the value gradients sum to the summed dout of its
+rows, and the key gradients sum to zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parallax_local_linear_decode_amd as plx
+from parallax_local_linear_decode_amd.workloads import host_array, prefill_dout, prefill_inputs
+
+from helpers import RMS_BWD, RMS_PREFILL, TAU_BF16, TAU_BWD, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+# log-sum-exp: the forward's denominator sums bf16-rounded numerators, each
+# within 2^-9 relative, so log Z is within about 2e-3 of the exact value.
+LSE_ABS = 4e-3
+
+
+def forward_backward(q, rho, k, v, dout, scale, window=0):
+    out, lse, rmean, o_sa = plx.parallax_prefill(q, rho, k, v, scale=scale, window=window,
+                                                 return_stats=True)
+    grads = plx.parallax_prefill_backward(q, rho, k, v, dout, out, o_sa, lse, rmean,
+                                          scale=scale, window=window)
+    torch.cuda.synchronize()
+    return (out, lse, rmean, o_sa), grads
+
+
+def case(B, S, Hq, Hkv, seed, device):
+    q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, 128, seed=seed, device=device)
+    dout = prefill_dout(B, S, Hq, 128, seed=seed + 7919, device=device)
+    return q, rho, k, v, dout, scale
+
+
+def check_stats(stats, q, rho, k, v, scale, window=0, rows=None, what=""):
+    out, lse, rmean, o_sa = stats
+    h = [host_array(t) for t in (q, rho, k, v)]
+    ref_lse, ref_r, ref_a = oracle.prefill_stats(*h, scale, rows=rows, window=window)
+    sel = slice(None) if rows is None else torch.as_tensor(rows, dtype=torch.long)
+    got_lse = lse[:, :, sel].permute(0, 2, 1).double().cpu().numpy()
+    got_r = rmean[:, :, sel].permute(0, 2, 1)
+    assert np.all(np.isfinite(got_lse))
+    err = float(np.max(np.abs(got_lse - ref_lse)))
+    assert err <= LSE_ABS, f"{what}: lse err {err:.2e}"
+    assert_parity(got_r, ref_r, TAU_BF16, RMS_PREFILL, what=f"{what} r")
+    assert_parity(o_sa[:, sel], ref_a, TAU_BF16, RMS_PREFILL, what=f"{what} o_sa")
+
+
+@pytest.mark.parametrize("S", [1, 17, 31, 32, 33, 64, 100, 129, 257])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2), (8, 2)])
+def test_small_every_gradient(gpu, S, Hq, Hkv):
+    q, rho, k, v, dout, scale = case(2, S, Hq, Hkv, S * 10 + Hq, gpu)
+    stats, grads = forward_backward(q, rho, k, v, dout, scale)
+    check_stats(stats, q, rho, k, v, scale, what=f"S={S} {Hq}/{Hkv}")
+    ref = oracle.prefill_backward(*(host_array(t) for t in (q, rho, k, v, dout)), scale)
+    for name, g, r in zip(("dq", "drho", "dk", "dv"), grads, ref):
+        assert_parity(g, r, TAU_BWD, RMS_BWD, what=f"S={S} {Hq}/{Hkv} {name}")
+
+
+@pytest.mark.parametrize("W", [1, 5, 31, 32, 33, 100])
+@pytest.mark.parametrize("S,Hq,Hkv", [(100, 4, 2), (300, 2, 1), (257, 8, 2)])
+def test_window_every_gradient(gpu, S, Hq, Hkv, W):
+    q, rho, k, v, dout, scale = case(1, S, Hq, Hkv, S + W, gpu)
+    stats, grads = forward_backward(q, rho, k, v, dout, scale, window=W)
+    check_stats(stats, q, rho, k, v, scale, window=W, what=f"S={S} W={W}")
+    ref = oracle.prefill_backward(*(host_array(t) for t in (q, rho, k, v, dout)), scale,
+                                  window=W)
+    for name, g, r in zip(("dq", "drho", "dk", "dv"), grads, ref):
+        assert_parity(g, r, TAU_BWD, RMS_BWD, what=f"S={S} W={W} {name}")
+
+
+def test_window_at_least_the_sequence_is_full(gpu):
+    q, rho, k, v, dout, scale = case(1, 200, 4, 2, 11, gpu)
+    _, full = forward_backward(q, rho, k, v, dout, scale)
+    full = [t.clone() for t in full]
+    for W in (200, 5000):
+        _, win = forward_backward(q, rho, k, v, dout, scale, window=W)
+        for a, b in zip(full, win):
+            assert torch.equal(a, b)
+
+
+def test_rho_zero_matches_softmax_attention_gradients(gpu):
+    """rho = 0: dq, dk, dv are those of plain causal softmax attention
+    (torch autograd in fp64 on the CPU)."""
+    q, rho, k, v, dout, scale = case(1, 150, 4, 2, 12, gpu)
+    rho = torch.zeros_like(rho)
+    _, grads = forward_backward(q, rho, k, v, dout, scale)
+    tq, tk, tv = (t.double().cpu().requires_grad_() for t in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.transpose(1, 2), tk.repeat_interleave(2, dim=2).transpose(1, 2),
+        tv.repeat_interleave(2, dim=2).transpose(1, 2), is_causal=True, scale=scale)
+    (o.transpose(1, 2) * dout.double().cpu()).sum().backward()
+    for name, g, r in (("dq", grads[0], tq.grad), ("dk", grads[2], tk.grad),
+                       ("dv", grads[3], tv.grad)):
+        assert_parity(g, r.numpy(), TAU_BWD, RMS_BWD, what=f"rho=0 {name}")
+
+
+def test_strided_views_and_preallocated_outputs(gpu):
+    """Inputs as views into wider buffers and caller-owned outputs (given
+    garbage first) give the same bits as contiguous tensors."""
+    q, rho, k, v, dout, scale = case(1, 96, 4, 2, 13, gpu)
+    _, ref = forward_backward(q, rho, k, v, dout, scale)
+    wide = torch.zeros((1, 96, 4, 256), dtype=torch.bfloat16, device=gpu)
+    wide[..., 64:192] = q
+    qv = wide[..., 64:192]
+    stats = plx.parallax_prefill(qv, rho, k, v, scale=scale, return_stats=True)
+    outs = [torch.full_like(t, float("nan")) for t in ref]
+    ws = torch.full((1 << 16,), 255, dtype=torch.uint8, device=gpu)
+    got = plx.parallax_prefill_backward(qv, rho, k, v, dout, *stats[:1], stats[3], stats[1],
+                                        stats[2], scale=scale, dq=outs[0], drho=outs[1],
+                                        dk=outs[2], dv=outs[3], workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
+def test_deterministic_small(gpu):
+    q, rho, k, v, dout, scale = case(2, 300, 8, 2, 14, gpu)
+    _, first = forward_backward(q, rho, k, v, dout, scale)
+    first = [t.clone() for t in first]
+    for _ in range(10):
+        _, again = forward_backward(q, rho, k, v, dout, scale)
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_full_size(gpu):
+    B, S, Hq, Hkv = 4, 8192, 16, 8
+    q, rho, k, v, dout, scale = case(B, S, Hq, Hkv, 15, gpu)
+    stats, grads = forward_backward(q, rho, k, v, dout, scale)
+    dq, drho, dk, dv = grads
+    for t in grads:
+        assert torch.isfinite(t).all()
+    rng = np.random.default_rng(15)
+    early = [0, 1, 31, 32, 127, 128, 1000, 4095, 4096] + sorted(rng.integers(0, S - 64, 12))
+    tail = list(range(S - 64, S))
+    rows = np.array(sorted(set(early)) + tail, dtype=np.int32)
+    # the oracle on sequences 0 and 3 (every head), to bound its CPU time
+    bs = [0, 3]
+    sub = [t[bs] for t in (q, rho, k, v, dout)]
+    check_stats([t[bs] for t in stats], *sub[:4], scale, rows=rows, what="full size")
+    r_dq, r_drho, r_dk, r_dv = oracle.prefill_backward(*(host_array(t) for t in sub), scale,
+                                                       rows=rows)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    assert_parity(dq[bs][:, sel], r_dq, TAU_BWD, RMS_BWD, what="full dq")
+    assert_parity(drho[bs][:, sel], r_drho, TAU_BWD, RMS_BWD, what="full drho")
+    assert_parity(dk[bs, S - 64:], r_dk[:, S - 64:], TAU_BWD, RMS_BWD, what="full dk tail")
+    assert_parity(dv[bs, S - 64:], r_dv[:, S - 64:], TAU_BWD, RMS_BWD, what="full dv tail")
+    # invariants over every key
+    g_sum = dout.double().reshape(B, S, Hkv, Hq // Hkv, 128).sum(dim=(1, 3)).cpu().numpy()
+    assert_parity(dv.double().sum(dim=1), g_sum, TAU_BWD, RMS_BWD, what="sum dv")
+    dk_sum = dk.double().sum(dim=1).abs().max().item()
+    dk_scale = dk.double().abs().sum(dim=1).max().item()
+    assert dk_sum <= 1e-3 * dk_scale, (dk_sum, dk_scale)
+
+
+@pytest.mark.slow
+def test_full_size_deterministic(gpu):
+    q, rho, k, v, dout, scale = case(4, 8192, 16, 8, 16, gpu)
+    stats, first = forward_backward(q, rho, k, v, dout, scale)
+    first = [t.clone() for t in first]
+    for _ in range(5):
+        grads = plx.parallax_prefill_backward(q, rho, k, v, dout, stats[0], stats[3], stats[1],
+                                              stats[2], scale=scale)
+        torch.cuda.synchronize()
+        for a, b in zip(first, grads):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_full_size_window(gpu):
+    B, S, Hq, Hkv, W = 4, 8192, 16, 8, 1024
+    q, rho, k, v, dout, scale = case(B, S, Hq, Hkv, 17, gpu)
+    _, (dq, drho, dk, dv) = forward_backward(q, rho, k, v, dout, scale, window=W)
+    # rows 3000..4063 are every row that sees keys 3000..3040 (window 1024);
+    # the oracle on sequence 1, every head
+    rows = np.arange(3000, 3000 + 40 + W, dtype=np.int32)
+    sub = [t[1:2] for t in (q, rho, k, v, dout)]
+    r_dq, r_drho, r_dk, r_dv = oracle.prefill_backward(*(host_array(t) for t in sub), scale,
+                                                       rows=rows, window=W)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    assert_parity(dq[1:2, sel], r_dq, TAU_BWD, RMS_BWD, what="window dq")
+    assert_parity(drho[1:2, sel], r_drho, TAU_BWD, RMS_BWD, what="window drho")
+    assert_parity(dk[1:2, 3000:3040], r_dk[:, 3000:3040], TAU_BWD, RMS_BWD,
+                  what="window dk")
+    assert_parity(dv[1:2, 3000:3040], r_dv[:, 3000:3040], TAU_BWD, RMS_BWD,
+                  what="window dv")
