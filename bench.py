@@ -17,8 +17,8 @@ this GPU, and `frac_of_read_stream` = value / that rate.
 
 Prints ONE JSON line.  Other workloads: --workload paged (256 sequences, ctx
 U[128, 32768], 16-token pages), prefill (batch 4, seq 8192, 16/8 heads),
-sweep (batch x ctx grid), copy (a plain device copy used to calibrate the
-HBM byte counters).
+prefill_bwd (the backward pass of that prefill), sweep (batch x ctx grid),
+copy (a plain device copy used to calibrate the HBM byte counters).
 """
 from __future__ import annotations
 
@@ -45,6 +45,7 @@ KERNEL_SOURCES = {  # what the kernels of a workload are built from
     "decode": ["parallax_local_linear_decode_amd/csrc/decode.hip"] + _COMMON,
     "paged": ["parallax_local_linear_decode_amd/csrc/decode.hip"] + _COMMON,
     "prefill": ["parallax_local_linear_decode_amd/csrc/prefill.hip"] + _COMMON,
+    "prefill_bwd": ["parallax_local_linear_decode_amd/csrc/prefill_bwd.hip"] + _COMMON,
 }
 
 
@@ -394,6 +395,100 @@ def run_prefill(args, torch, plx):
     }
 
 
+def prefill_bwd_flops(B, S, Hq, d, window=0):
+    """Algorithmic flops of the backward pass: per causal (query, key) pair
+    and query head, eight products of 2*d flops each -- the scores q.k and
+    probe projections rho.k recomputed, u = dout.v, and the gradient sums
+    into dv, dk (from ds and from dt), dq and drho."""
+    return 8 * 2 * d * causal_pairs(S, window) * B * Hq
+
+
+def run_prefill_bwd(args, torch, plx):
+    import ctypes
+    import numpy as np
+    import oracle
+    from parallax_local_linear_decode_amd.workloads import (host_array, prefill_dout,
+                                                            prefill_inputs)
+    B, S, Hq, Hkv, d = 4, 8192, 16, 8, 128
+    W = args.window
+    dev = torch.device("cuda:0")
+    q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, d, seed=0, device=dev)
+    dout = prefill_dout(B, S, Hq, d, seed=1, device=dev)
+    out, lse, rmean, o_sa = plx.parallax_prefill(q, rho, k, v, scale=scale, window=W,
+                                                 return_stats=True)
+    dq = torch.empty((B, S, Hq, d), dtype=torch.float32, device=dev)
+    drho = torch.empty_like(dq)
+    dk = torch.empty((B, S, Hkv, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    lib = plx.load_library()
+    a = plx._backward_args(q, rho, k, v, dout, out, o_sa, lse, rmean, dq, drho, dk, dv, scale,
+                           True, W)
+    need = ctypes.c_size_t(0)
+    if lib.parallax_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(need)) != 0:
+        raise SystemExit(plx.parallax_last_error())
+    ws = torch.empty(int(need.value), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(i):
+        st = lib.parallax_prefill_backward(ctypes.byref(a), ctypes.c_void_p(ws.data_ptr()),
+                                           ws.numel(), stream)
+        if st != 0:
+            plx._raise(st, lib)
+
+    launch(0)
+    torch.cuda.synchronize()
+    # parity of the timed data: sampled rows' dq / drho, the last 64 keys'
+    # dk / dv (exact from rows S-64..S-1), on sequence 0 and every head
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([rng.integers(0, S - 64, 8), np.arange(S - 64, S)]))
+    rows = rows.astype(np.int32)
+    sub = [host_array(t[:1]) for t in (q, rho, k, v, dout)]
+    r_dq, r_drho, r_dk, r_dv = oracle.prefill_backward(*sub, scale, rows=rows, window=W)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    for got, ref in ((dq[:1, sel], r_dq), (drho[:1, sel], r_drho), (dk[:1, S - 64:], r_dk[:, S - 64:]),
+                     (dv[:1, S - 64:], r_dv[:, S - 64:])):
+        gate(got.double().cpu().numpy(), ref, 0.15, 1e-2)
+    flops = prefill_bwd_flops(B, S, Hq, d, W)
+    cpu = None
+    if args.cpu_baseline:
+        # the oracle's backward over a growing sample of query rows of every
+        # (batch, head); its time is scaled by the causal pairs covered
+        hq = [host_array(t) for t in (q, rho, k, v, dout)]
+        threads = oracle.default_threads()
+        order = rng.permutation(S).astype(np.int32)
+        secs, n, done, seen = 0.0, 8, 0, 0
+        while secs < 10.0 and done < S:
+            batch = np.sort(order[done:done + n])
+            t0 = time.perf_counter()
+            oracle.prefill_backward(*hq, scale, rows=batch, window=W, threads=threads)
+            secs += time.perf_counter() - t0
+            seen += int(np.sum(batch + 1 if W <= 0 else np.minimum(batch + 1, W)))
+            done += n
+            n *= 2
+        full = secs * causal_pairs(S, W) / seen
+        cpu = {"value": flops / full / 1e12, "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle", "seconds_per_step": full,
+               "sample": f"{done} query rows x all (batch, head), fp64 chain rule; time "
+                         f"scaled by causal pairs ({secs:.1f} s measured)"}
+    secs = time_launches(torch, launch, 1, args.steps, args.warmup)
+    per = secs / args.steps
+    tflops = flops / per / 1e12
+    wtxt = f", local window {W}" if W > 0 else ""
+    return {
+        "metric": "Parallax causal prefill backward TFLOP/s (% of bf16 MFMA peak)",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "ms_per_step": per * 1e3, "dtype": "bf16",
+        "config": {"workload": "causal prefill backward (dq, drho, dk, dv): batch 4, seq 8192, "
+                               f"16 query / 8 KV heads, d 128, bf16 inputs and dout{wtxt}",
+                   "batch": B, "seq_len": S, "window": W},
+        "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "tokens_per_s": B * S / per,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_for("prefill_bwd") if W <= 0 else None},
+        "cpu_baseline": cpu,
+    }
+
+
 def gate(gpu, ref, tau, rms):
     import numpy as np
     ratio = float(np.max(np.abs(gpu - ref) / (1 + np.abs(ref))))
@@ -409,7 +504,7 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "paged", "prefill", "sweep", "copy"])
+                    choices=["decode", "paged", "prefill", "prefill_bwd", "sweep", "copy"])
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--ctx", type=int, default=4096)
     ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
@@ -433,7 +528,8 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     plx.load_library()
     runner = {"decode": run_decode, "paged": run_paged, "sweep": run_sweep,
-              "copy": run_copy, "prefill": run_prefill}.get(args.workload)
+              "copy": run_copy, "prefill": run_prefill,
+              "prefill_bwd": run_prefill_bwd}.get(args.workload)
     if runner is None:
         raise SystemExit(f"workload {args.workload} is not available")
     rec = runner(args, torch, plx)
