@@ -17,6 +17,12 @@ the softmax denominator, ``r``, ``o_SA``) and ``prefill_backward`` the
 gradients of ``sum(dout * out)`` with respect to q, rho, k and v, by the chain
 rule through the forward steps.
 
+Local linear attention's solved probe (same page, sections 1.2-1.3 and the
+taxonomy of section 2.1): ``solved_probe`` gives, per decode row,
+rho* = (S_KK + lam I)^{-1} (kbar - q) by a direct fp64 solve, and
+``lla_decode`` the Parallax output with that probe, which is the intercept of
+the softmax-weighted, ridge-regularised local linear fit v ~ b + W (k - q).
+
 Array conventions (numpy):
   * float64 / float32 arrays are read as such;
   * uint16 arrays are raw bfloat16 bit patterns (widened exactly).
@@ -273,3 +279,77 @@ def prefill_backward(q, rho, k, v, dout, scale, *, rows=None, window=0, threads=
     if rc != 0:
         raise ValueError("oracle: orc_prefill_backward rejected its arguments")
     return dq, drho, dkk, dvv
+
+
+def _row_keys(k, b, hk, L, block_table, window):
+    """Keys [n, dk] (float64) of decode row (b, kv head hk) over its L cached
+    tokens, restricted to the last `window` of them when window >= 1."""
+    j0 = max(0, L - window) if window > 0 else 0
+    js = np.arange(j0, L)
+    if block_table is None:
+        rows = k[b, hk, js]
+    else:
+        P = k.shape[2]
+        rows = k[block_table[b, js // P], hk, js % P]
+    return _as_f64(rows)
+
+
+def _as_f64(a):
+    a = np.asarray(a)
+    if a.dtype == np.uint16:  # raw bf16 bits
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def solved_probe(q, k, scale, lam, *, seq_lens=None, block_table=None, window=0):
+    """LLA's solved probe for every decode row (b, h):
+    rho* = (S_KK + lam I)^{-1} (kbar - q), where p = softmax(scale K q) over
+    the row's keys, kbar = sum p_j k_j and S_KK = sum p_j (k_j - kbar)(k_j -
+    kbar)^T.  A row with no keys gets rho* = 0.
+
+    The pages state the per-token system S x = mu with a regulariser lam
+    (page "Parallax: Parameterized Local Linear Attention ...", section 1.2)
+    and the optimal probe rho* = S^{-1} mu (section 1.3) without defining mu;
+    mu = kbar - q and S = S_KK + lam I is the reading under which the
+    softmax-weighted fit v ~ b + W (k - q) with ridge penalty lam ||W||^2 has
+    intercept o_SA - S_KV rho*.  Solved directly (numpy.linalg.solve) in fp64.
+
+    q [B, Hq, dk]; k contiguous [B, Hkv, Lcap, dk] or paged [NB, Hkv, P, dk]
+    with block_table [B, max_blocks]; seq_lens [B] (default: all Lcap).
+    Returns rho* [B, Hq, dk] float64.
+    """
+    qd = _as_f64(q)
+    B, Hq, dk = qd.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if seq_lens is None:
+        if block_table is not None:
+            raise ValueError("paged keys need seq_lens")
+        seq_lens = np.full(B, k.shape[2], dtype=np.int64)
+    out = np.zeros((B, Hq, dk), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for hk in range(Hkv):
+            K = _row_keys(k, b, hk, L, block_table, window)
+            if K.shape[0] == 0:
+                continue
+            for h in range(hk * G, (hk + 1) * G):
+                s = scale * (K @ qd[b, h])
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                kbar = p @ K
+                Kc = K - kbar
+                S_KK = (Kc * p[:, None]).T @ Kc
+                out[b, h] = np.linalg.solve(S_KK + lam * np.eye(dk), kbar - qd[b, h])
+    return out
+
+
+def lla_decode(q, k, v, scale, lam, *, seq_lens=None, block_table=None, window=0,
+               threads=None):
+    """Decode with LLA's solved probe: (out, rho*), out = o_SA - S_KV rho*
+    (the Parallax output with the solved probe), both float64."""
+    rho = solved_probe(q, k, scale, lam, seq_lens=seq_lens, block_table=block_table,
+                       window=window)
+    out = decode(q, rho, k, v, scale, seq_lens=seq_lens, block_table=block_table,
+                 window=window, threads=threads)
+    return out, rho
