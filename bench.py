@@ -17,7 +17,8 @@ this GPU, and `frac_of_read_stream` = value / that rate.
 
 Prints ONE JSON line.  Other workloads: --workload paged (256 sequences, ctx
 U[128, 32768], 16-token pages), prefill (batch 4, seq 8192, 16/8 heads),
-prefill_bwd (the backward pass of that prefill), sweep (batch x ctx grid),
+prefill_bwd (the backward pass of that prefill), lla (decode with local
+linear attention's solved probe), sweep (batch x ctx grid),
 copy (a plain device copy used to calibrate the HBM byte counters).
 """
 from __future__ import annotations
@@ -220,6 +221,78 @@ def run_decode(args, torch, plx):
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_lla(args, torch, plx):
+    """Decode with LLA's solved probe: per step, `--lla-iters` conjugate-
+    gradient sweeps plus the kbar sweep and the final Parallax sweep over the
+    same cache -- the per-token solve the Parallax page contrasts with its one
+    sweep.  Reports the KV bytes all sweeps stream per second, and the same
+    cache's single-sweep Parallax decode time beside it."""
+    import numpy as np
+    import oracle
+    from parallax_local_linear_decode_amd.workloads import decode_inputs, host_array
+    B, Hq, Hkv, d, L = args.batch, 16, 8, 128, args.ctx
+    lam, iters = args.lla_lambda, args.lla_iters
+    dev = torch.device("cuda:0")
+    kv_bytes = B * Hkv * L * d * 2 * 2
+    n_bufs = max(1, math.ceil(args.cold_bytes / kv_bytes))
+    sets = [decode_inputs(B, Hq, Hkv, d, L, seed=i, device=dev) for i in range(n_bufs)]
+    outs = [plx.parallax_decode_lla(s.q, s.k, s.v, lam=lam, iterations=iters, scale=s.scale)
+            for s in sets[:1]]
+    torch.cuda.synchronize()
+    out, rho, resid = outs[0]
+    # parity of copy 0 against the oracle's direct solve (sequences 0 and B-1)
+    idx = [0, B - 1]
+    ref_out, ref_rho = oracle.lla_decode(host_array(sets[0].q[idx]), host_array(sets[0].k[idx]),
+                                         host_array(sets[0].v[idx]), sets[0].scale, lam)
+    gate(rho[idx].double().cpu().numpy(), ref_rho, 1e-3, 1e-3)
+    gate(out[idx].double().cpu().numpy(), ref_out, 1e-3, 1e-3)
+    cpu = None
+    if args.cpu_baseline:
+        hq, hk, hv = (host_array(t) for t in (sets[0].q, sets[0].k, sets[0].v))
+        t0 = time.perf_counter()
+        oracle.lla_decode(hq, hk, hv, sets[0].scale, lam)
+        secs = time.perf_counter() - t0
+        cpu = {"value": B / secs, "unit": "tokens/s", "cores": oracle.default_threads(),
+               "kind": "oracle", "seconds_per_step": secs,
+               "sample": "the full workload once: numpy fp64 direct solves of the probe, then the "
+                         "C oracle's decode"}
+    ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+    res = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(3)]
+    rsd = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        s = sets[i]
+        plx.parallax_decode_lla(s.q, s.k, s.v, lam=lam, iterations=iters, scale=s.scale,
+                                out=res[0], rho_out=res[1], resid=rsd, workspace=ws)
+
+    secs = time_launches(torch, launch, n_bufs, args.steps, args.warmup)
+    per = secs / args.steps
+    zero = torch.zeros((B, Hq, d), dtype=torch.float32, device=dev)
+    single = time_launches(torch, lambda i: plx.parallax_decode(
+        sets[i].q, zero, sets[i].k, sets[i].v, scale=sets[i].scale, out=res[2]),
+        n_bufs, args.steps, args.warmup) / args.steps
+    sweeps = iters + 2
+    nbytes = sweeps * decode_bytes(B, Hq, Hkv, d, [L] * B)
+    gbps = nbytes / per / 1e9
+    return {
+        "metric": "LLA solved-probe decode: KV GB/s over all sweeps (% of HBM peak)",
+        "value": round(gbps, 2), "unit": "GB/s", "ms_per_step": per * 1e3, "dtype": DECODE_DTYPE,
+        "config": {"workload": f"LLA decode: batch {B}, 16 query / 8 KV heads, d 128, ctx {L}, "
+                               f"bf16 KV cache, lambda {lam}, {iters} CG iterations "
+                               f"({sweeps} sweeps per step)",
+                   "batch": B, "ctx": L, "lambda": lam, "iterations": iters,
+                   "sweeps_per_step": sweeps, "cold_copies": n_bufs},
+        "tokens_per_s": B / per,
+        "max_rel_residual": float(resid.max().item()),
+        "parallax_ms_per_step": single * 1e3,
+        "lla_over_parallax_time": round(per / single, 2),
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
         "cpu_baseline": cpu,
     }
 
@@ -504,12 +577,14 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "paged", "prefill", "prefill_bwd", "sweep", "copy"])
+                    choices=["decode", "paged", "prefill", "prefill_bwd", "lla", "sweep", "copy"])
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--ctx", type=int, default=4096)
     ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
     ap.add_argument("--window", type=int, default=0,
                     help="local window for decode / prefill (0 = full attention)")
+    ap.add_argument("--lla-lambda", type=float, default=0.5, help="LLA ridge term (workload lla)")
+    ap.add_argument("--lla-iters", type=int, default=16, help="LLA CG iterations (workload lla)")
     ap.add_argument("--cold-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
@@ -529,7 +604,7 @@ def main():
     plx.load_library()
     runner = {"decode": run_decode, "paged": run_paged, "sweep": run_sweep,
               "copy": run_copy, "prefill": run_prefill,
-              "prefill_bwd": run_prefill_bwd}.get(args.workload)
+              "prefill_bwd": run_prefill_bwd, "lla": run_lla}.get(args.workload)
     if runner is None:
         raise SystemExit(f"workload {args.workload} is not available")
     rec = runner(args, torch, plx)
@@ -539,7 +614,8 @@ def main():
             "dtype": rec["dtype"], "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1^2) rho)",
             "config": rec["config"]}
     for k in ("pct_hbm_peak", "tokens_per_s", "kv_tokens_per_s", "warm_cache_gbps",
-              "read_stream", "frac_of_read_stream", "mfma_util"):
+              "read_stream", "frac_of_read_stream", "mfma_util", "max_rel_residual",
+              "parallax_ms_per_step", "lla_over_parallax_time"):
         if k in rec:
             line[k] = rec[k]
     line["roofline"] = rec["roofline"]

@@ -140,6 +140,46 @@ parallax_status_t parallax_decode_workspace_size(const parallax_decode_args_t *a
 parallax_status_t parallax_decode(const parallax_decode_args_t *args, void *workspace,
                                   size_t workspace_bytes, void *hip_stream);
 
+/* --------------------------------------------- LLA solved-probe decode --- */
+/*
+ * Decode with local linear attention's solved probe instead of a given rho
+ * (page "Parallax: Parameterized Local Linear Attention Gives Transformers a
+ * 'Second Eye'": section 1.2 -- each token solves a regularised system
+ * S x = mu by conjugate gradients, every iteration one sweep over the KV
+ * cache; section 1.3 -- rho* = S^{-1} mu is the optimal probe, and Parallax
+ * with that probe is LLA).  For each decode row, with p the softmax weights
+ * over its keys (window included):
+ *     rho* = (S_KK + lambda I)^{-1} (kbar - q),
+ *     S_KK = sum_j p_j (k_j - kbar)(k_j - kbar)^T,  kbar = sum_j p_j k_j,
+ * approximated by `iterations` conjugate-gradient steps from x = 0; then
+ * out = o_SA - S_KV rho* exactly as parallax_decode computes it.  (mu =
+ * kbar - q makes out the intercept of the softmax-weighted local linear fit
+ * v ~ b + W (k - q) with penalty lambda |W|^2.)
+ * The CG matrix-vector product is the decode pass with the keys as values:
+ * S_KK y = kbar - o(V = K, rho = y); one call runs iterations + 2 decode
+ * passes and no host synchronisation.  A row without keys gets rho* = 0.
+ * `decode` is used as for parallax_decode except that decode->rho is ignored
+ * (may be NULL).  rho_out fp32 [B, Hq, d] contiguous, may be NULL; resid fp32
+ * [B, Hq], may be NULL: |mu - (S_KK + lambda I) x| / |mu| after the last step,
+ * as the recurrence carries it.  lambda must be finite and > 0; iterations in
+ * [1, 4096] (else PARALLAX_ERR_INVALID_ARG).  Workspace:
+ * parallax_decode_lla_workspace_size bytes, 16-byte aligned.
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(parallax_lla_args_t) */
+    float lambda;
+    int32_t iterations;
+    float *rho_out;
+    float *resid;
+} parallax_lla_args_t;
+
+parallax_status_t parallax_decode_lla_workspace_size(const parallax_decode_args_t *decode,
+                                                     const parallax_lla_args_t *lla,
+                                                     size_t *bytes);
+parallax_status_t parallax_decode_lla(const parallax_decode_args_t *decode,
+                                      const parallax_lla_args_t *lla, void *workspace,
+                                      size_t workspace_bytes, void *hip_stream);
+
 /* ------------------------------------------------------------ prefill --- */
 /*
  * Causal prefill: row i of (b, h) attends to keys 0..i of KV head

@@ -69,6 +69,12 @@ class PrefillArgs(ctypes.Structure):
     ]
 
 
+class LlaArgs(ctypes.Structure):
+    """Mirror of parallax_lla_args_t."""
+    _fields_ = [("struct_size", _u32), ("lam", _f32), ("iterations", _i32), ("rho_out", _vp),
+                ("resid", _vp)]
+
+
 class PrefillBackwardArgs(ctypes.Structure):
     """Mirror of parallax_prefill_backward_args_t."""
     _fields_ = [
@@ -113,6 +119,12 @@ def load_library():
     lib.parallax_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
     lib.parallax_prefill.restype = ctypes.c_int
     lib.parallax_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
+    lib.parallax_decode_lla_workspace_size.restype = ctypes.c_int
+    lib.parallax_decode_lla_workspace_size.argtypes = [
+        ctypes.POINTER(DecodeArgs), ctypes.POINTER(LlaArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.parallax_decode_lla.restype = ctypes.c_int
+    lib.parallax_decode_lla.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(LlaArgs), _vp,
+                                        ctypes.c_size_t, _vp]
     lib.parallax_prefill_backward_workspace_size.restype = ctypes.c_int
     lib.parallax_prefill_backward_workspace_size.argtypes = [
         ctypes.POINTER(PrefillBackwardArgs), ctypes.POINTER(ctypes.c_size_t)]
@@ -267,6 +279,47 @@ def parallax_decode(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None
     return out
 
 
+def parallax_decode_lla(q, k, v, *, lam, iterations, scale=None, seq_lens=None,
+                        block_table=None, max_seq_len=None, out=None, rho_out=None, resid=None,
+                        workspace=None, split_tokens=0, window=0, stream=None):
+    """Decode with local linear attention's solved probe
+    rho* = (S_KK + lam I)^{-1} (kbar - q), by `iterations` conjugate-gradient
+    steps, each one decode sweep with the keys as values.  Cache arguments as
+    parallax_decode.  Returns (out, rho_out, resid): out float32 [B, Hq, d]
+    (the Parallax output with rho*), rho_out float32 [B, Hq, d], resid float32
+    [B, Hq] (|residual| / |kbar - q| after the last step)."""
+    lib = load_library()
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if rho_out is None:
+        rho_out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if resid is None:
+        resid = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if not (rho_out.is_contiguous() and resid.is_contiguous()):
+        raise ValueError("rho_out and resid must be contiguous")
+    a = _decode_args(q, q, k, v, out, scale, seq_lens, block_table, max_seq_len, split_tokens,
+                     window)
+    a.rho = None
+    la = LlaArgs()
+    la.struct_size = ctypes.sizeof(LlaArgs)
+    la.lam, la.iterations = float(lam), int(iterations)
+    la.rho_out, la.resid = _ptr(rho_out), _ptr(resid)
+    nbytes = ctypes.c_size_t(0)
+    st = lib.parallax_decode_lla_workspace_size(ctypes.byref(a), ctypes.byref(la),
+                                                ctypes.byref(nbytes))
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    s = _stream_handle(q, stream)
+    if workspace is None:
+        workspace = _workspace(q.device, s, nbytes.value)
+    st = lib.parallax_decode_lla(ctypes.byref(a), ctypes.byref(la), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), s)
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    return out, rho_out, resid
+
+
 def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, window=0,
                      stream=None, return_stats=False):
     """Causal Parallax prefill.  q, rho bf16 [B, S, Hq, d]; k, v bf16
@@ -377,7 +430,7 @@ def parallax_prefill_backward(q, rho, k, v, dout, out, o_sa, lse, rmean, *, scal
 
 __all__ = [
     "parallax_decode", "parallax_decode_workspace_size", "parallax_prefill",
-    "parallax_prefill_backward", "PrefillBackwardArgs",
+    "parallax_prefill_backward", "PrefillBackwardArgs", "parallax_decode_lla", "LlaArgs",
     "parallax_status_string", "parallax_last_error", "parallax_abi_version", "load_library",
     "DecodeArgs", "PrefillArgs", "ParallaxError",
 ]

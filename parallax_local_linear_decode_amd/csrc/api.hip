@@ -238,6 +238,80 @@ size_t prefill_backward_workspace(const parallax_prefill_backward_args_t *a) {
     return (size_t)a->batch * a->num_q_heads * a->seq_len * 16;  // one float4 per query row
 }
 
+plx::DecodeParams decode_params(const parallax_decode_args_t *a, const DecodePlan &pl,
+                                void *workspace) {
+    plx::DecodeParams p;
+    p.q = a->q;
+    p.rho = a->rho;
+    p.out = a->out;
+    p.q_sb = a->q_stride_b;
+    p.q_sh = a->q_stride_h;
+    p.rho_sb = a->rho_stride_b;
+    p.rho_sh = a->rho_stride_h;
+    p.out_sb = a->out_stride_b;
+    p.out_sh = a->out_stride_h;
+    p.k = a->k;
+    p.v = a->v;
+    p.k_s0 = a->k_stride_0;
+    p.k_sh = a->k_stride_h;
+    p.k_st = a->k_stride_t;
+    p.v_s0 = a->v_stride_0;
+    p.v_sh = a->v_stride_h;
+    p.v_st = a->v_stride_t;
+    p.seq_lens = a->seq_lens;
+    p.block_table = a->block_table;
+    p.max_seq_len = a->max_seq_len;
+    p.max_blocks = pl.paged ? a->max_blocks_per_seq : 0;
+    p.num_kv_heads = a->num_kv_heads;
+    p.split = pl.split;
+    p.nsplit = pl.nsplit;
+    p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
+    p.partials = pl.workspace_bytes > 0 ? static_cast<float *>(workspace) : nullptr;
+    p.window = a->window;
+    return p;
+}
+
+// Solved-probe decode: the decode plan of the user's arguments (rho is not
+// read), then the conjugate-gradient vectors kbar, o_k, x, r, dir ([B*Hq][d]
+// each) and [B*Hq][2] squared norms after the decode partials.
+struct LlaPlan {
+    DecodePlan dplan;
+    size_t decode_bytes;
+    size_t total_bytes;
+};
+
+constexpr int kLlaMaxIterations = 4096;
+
+parallax_status_t plan_lla(const parallax_decode_args_t *dec, const parallax_lla_args_t *lla,
+                           LlaPlan *lp) {
+    if (dec == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "lla: decode args is NULL");
+    if (lla == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "lla: lla args is NULL");
+    if (lla->struct_size != sizeof(parallax_lla_args_t))
+        return fail(PARALLAX_ERR_INVALID_ARG, "lla: struct_size %u, expected %zu", lla->struct_size,
+                    sizeof(parallax_lla_args_t));
+    if (!isfinite(lla->lambda) || !(lla->lambda > 0.0f))
+        return fail(PARALLAX_ERR_INVALID_ARG, "lla: lambda must be finite and > 0");
+    if (lla->iterations < 1 || lla->iterations > kLlaMaxIterations)
+        return fail(PARALLAX_ERR_INVALID_ARG, "lla: iterations must be in [1, %d]",
+                    kLlaMaxIterations);
+    if (!aligned16(lla->rho_out))
+        return fail(PARALLAX_ERR_UNSUPPORTED, "lla: rho_out must be 16-byte aligned");
+    if (dec->struct_size != sizeof(parallax_decode_args_t))  // before reading the rest
+        return fail(PARALLAX_ERR_INVALID_ARG, "decode: struct_size %u, expected %zu",
+                    dec->struct_size, sizeof(parallax_decode_args_t));
+    // rho is not read: validate the rest with q standing in for it
+    parallax_decode_args_t probe = *dec;
+    probe.rho = dec->q;
+    probe.rho_stride_b = dec->q_stride_b;
+    probe.rho_stride_h = dec->q_stride_h;
+    parallax_status_t s = plan_decode(&probe, &lp->dplan);
+    if (s != PARALLAX_OK) return s;
+    const size_t n = (size_t)dec->batch * dec->num_q_heads * dec->head_dim;
+    lp->decode_bytes = (size_t)round_up((int64_t)lp->dplan.workspace_bytes, 256);
+    lp->total_bytes = lp->decode_bytes + (5 * n + 2 * (size_t)dec->batch * dec->num_q_heads) * 4;
+    return PARALLAX_OK;
+}
+
 parallax_status_t hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return PARALLAX_OK;
     return fail(PARALLAX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -282,37 +356,90 @@ PLX_EXPORT parallax_status_t parallax_decode(const parallax_decode_args_t *a, vo
         if (!aligned16(workspace))
             return fail(PARALLAX_ERR_WORKSPACE, "decode: workspace must be 16-byte aligned");
     }
-    plx::DecodeParams p;
-    p.q = a->q;
-    p.rho = a->rho;
-    p.out = a->out;
-    p.q_sb = a->q_stride_b;
-    p.q_sh = a->q_stride_h;
-    p.rho_sb = a->rho_stride_b;
-    p.rho_sh = a->rho_stride_h;
-    p.out_sb = a->out_stride_b;
-    p.out_sh = a->out_stride_h;
-    p.k = a->k;
-    p.v = a->v;
-    p.k_s0 = a->k_stride_0;
-    p.k_sh = a->k_stride_h;
-    p.k_st = a->k_stride_t;
-    p.v_s0 = a->v_stride_0;
-    p.v_sh = a->v_stride_h;
-    p.v_st = a->v_stride_t;
-    p.seq_lens = a->seq_lens;
-    p.block_table = a->block_table;
-    p.max_seq_len = a->max_seq_len;
-    p.max_blocks = pl.paged ? a->max_blocks_per_seq : 0;
-    p.num_kv_heads = a->num_kv_heads;
-    p.split = pl.split;
-    p.nsplit = pl.nsplit;
-    p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
-    p.partials = pl.workspace_bytes > 0 ? static_cast<float *>(workspace) : nullptr;
-    p.window = a->window;
+    plx::DecodeParams p = decode_params(a, pl, workspace);
     return hip_status(plx::launch_decode(p, a->kv_dtype, a->head_dim, pl.group, pl.paged, a->batch,
                                          static_cast<hipStream_t>(hip_stream)),
                       "decode launch");
+}
+
+PLX_EXPORT parallax_status_t parallax_decode_lla_workspace_size(const parallax_decode_args_t *dec,
+                                                                const parallax_lla_args_t *lla,
+                                                                size_t *bytes) {
+    if (bytes == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "lla: bytes is NULL");
+    LlaPlan lp;
+    parallax_status_t s = plan_lla(dec, lla, &lp);
+    if (s != PARALLAX_OK) return s;
+    *bytes = lp.total_bytes;
+    return PARALLAX_OK;
+}
+
+PLX_EXPORT parallax_status_t parallax_decode_lla(const parallax_decode_args_t *dec,
+                                                 const parallax_lla_args_t *lla, void *workspace,
+                                                 size_t workspace_bytes, void *hip_stream) {
+    LlaPlan lp;
+    parallax_status_t s = plan_lla(dec, lla, &lp);
+    if (s != PARALLAX_OK) return s;
+    if (workspace == nullptr || workspace_bytes < lp.total_bytes)
+        return fail(PARALLAX_ERR_WORKSPACE, "lla: workspace of %zu bytes needed, %zu given",
+                    lp.total_bytes, workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned16(workspace))
+        return fail(PARALLAX_ERR_WORKSPACE, "lla: workspace must be 16-byte aligned");
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const int64_t n = (int64_t)dec->batch * dec->num_q_heads * dec->head_dim;
+    float *vec = reinterpret_cast<float *>(ws + lp.decode_bytes);
+    float *kbar = vec, *ok = vec + n, *x = vec + 2 * n, *r = vec + 3 * n, *dir = vec + 4 * n;
+    float *rs = vec + 5 * n;
+
+    // the user's decode with rho = x, and the CG sweep: keys as values, rho = dir
+    plx::DecodeParams fin = decode_params(dec, lp.dplan, workspace);
+    fin.rho = x;
+    fin.rho_sb = (int64_t)dec->num_q_heads * dec->head_dim;
+    fin.rho_sh = dec->head_dim;
+    plx::DecodeParams sweep = fin;
+    sweep.v = sweep.k;
+    sweep.v_s0 = sweep.k_s0;
+    sweep.v_sh = sweep.k_sh;
+    sweep.v_st = sweep.k_st;
+    sweep.rho = dir;
+    sweep.out = kbar;
+    sweep.out_sb = fin.rho_sb;
+    sweep.out_sh = fin.rho_sh;
+
+    plx::LlaParams lpar;
+    lpar.q = dec->q;
+    lpar.q_sb = dec->q_stride_b;
+    lpar.q_sh = dec->q_stride_h;
+    lpar.kbar = kbar;
+    lpar.ok = ok;
+    lpar.x = x;
+    lpar.r = r;
+    lpar.dir = dir;
+    lpar.rs = rs;
+    lpar.seq_lens = dec->seq_lens;
+    lpar.max_seq_len = dec->max_seq_len;
+    lpar.rho_out = lla->rho_out;
+    lpar.resid = lla->resid;
+    lpar.batch = dec->batch;
+    lpar.num_q_heads = dec->num_q_heads;
+    lpar.d = dec->head_dim;
+    lpar.lambda = lla->lambda;
+
+    auto run_decode = [&](const plx::DecodeParams &dp) {
+        return plx::launch_decode(dp, dec->kv_dtype, dec->head_dim, lp.dplan.group, lp.dplan.paged,
+                                  dec->batch, stream);
+    };
+    hipError_t e = plx::launch_lla_zero(dir, n, stream);  // rho = 0: the sweep gives kbar
+    if (e == hipSuccess) e = run_decode(sweep);
+    if (e == hipSuccess) e = plx::launch_lla_init(lpar, stream);
+    sweep.out = ok;
+    for (int it = 0; it < lla->iterations && e == hipSuccess; ++it) {
+        e = run_decode(sweep);
+        if (e == hipSuccess) e = plx::launch_lla_step(lpar, stream);
+    }
+    if (e == hipSuccess) e = run_decode(fin);
+    if (e == hipSuccess) e = plx::launch_lla_finish(lpar, stream);
+    return hip_status(e, "lla launch");
 }
 
 PLX_EXPORT parallax_status_t parallax_prefill(const parallax_prefill_args_t *a, void *hip_stream) {

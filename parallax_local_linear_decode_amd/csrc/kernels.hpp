@@ -1,5 +1,5 @@
 // Internal launch parameters shared by the host dispatcher (api.hip) and the
-// gfx950 kernels (decode.hip, prefill.hip, prefill_bwd.hip).  Not part of the public ABI.
+// gfx950 kernels (decode.hip, prefill.hip, prefill_bwd.hip, lla.hip).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -89,11 +89,32 @@ struct PrefillBwdParams {
     int32_t window;
 };
 
+// Conjugate-gradient state of local linear attention's solved probe, one
+// row per (batch, query head), vectors contiguous [B * Hq][d].
+struct LlaParams {
+    const float *q;
+    int64_t q_sb, q_sh;
+    const float *kbar;  // o(V = K, rho = 0)
+    const float *ok;    // o(V = K, rho = dir) of the current sweep
+    float *x, *r, *dir;
+    float *rs;          // [B * Hq][2]: |r|^2 and |mu|^2
+    const int32_t *seq_lens;  // may be null: every row has max_seq_len tokens
+    int32_t max_seq_len;
+    float *rho_out;     // may be null
+    float *resid;       // may be null
+    int32_t batch, num_q_heads, d;
+    float lambda;
+};
+
 // Launchers (defined next to their kernels).  They return the HIP status of
 // the launch.
 hipError_t launch_decode(const DecodeParams &p, int kv_dtype, int d, int group, bool paged,
                          int batch, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream);
 hipError_t launch_prefill_backward(const PrefillBwdParams &p, int d, hipStream_t stream);
+hipError_t launch_lla_zero(float *a, int64_t n, hipStream_t stream);
+hipError_t launch_lla_init(const LlaParams &p, hipStream_t stream);
+hipError_t launch_lla_step(const LlaParams &p, hipStream_t stream);
+hipError_t launch_lla_finish(const LlaParams &p, hipStream_t stream);
 
 }  // namespace plx

@@ -24,6 +24,7 @@ def test_exports_every_declared_function(lib):
     names = set(re.findall(r"\b(parallax_[a-z_]+)\s*\(", text))
     assert {"parallax_decode", "parallax_prefill", "parallax_decode_workspace_size",
             "parallax_prefill_backward", "parallax_prefill_backward_workspace_size",
+            "parallax_decode_lla", "parallax_decode_lla_workspace_size",
             "parallax_status_string", "parallax_last_error", "parallax_abi_version"} <= names
     for n in sorted(names):
         assert hasattr(lib, n), f"{n} is declared but not exported"
@@ -275,3 +276,70 @@ def test_window_shrinks_the_split_plan(lib):
     assert st == plx.PARALLAX_OK and n_win == 0
     full.window = 40000  # at least the cache: same plan as full attention
     assert ws_size(lib, full) == (plx.PARALLAX_OK, n_full)
+
+
+def good_lla(**over):
+    la = plx.LlaArgs()
+    la.struct_size = ctypes.sizeof(plx.LlaArgs)
+    la.lam, la.iterations = 0.5, 16
+    la.rho_out = la.resid = FAKE
+    for k, v in over.items():
+        setattr(la, k, v)
+    return la
+
+
+def lla_size(lib, a, la):
+    n = ctypes.c_size_t(7)
+    st = lib.parallax_decode_lla_workspace_size(ctypes.byref(a), ctypes.byref(la), ctypes.byref(n))
+    return st, n.value
+
+
+def test_lla_workspace_size(lib):
+    """The decode partials (rounded up to 256 bytes), then five [B, Hq, d]
+    conjugate-gradient vectors and two squared norms per row; rho is not
+    read, so it may be NULL."""
+    a = good_decode(rho=None)
+    st, dec = ws_size(lib, good_decode())
+    assert st == plx.PARALLAX_OK
+    st, n = lla_size(lib, a, good_lla())
+    assert st == plx.PARALLAX_OK
+    assert n == (dec + 255) // 256 * 256 + (5 * 8 * 16 * 128 + 2 * 8 * 16) * 4
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(struct_size=16), INVALID, "struct_size"),
+    (dict(lam=0.0), INVALID, "lambda"),
+    (dict(lam=-1.0), INVALID, "lambda"),
+    (dict(lam=float("nan")), INVALID, "lambda"),
+    (dict(iterations=0), INVALID, "iterations"),
+    (dict(iterations=5000), INVALID, "iterations"),
+    (dict(rho_out=FAKE + 4), UNSUPP, "aligned"),
+])
+def test_lla_rejects(lib, over, status, needle):
+    a = good_decode(rho=None)
+    la = good_lla(**over)
+    assert lla_size(lib, a, la)[0] == status
+    assert needle in plx.parallax_last_error()
+    assert lib.parallax_decode_lla(ctypes.byref(a), ctypes.byref(la), FAKE, 1 << 30, None) == status
+
+
+def test_lla_checks_the_decode_arguments(lib):
+    la = good_lla()
+    assert lla_size(lib, good_decode(num_kv_heads=3), la)[0] == INVALID
+    assert lla_size(lib, good_decode(head_dim=96), la)[0] == UNSUPP
+    assert lla_size(lib, good_decode(struct_size=8), la)[0] == INVALID
+    assert "struct_size" in plx.parallax_last_error()
+    assert lib.parallax_decode_lla(None, ctypes.byref(la), FAKE, 1 << 30, None) == INVALID
+    assert lib.parallax_decode_lla(ctypes.byref(good_decode()), None, FAKE, 1 << 30, None) == \
+        INVALID
+
+
+def test_lla_workspace_checks(lib):
+    a, la = good_decode(rho=None), good_lla()
+    _, need = lla_size(lib, a, la)
+    assert lib.parallax_decode_lla(ctypes.byref(a), ctypes.byref(la), FAKE, need - 4, None) == \
+        plx.PARALLAX_ERR_WORKSPACE
+    assert lib.parallax_decode_lla(ctypes.byref(a), ctypes.byref(la), None, need, None) == \
+        plx.PARALLAX_ERR_WORKSPACE
+    assert lib.parallax_decode_lla(ctypes.byref(a), ctypes.byref(la), FAKE + 8, need, None) == \
+        plx.PARALLAX_ERR_WORKSPACE
