@@ -23,6 +23,11 @@ rho* = (S_KK + lam I)^{-1} (kbar - q) by a direct fp64 solve, and
 ``lla_decode`` the Parallax output with that probe, which is the intercept of
 the softmax-weighted, ridge-regularised local linear fit v ~ b + W (k - q).
 
+The probe projection (same page, section 1.3: rho = W_R x, a learned linear
+map of the layer input, computed beside the query projection q = W_Q x):
+``qr_projection`` gives both for a batch of token rows, as fp64 matrix
+products.
+
 Array conventions (numpy):
   * float64 / float32 arrays are read as such;
   * uint16 arrays are raw bfloat16 bit patterns (widened exactly).
@@ -353,3 +358,15 @@ def lla_decode(q, k, v, scale, lam, *, seq_lens=None, block_table=None, window=0
     out = decode(q, rho, k, v, scale, seq_lens=seq_lens, block_table=block_table,
                  window=window, threads=threads)
     return out, rho
+
+
+def qr_projection(x, w_q, w_r):
+    """q = W_Q x and rho = W_R x for every token row of x.
+
+    x [T, D]; w_q, w_r [N, D] (N = heads * head_dim).  Returns q, rho [T, N]
+    float64: plain fp64 matrix products of the exactly widened inputs.
+    """
+    xd, wq, wr = _as_f64(x), _as_f64(w_q), _as_f64(w_r)
+    if xd.ndim != 2 or wq.shape != wr.shape or wq.shape[1] != xd.shape[1]:
+        raise ValueError("x must be [T, D] and w_q, w_r [N, D]")
+    return xd @ wq.T, xd @ wr.T

@@ -552,3 +552,35 @@ def test_window_mutants_are_caught():
                                     0.45)
                 worst = max(worst, rel_err(got, want))
         assert worst > 1e-6, name
+
+
+# ------------------------------------------------------ probe projection ---
+# rho = W_R x beside q = W_Q x (section 1.3); W_R = 0 gives rho = 0, which
+# the page notes turns Parallax back into plain softmax attention.
+
+def test_qr_projection_hand_example():
+    x = np.array([[1.0, 2.0], [0.5, -1.0]])
+    w_q = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 3.0]])
+    w_r = np.array([[1.0, 1.0], [-1.0, 0.0], [0.0, 0.0]])
+    q, rho = oracle.qr_projection(x, w_q, w_r)
+    assert np.array_equal(q, [[1.0, 2.0, 8.0], [0.5, -1.0, -2.0]])
+    assert np.array_equal(rho, [[3.0, -1.0, 0.0], [-0.5, -0.5, 0.0]])
+
+
+def test_qr_projection_brute_force_and_zero_probe():
+    rng = np.random.default_rng(60)
+    x, w_q, w_r = (rng.standard_normal(s) for s in ((5, 7), (4, 7), (4, 7)))
+    q, rho = oracle.qr_projection(x, w_q, w_r)
+    for t in range(5):
+        for n in range(4):
+            assert abs(q[t, n] - sum(w_q[n, k] * x[t, k] for k in range(7))) < 1e-12
+            assert abs(rho[t, n] - sum(w_r[n, k] * x[t, k] for k in range(7))) < 1e-12
+    assert np.all(oracle.qr_projection(x, w_q, np.zeros_like(w_r))[1] == 0)
+
+
+def test_qr_projection_reads_bf16_bits_exactly():
+    vals = np.array([1.0, -2.5, 0.15625, 3.0e-3], dtype=np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)  # exactly representable in bf16
+    widened = (bits.astype(np.uint32) << 16).view(np.float32)
+    q, _ = oracle.qr_projection(bits[None, :], bits[None, :], bits[None, :])
+    assert q[0, 0] == float(np.dot(widened.astype(np.float64), widened.astype(np.float64)))
