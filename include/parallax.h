@@ -180,6 +180,43 @@ parallax_status_t parallax_decode_lla(const parallax_decode_args_t *decode,
                                       const parallax_lla_args_t *lla, void *workspace,
                                       size_t workspace_bytes, void *hip_stream);
 
+/* ------------------------------------------------- probe projection --- */
+/*
+ * The query and probe projections of T token rows in one launch:
+ *     q[t] = W_Q x[t],   rho[t] = W_R x[t]
+ * (page "Parallax: Parameterized Local Linear Attention Gives Transformers a
+ * 'Second Eye'", section 1.3: the probe is a learned linear projection of the
+ * layer input; W_R = 0 gives plain softmax attention).  x bf16 [T, D];
+ * w_q, w_r bf16 [Hq * head_dim, D] (row n = head n / head_dim, element
+ * n % head_dim) with row stride w_stride_n; q and rho [T, Hq, head_dim] of
+ * out_dtype (PARALLAX_F32 for parallax_decode, PARALLAX_BF16 for
+ * parallax_prefill; a [B, S] token grid is T = B * S rows when its token
+ * stride is uniform).  bf16 matrix cores, fp32 accumulation, one rounding
+ * to out_dtype.  D must be a multiple of 256, head_dim 64 or 128, T in
+ * [1, 4194304]; pointers 16-byte aligned, strides multiples of 16 bytes
+ * (else PARALLAX_ERR_UNSUPPORTED / INVALID_ARG).
+ */
+typedef struct {
+    uint32_t struct_size; /* = sizeof(parallax_qr_projection_args_t) */
+    int32_t tokens;
+    int32_t model_dim;
+    int32_t num_q_heads;
+    int32_t head_dim;
+    parallax_dtype_t out_dtype;
+    const void *x;
+    int64_t x_stride_t;
+    const void *w_q;
+    const void *w_r;
+    int64_t w_stride_n;
+    void *q;
+    int64_t q_stride_t, q_stride_h;
+    void *rho;
+    int64_t rho_stride_t, rho_stride_h;
+} parallax_qr_projection_args_t;
+
+parallax_status_t parallax_qr_projection(const parallax_qr_projection_args_t *args,
+                                         void *hip_stream);
+
 /* ------------------------------------------------------------ prefill --- */
 /*
  * Causal prefill: row i of (b, h) attends to keys 0..i of KV head

@@ -75,6 +75,17 @@ class LlaArgs(ctypes.Structure):
                 ("resid", _vp)]
 
 
+class ProjectionArgs(ctypes.Structure):
+    """Mirror of parallax_qr_projection_args_t."""
+    _fields_ = [
+        ("struct_size", _u32), ("tokens", _i32), ("model_dim", _i32), ("num_q_heads", _i32),
+        ("head_dim", _i32), ("out_dtype", _i32),
+        ("x", _vp), ("x_stride_t", _i64), ("w_q", _vp), ("w_r", _vp), ("w_stride_n", _i64),
+        ("q", _vp), ("q_stride_t", _i64), ("q_stride_h", _i64),
+        ("rho", _vp), ("rho_stride_t", _i64), ("rho_stride_h", _i64),
+    ]
+
+
 class PrefillBackwardArgs(ctypes.Structure):
     """Mirror of parallax_prefill_backward_args_t."""
     _fields_ = [
@@ -125,6 +136,8 @@ def load_library():
     lib.parallax_decode_lla.restype = ctypes.c_int
     lib.parallax_decode_lla.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(LlaArgs), _vp,
                                         ctypes.c_size_t, _vp]
+    lib.parallax_qr_projection.restype = ctypes.c_int
+    lib.parallax_qr_projection.argtypes = [ctypes.POINTER(ProjectionArgs), _vp]
     lib.parallax_prefill_backward_workspace_size.restype = ctypes.c_int
     lib.parallax_prefill_backward_workspace_size.argtypes = [
         ctypes.POINTER(PrefillBackwardArgs), ctypes.POINTER(ctypes.c_size_t)]
@@ -320,6 +333,46 @@ def parallax_decode_lla(q, k, v, *, lam, iterations, scale=None, seq_lens=None,
     return out, rho_out, resid
 
 
+def parallax_qr_projection(x, w_q, w_r, *, num_q_heads, out_dtype=torch.float32, q=None,
+                           rho=None, stream=None):
+    """q = W_Q x and rho = W_R x for every token row, in one launch.
+
+    x bf16 [T, D]; w_q, w_r bf16 [Hq * d, D].  Returns (q, rho) of out_dtype
+    (float32 for parallax_decode, bfloat16 for parallax_prefill), each
+    [T, Hq, d] -- or written into the given tensors (any strides with a
+    contiguous head dim)."""
+    lib = load_library()
+    for name, t in (("x", x), ("w_q", w_q), ("w_r", w_r)):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a 2-d bfloat16 tensor with contiguous rows")
+    if w_q.shape != w_r.shape or w_q.stride() != w_r.stride() or w_q.shape[1] != x.shape[1]:
+        raise ValueError("w_q and w_r must be [Hq * d, D] with the same strides")
+    T, D = x.shape
+    N = w_q.shape[0]
+    if N % num_q_heads:
+        raise ValueError("w_q rows must be num_q_heads * head_dim")
+    d = N // num_q_heads
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    q = torch.empty((T, num_q_heads, d), dtype=out_dtype, device=x.device) if q is None else q
+    rho = torch.empty_like(q) if rho is None else rho
+    for name, t in (("q", q), ("rho", rho)):
+        if t.dtype != out_dtype or tuple(t.shape) != (T, num_q_heads, d) or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be {out_dtype} [T, Hq, d] with a contiguous head dim")
+    a = ProjectionArgs()
+    a.struct_size = ctypes.sizeof(ProjectionArgs)
+    a.tokens, a.model_dim, a.num_q_heads, a.head_dim = T, D, num_q_heads, d
+    a.out_dtype = PARALLAX_F32 if out_dtype == torch.float32 else PARALLAX_BF16
+    a.x, a.x_stride_t = _ptr(x), x.stride(0)
+    a.w_q, a.w_r, a.w_stride_n = _ptr(w_q), _ptr(w_r), w_q.stride(0)
+    a.q, a.q_stride_t, a.q_stride_h = _ptr(q), q.stride(0), q.stride(1)
+    a.rho, a.rho_stride_t, a.rho_stride_h = _ptr(rho), rho.stride(0), rho.stride(1)
+    st = lib.parallax_qr_projection(ctypes.byref(a), _stream_handle(x, stream))
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    return q, rho
+
+
 def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, window=0,
                      stream=None, return_stats=False):
     """Causal Parallax prefill.  q, rho bf16 [B, S, Hq, d]; k, v bf16
@@ -431,6 +484,7 @@ def parallax_prefill_backward(q, rho, k, v, dout, out, o_sa, lse, rmean, *, scal
 __all__ = [
     "parallax_decode", "parallax_decode_workspace_size", "parallax_prefill",
     "parallax_prefill_backward", "PrefillBackwardArgs", "parallax_decode_lla", "LlaArgs",
+    "parallax_qr_projection", "ProjectionArgs",
     "parallax_status_string", "parallax_last_error", "parallax_abi_version", "load_library",
     "DecodeArgs", "PrefillArgs", "ParallaxError",
 ]

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libparallax.so")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill_bwd.hip", "lla.hip"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill_bwd.hip", "lla.hip", "proj.hip"]
 # A plain read-stream kernel the benchmark times as the HBM reference; its
 # own library, not part of libparallax.
 PROBE_LIB = os.path.join(PKG, "libparallax_probe.so")

@@ -312,6 +312,46 @@ parallax_status_t plan_lla(const parallax_decode_args_t *dec, const parallax_lla
     return PARALLAX_OK;
 }
 
+constexpr int64_t kProjMaxTokens = 4194304;  // grid.y limit at 64 tokens per workgroup
+
+parallax_status_t check_projection(const parallax_qr_projection_args_t *a) {
+    if (a == nullptr) return fail(PARALLAX_ERR_INVALID_ARG, "projection: args is NULL");
+    if (a->struct_size != sizeof(parallax_qr_projection_args_t))
+        return fail(PARALLAX_ERR_INVALID_ARG, "projection: struct_size %u, expected %zu",
+                    a->struct_size, sizeof(parallax_qr_projection_args_t));
+    if (a->tokens < 1 || a->model_dim < 1 || a->num_q_heads < 1 || a->head_dim < 1)
+        return fail(PARALLAX_ERR_INVALID_ARG,
+                    "projection: tokens, model_dim, num_q_heads and head_dim must be >= 1");
+    if (a->out_dtype != PARALLAX_F32 && a->out_dtype != PARALLAX_BF16)
+        return fail(PARALLAX_ERR_INVALID_ARG, "projection: unknown out_dtype %d", a->out_dtype);
+    if (!a->x || !a->w_q || !a->w_r || !a->q || !a->rho)
+        return fail(PARALLAX_ERR_INVALID_ARG, "projection: x, w_q, w_r, q and rho must be non-NULL");
+    if (a->x_stride_t < 0 || a->w_stride_n < 0 || a->q_stride_t < 0 || a->q_stride_h < 0 ||
+        a->rho_stride_t < 0 || a->rho_stride_h < 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "projection: strides must be non-negative");
+    if (a->tokens > kProjMaxTokens)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "projection: tokens %d above %lld", a->tokens,
+                    (long long)kProjMaxTokens);
+    if (a->model_dim % 256 != 0)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "projection: model_dim %d is not a multiple of 256",
+                    a->model_dim);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "projection: head_dim %d (supported: 64, 128)",
+                    a->head_dim);
+    if ((int64_t)a->num_q_heads * a->head_dim * 2 / 16 > 0x7fffffffLL)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "projection: too many output features");
+    const int64_t oes = a->out_dtype == PARALLAX_F32 ? 4 : 2;
+    if (!aligned16(a->x) || !aligned16(a->w_q) || !aligned16(a->w_r) || !aligned16(a->q) ||
+        !aligned16(a->rho))
+        return fail(PARALLAX_ERR_UNSUPPORTED, "projection: every pointer must be 16-byte aligned");
+    if (!bytes16(a->x_stride_t, 2) || !bytes16(a->w_stride_n, 2) || !bytes16(a->q_stride_t, oes) ||
+        !bytes16(a->q_stride_h, oes) || !bytes16(a->rho_stride_t, oes) ||
+        !bytes16(a->rho_stride_h, oes))
+        return fail(PARALLAX_ERR_UNSUPPORTED,
+                    "projection: every stride must span a multiple of 16 bytes");
+    return PARALLAX_OK;
+}
+
 parallax_status_t hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return PARALLAX_OK;
     return fail(PARALLAX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -440,6 +480,31 @@ PLX_EXPORT parallax_status_t parallax_decode_lla(const parallax_decode_args_t *d
     if (e == hipSuccess) e = run_decode(fin);
     if (e == hipSuccess) e = plx::launch_lla_finish(lpar, stream);
     return hip_status(e, "lla launch");
+}
+
+PLX_EXPORT parallax_status_t parallax_qr_projection(const parallax_qr_projection_args_t *a,
+                                                    void *hip_stream) {
+    parallax_status_t s = check_projection(a);
+    if (s != PARALLAX_OK) return s;
+    plx::ProjParams p;
+    p.x = static_cast<const uint16_t *>(a->x);
+    p.x_st = a->x_stride_t;
+    p.w_q = static_cast<const uint16_t *>(a->w_q);
+    p.w_r = static_cast<const uint16_t *>(a->w_r);
+    p.w_sn = a->w_stride_n;
+    p.q = a->q;
+    p.rho = a->rho;
+    p.q_st = a->q_stride_t;
+    p.q_sh = a->q_stride_h;
+    p.r_st = a->rho_stride_t;
+    p.r_sh = a->rho_stride_h;
+    p.tokens = a->tokens;
+    p.model_dim = a->model_dim;
+    p.n = a->num_q_heads * a->head_dim;
+    p.head_dim = a->head_dim;
+    p.out_bf16 = a->out_dtype == PARALLAX_BF16 ? 1 : 0;
+    return hip_status(plx::launch_qr_projection(p, static_cast<hipStream_t>(hip_stream)),
+                      "projection launch");
 }
 
 PLX_EXPORT parallax_status_t parallax_prefill(const parallax_prefill_args_t *a, void *hip_stream) {

@@ -1,5 +1,5 @@
 // Internal launch parameters shared by the host dispatcher (api.hip) and the
-// gfx950 kernels (decode.hip, prefill.hip, prefill_bwd.hip, lla.hip).  Not part of the public ABI.
+// gfx950 kernels (decode.hip, prefill.hip, prefill_bwd.hip, lla.hip, proj.hip).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -106,6 +106,21 @@ struct LlaParams {
     float lambda;
 };
 
+// q = W_Q x and rho = W_R x for T token rows (x [T, D], weights [N, D],
+// outputs [T, Hq, d] with N = Hq * d).
+struct ProjParams {
+    const uint16_t *x;
+    int64_t x_st;
+    const uint16_t *w_q;
+    const uint16_t *w_r;
+    int64_t w_sn;
+    void *q;
+    void *rho;
+    int64_t q_st, q_sh, r_st, r_sh;
+    int32_t tokens, model_dim, n, head_dim;
+    int32_t out_bf16;
+};
+
 // Launchers (defined next to their kernels).  They return the HIP status of
 // the launch.
 hipError_t launch_decode(const DecodeParams &p, int kv_dtype, int d, int group, bool paged,
@@ -116,5 +131,6 @@ hipError_t launch_lla_zero(float *a, int64_t n, hipStream_t stream);
 hipError_t launch_lla_init(const LlaParams &p, hipStream_t stream);
 hipError_t launch_lla_step(const LlaParams &p, hipStream_t stream);
 hipError_t launch_lla_finish(const LlaParams &p, hipStream_t stream);
+hipError_t launch_qr_projection(const ProjParams &p, hipStream_t stream);
 
 }  // namespace plx

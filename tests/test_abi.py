@@ -24,7 +24,7 @@ def test_exports_every_declared_function(lib):
     names = set(re.findall(r"\b(parallax_[a-z_]+)\s*\(", text))
     assert {"parallax_decode", "parallax_prefill", "parallax_decode_workspace_size",
             "parallax_prefill_backward", "parallax_prefill_backward_workspace_size",
-            "parallax_decode_lla", "parallax_decode_lla_workspace_size",
+            "parallax_decode_lla", "parallax_decode_lla_workspace_size", "parallax_qr_projection",
             "parallax_status_string", "parallax_last_error", "parallax_abi_version"} <= names
     for n in sorted(names):
         assert hasattr(lib, n), f"{n} is declared but not exported"
@@ -343,3 +343,37 @@ def test_lla_workspace_checks(lib):
         plx.PARALLAX_ERR_WORKSPACE
     assert lib.parallax_decode_lla(ctypes.byref(a), ctypes.byref(la), FAKE + 8, need, None) == \
         plx.PARALLAX_ERR_WORKSPACE
+
+
+def good_projection(**over):
+    a = plx.ProjectionArgs()
+    a.struct_size = ctypes.sizeof(plx.ProjectionArgs)
+    a.tokens, a.model_dim, a.num_q_heads, a.head_dim = 8, 2048, 16, 128
+    a.out_dtype = plx.PARALLAX_F32
+    a.x = a.w_q = a.w_r = a.q = a.rho = FAKE
+    a.x_stride_t, a.w_stride_n = 2048, 2048
+    a.q_stride_t, a.q_stride_h = 2048, 128
+    a.rho_stride_t, a.rho_stride_h = 2048, 128
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(struct_size=12), INVALID, "struct_size"),
+    (dict(tokens=0), INVALID, "tokens"),
+    (dict(out_dtype=7), INVALID, "out_dtype"),
+    (dict(w_r=None), INVALID, "non-NULL"),
+    (dict(q_stride_h=-128), INVALID, "non-negative"),
+    (dict(model_dim=2176), UNSUPP, "multiple of 256"),
+    (dict(head_dim=96), UNSUPP, "head_dim"),
+    (dict(x=FAKE + 2), UNSUPP, "aligned"),
+    (dict(x_stride_t=2052), UNSUPP, "16 bytes"),
+    (dict(out_dtype=plx.PARALLAX_BF16, q_stride_h=132), UNSUPP, "16 bytes"),
+    (dict(tokens=(1 << 22) + 1), UNSUPP, "tokens"),
+])
+def test_projection_rejects(lib, over, status, needle):
+    a = good_projection(**over)
+    assert lib.parallax_qr_projection(ctypes.byref(a), None) == status
+    assert needle in plx.parallax_last_error()
+    assert lib.parallax_qr_projection(None, None) == INVALID

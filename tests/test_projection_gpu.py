@@ -1,0 +1,74 @@
+"""GPU parity of parallax_qr_projection (q = W_Q x and rho = W_R x in one
+launch) against the oracle's fp64 products, through the C ABI, and its use as
+the input of decode and prefill through strided views.
+
+Tolerance: bf16 inputs are exact matrix-core operands and the sums run in
+fp32 over D terms, so fp32 outputs are within a few fp32 ulps of the sum of
+|terms| (bound 1e-5 (1 + |ref|) at D <= 4096 for these inputs); bf16 outputs
+add one rounding, 2^-9 relative (bound 2^-8 (1 + |ref|)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parallax_local_linear_decode_amd as plx
+from parallax_local_linear_decode_amd.workloads import decode_inputs, host_array
+
+from helpers import RMS_DECODE_BF16, TAU_BF16, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def weights(T, D, N, seed, dev):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn((T, D), generator=g).to(torch.bfloat16)
+    w_q = (torch.randn((N, D), generator=g) / D ** 0.5).to(torch.bfloat16)
+    w_r = (torch.randn((N, D), generator=g) / D ** 0.5).to(torch.bfloat16)
+    return x.to(dev), w_q.to(dev), w_r.to(dev)
+
+
+@pytest.mark.parametrize("T", [1, 8, 16, 17, 64, 100, 300])
+@pytest.mark.parametrize("D,Hq,d", [(256, 2, 64), (2048, 16, 128), (1280, 4, 64)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_every_element(gpu, T, D, Hq, d, out_dtype):
+    x, w_q, w_r = weights(T, D, Hq * d, T * 7 + D, gpu)
+    q, rho = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=Hq, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    rq, rr = oracle.qr_projection(host_array(x), host_array(w_q), host_array(w_r))
+    tau = 1e-5 if out_dtype == torch.float32 else 2.0 ** -8
+    assert_parity(q.reshape(T, -1), rq, tau, what="q")
+    assert_parity(rho.reshape(T, -1), rr, tau, what="rho")
+
+
+def test_zero_probe_weights_give_zero_rho(gpu):
+    x, w_q, w_r = weights(8, 2048, 2048, 70, gpu)
+    _, rho = plx.parallax_qr_projection(x, w_q, torch.zeros_like(w_r), num_q_heads=16)
+    torch.cuda.synchronize()
+    assert torch.all(rho == 0)
+
+
+def test_into_strided_views_feeds_decode(gpu):
+    """q and rho written into one [B, 2, Hq, d] buffer (the layout of a
+    stacked projection), then read by parallax_decode through their strides."""
+    B, Hq, Hkv, d, D = 8, 16, 8, 128, 2048
+    x, w_q, w_r = weights(B, D, Hq * d, 71, gpu)
+    buf = torch.full((B, 2, Hq, d), float("nan"), dtype=torch.float32, device=gpu)
+    q, rho = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=Hq, q=buf[:, 0], rho=buf[:, 1])
+    inp = decode_inputs(B, Hq, Hkv, d, 700, seed=72)
+    k, v = inp.k.to(gpu), inp.v.to(gpu)
+    out = plx.parallax_decode(q, rho, k, v, scale=inp.scale)
+    torch.cuda.synchronize()
+    rq, rr = oracle.qr_projection(host_array(x), host_array(w_q), host_array(w_r))
+    ref = oracle.decode(rq.reshape(B, Hq, d), rr.reshape(B, Hq, d), host_array(inp.k),
+                        host_array(inp.v), inp.scale)
+    assert_parity(out, ref, TAU_BF16, RMS_DECODE_BF16, what="decode from projection")
+
+
+def test_deterministic(gpu):
+    x, w_q, w_r = weights(300, 2048, 2048, 73, gpu)
+    a = [t.clone() for t in plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=16)]
+    for _ in range(5):
+        b = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=16)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
