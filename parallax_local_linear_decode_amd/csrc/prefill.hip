@@ -73,8 +73,10 @@ __device__ __forceinline__ float group_max(float x) {
 }
 
 // WIN: the local-window form (instantiated separately, so full causal
-// attention carries none of its index arithmetic).
-template <int G, bool WIN>
+// attention carries none of its index arithmetic).  STATS: also write lse, r
+// and o_SA for a backward pass (separately too: the plain forward keeps the
+// code it had without them).
+template <int G, bool WIN, bool STATS>
 __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p) {
     constexpr int D = kPfD;
     constexpr int KS = D / 32;                      // score MFMAs per 16-key block
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
             score_step(t + 1);
             advance(t + 1, std::integral_constant<int, 1>{});
         }
-        if (p.lse != nullptr) {  // the value wave turns its Z into log(sum e^s)
+        if constexpr (STATS) {  // the value wave turns its Z into log(sum e^s)
             mfin[pair][0][c] = mref[0];
             mfin[pair][1][c] = mref[1];
             __syncthreads();
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
             advance(t + 1, std::integral_constant<int, 1>{});
         }
 
-        if (p.lse != nullptr) __syncthreads();  // mfin written by the score waves
+        if constexpr (STATS) __syncthreads();  // mfin written by the score waves
 
         // ---- o = a - (b - a r) per query row; lane (c, g) holds d = 16db + 4g + j
 #pragma unroll
@@ -377,12 +379,14 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
             }
             // what a backward pass needs: log of the softmax denominator
             // (natural log; Z is kept relative to 2^m), r and o_SA
-            const int64_t ri = ((int64_t)b * p.num_q_heads + head) * S + qi;
-            if (p.lse != nullptr && g == 0)
-                p.lse[ri] = (mfin[pair][qc][c] + __builtin_log2f(acc[DB][qc][0])) *
-                            0.6931471805599453f;
-            if (p.rmean != nullptr && g == 0) p.rmean[ri] = r;
-            if (p.o_sa != nullptr) {
+            if constexpr (STATS) {
+                const int64_t ri = ((int64_t)b * p.num_q_heads + head) * S + qi;
+                if (p.lse != nullptr && g == 0)
+                    p.lse[ri] = (mfin[pair][qc][c] + __builtin_log2f(acc[DB][qc][0])) *
+                                0.6931471805599453f;
+                if (p.rmean != nullptr && g == 0) p.rmean[ri] = r;
+            }
+            if (STATS && p.o_sa != nullptr) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
                     *reinterpret_cast<float4 *>(p.o_sa + ooff + 16 * db + 4 * g) =
@@ -403,15 +407,21 @@ hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream) {
     const dim3 grid((unsigned)(units * ((p.seq_len + qb_rows - 1) / qb_rows)));
     const dim3 block(128 * kPfPairs);
     const bool win = p.window > 0 && p.window < p.seq_len;  // else every key 0..i is in range
-    switch (G * 2 + (win ? 1 : 0)) {
-        case 2: hipLaunchKernelGGL((prefill_kernel<1, false>), grid, block, 0, stream, p); break;
-        case 3: hipLaunchKernelGGL((prefill_kernel<1, true>), grid, block, 0, stream, p); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<2, false>), grid, block, 0, stream, p); break;
-        case 5: hipLaunchKernelGGL((prefill_kernel<2, true>), grid, block, 0, stream, p); break;
-        case 8: hipLaunchKernelGGL((prefill_kernel<4, false>), grid, block, 0, stream, p); break;
-        case 9: hipLaunchKernelGGL((prefill_kernel<4, true>), grid, block, 0, stream, p); break;
+    const bool stats = p.lse != nullptr || p.rmean != nullptr || p.o_sa != nullptr;
+#define PLX_PREFILL_CASE(G_, W_, S_)                                                         \
+    case G_ * 4 + W_ * 2 + S_:                                                               \
+        hipLaunchKernelGGL((prefill_kernel<G_, W_, S_>), grid, block, 0, stream, p);         \
+        break;
+    switch (G * 4 + (win ? 2 : 0) + (stats ? 1 : 0)) {
+        PLX_PREFILL_CASE(1, 0, 0) PLX_PREFILL_CASE(1, 0, 1)
+        PLX_PREFILL_CASE(1, 1, 0) PLX_PREFILL_CASE(1, 1, 1)
+        PLX_PREFILL_CASE(2, 0, 0) PLX_PREFILL_CASE(2, 0, 1)
+        PLX_PREFILL_CASE(2, 1, 0) PLX_PREFILL_CASE(2, 1, 1)
+        PLX_PREFILL_CASE(4, 0, 0) PLX_PREFILL_CASE(4, 0, 1)
+        PLX_PREFILL_CASE(4, 1, 0) PLX_PREFILL_CASE(4, 1, 1)
         default: return hipErrorInvalidValue;
     }
+#undef PLX_PREFILL_CASE
     return hipGetLastError();
 }
 
