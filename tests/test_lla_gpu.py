@@ -128,3 +128,31 @@ def test_full_size(gpu):
     assert_parity(out[idx.to(gpu)], ref_out, TAU[torch.bfloat16], TAU[torch.bfloat16],
                   what="full out")
     assert resid.max().item() < 1e-3
+
+
+def test_graph_replay(gpu):
+    """The whole solved-probe call (iterations + 2 decode sweeps and the
+    vector kernels, no host synchronisation, no memsets) captured once in a
+    HIP graph replays to the eager result, with eager calls in between."""
+    inp = to(decode_inputs(3, 16, 8, 128, 1500, seed=55), gpu)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=gpu)
+    bufs = [torch.empty((3, 16, 128), dtype=torch.float32, device=gpu) for _ in range(2)]
+    resid = torch.empty((3, 16), dtype=torch.float32, device=gpu)
+    want = [t.clone() for t in run(inp, 0.5, 12, workspace=ws)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        run(inp, 0.5, 12, workspace=ws, out=bufs[0], rho_out=bufs[1], resid=resid)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            plx.parallax_decode_lla(inp.q, inp.k, inp.v, lam=0.5, iterations=12,
+                                    scale=inp.scale, out=bufs[0], rho_out=bufs[1], resid=resid,
+                                    workspace=ws)
+    other = to(decode_inputs(2, 8, 4, 128, 700, seed=56), gpu)
+    for r in range(4):
+        for t in (*bufs, resid):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(want, (bufs[0], bufs[1], resid)):
+            assert torch.equal(a, b), f"replay {r}"
+        run(other, 0.3, 5, workspace=ws)  # an eager call of another shape in between

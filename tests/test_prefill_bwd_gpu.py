@@ -198,3 +198,33 @@ def test_full_size_window(gpu):
                   what="window dk")
     assert_parity(dv[1:2, 3000:3040], r_dv[:, 3000:3040], TAU_BWD, RMS_BWD,
                   what="window dv")
+
+
+def test_graph_replay(gpu):
+    """Forward with statistics plus backward captured in one HIP graph
+    replays to the eager result, with eager calls in between."""
+    q, rho, k, v, dout, scale = case(1, 300, 4, 2, 18, gpu)
+    stats, grads = forward_backward(q, rho, k, v, dout, scale)
+    want = [t.clone() for t in grads]
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device=gpu)
+    outs = [torch.empty_like(t) for t in grads]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, lse, rmean, o_sa = plx.parallax_prefill(q, rho, k, v, scale=scale, return_stats=True)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            # the forward again (its statistics are those of the eager call
+            # above: same inputs), then the backward
+            fo = plx.parallax_prefill(q, rho, k, v, scale=scale, out=out)
+            plx.parallax_prefill_backward(q, rho, k, v, dout, fo, o_sa, lse, rmean, scale=scale,
+                                          dq=outs[0], drho=outs[1], dk=outs[2], dv=outs[3],
+                                          workspace=ws)
+    other = case(1, 100, 2, 1, 19, gpu)
+    for r in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(want, outs):
+            assert torch.equal(a, b), f"replay {r}"
+        forward_backward(*other[:5], other[5])
