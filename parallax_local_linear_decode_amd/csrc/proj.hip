@@ -145,12 +145,154 @@ hipError_t launch_nt(const ProjParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- tiled ---
+// Prefill sizes (many tokens): a plain GEMM C[t][n] = sum_k x[t][k] W[n][k]
+// with both operands contiguous in k.  Workgroup tile: 128 stacked weight
+// rows x 128 tokens, four waves of 64 x 64 (4 x 4 MFMA tiles each).  K
+// advances in chunks of 64 through a double-buffered LDS tile pair; each
+// chunk's global loads are issued one chunk ahead through registers (every
+// thread moves four 16-byte pieces of each operand).
+constexpr int kTile = 128;
+constexpr int kChunk = 64;                       // k per LDS chunk
+constexpr int kLdsRow = kChunk * 2 + 16;         // 144-byte rows: 16 rows on distinct banks
+constexpr int kLdsTile = kTile * kLdsRow;
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(256, 2) void proj_tiled_kernel(ProjParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned char wt[2][kLdsTile];
+    __shared__ __attribute__((aligned(16))) unsigned char xt[2][kLdsTile];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int wr = wave & 1, wc = wave >> 1;  // wave's 64-row block (weights), 64-column block (tokens)
+    const int row0 = blockIdx.x * kTile;      // first stacked weight row
+    const int t0 = blockIdx.y * kTile;
+    const int T = p.tokens;
+
+    // loader: thread tid moves row tid / 8 + 32 i, 16-byte piece tid % 8 of
+    // both operands; offsets from the operand bases (no pointer arrays: the
+    // compiler kept those in scratch memory)
+    const int lrow = tid / 8, lpc = tid % 8;
+    int64_t woff[4], xoff[4];
+    bool wr_is_r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = row0 + lrow + 32 * i;  // stacked row (always < 2N: 2N is a multiple of 128)
+        wr_is_r[i] = r >= p.n;
+        woff[i] = (int64_t)(wr_is_r[i] ? r - p.n : r) * p.w_sn + 8 * lpc;
+        xoff[i] = (int64_t)min(t0 + lrow + 32 * i, T - 1) * p.x_st + 8 * lpc;
+    }
+    uint4 ws0, ws1, ws2, ws3, xs0, xs1, xs2, xs3;
+#define PLX_ISSUE(k0)                                                                          \
+    do {                                                                                       \
+        ws0 = *reinterpret_cast<const uint4 *>((wr_is_r[0] ? p.w_r : p.w_q) + woff[0] + (k0)); \
+        ws1 = *reinterpret_cast<const uint4 *>((wr_is_r[1] ? p.w_r : p.w_q) + woff[1] + (k0)); \
+        ws2 = *reinterpret_cast<const uint4 *>((wr_is_r[2] ? p.w_r : p.w_q) + woff[2] + (k0)); \
+        ws3 = *reinterpret_cast<const uint4 *>((wr_is_r[3] ? p.w_r : p.w_q) + woff[3] + (k0)); \
+        xs0 = *reinterpret_cast<const uint4 *>(p.x + xoff[0] + (k0));                         \
+        xs1 = *reinterpret_cast<const uint4 *>(p.x + xoff[1] + (k0));                         \
+        xs2 = *reinterpret_cast<const uint4 *>(p.x + xoff[2] + (k0));                         \
+        xs3 = *reinterpret_cast<const uint4 *>(p.x + xoff[3] + (k0));                         \
+    } while (0)
+#define PLX_STORE(buf)                                                                         \
+    do {                                                                                       \
+        unsigned char *wd = wt[buf] + lrow * kLdsRow + 16 * lpc;                               \
+        unsigned char *xd = xt[buf] + lrow * kLdsRow + 16 * lpc;                               \
+        *reinterpret_cast<uint4 *>(wd) = ws0;                                                  \
+        *reinterpret_cast<uint4 *>(wd + 32 * kLdsRow) = ws1;                                   \
+        *reinterpret_cast<uint4 *>(wd + 64 * kLdsRow) = ws2;                                   \
+        *reinterpret_cast<uint4 *>(wd + 96 * kLdsRow) = ws3;                                   \
+        *reinterpret_cast<uint4 *>(xd) = xs0;                                                  \
+        *reinterpret_cast<uint4 *>(xd + 32 * kLdsRow) = xs1;                                   \
+        *reinterpret_cast<uint4 *>(xd + 64 * kLdsRow) = xs2;                                   \
+        *reinterpret_cast<uint4 *>(xd + 96 * kLdsRow) = xs3;                                   \
+    } while (0)
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nchunks = p.model_dim / kChunk;
+    PLX_ISSUE(0);
+    PLX_STORE(0);
+    if (nchunks > 1) PLX_ISSUE(kChunk);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int buf = ch & 1;
+#pragma unroll
+        for (int kk = 0; kk < kChunk / 32; ++kk) {
+            bf16x8_t a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                  wt[buf] + (64 * wr + 16 * i + c) * kLdsRow + 64 * kk + 16 * g));
+                b[i] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                  xt[buf] + (64 * wc + 16 * i + c) * kLdsRow + 64 * kk + 16 * g));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        // the next chunk (loaded during this one) goes to the other buffer,
+        // free since the barrier that ended chunk ch - 1
+        if (ch + 1 < nchunks) {
+            PLX_STORE(1 - buf);
+            if (ch + 2 < nchunks) PLX_ISSUE((ch + 2) * kChunk);
+        }
+        __syncthreads();
+    }
+#undef PLX_ISSUE
+#undef PLX_STORE
+
+    // acc[i][j]: lane (c, g) holds stacked rows row0 + 64 wr + 16 i + 4g + (0..3)
+    // of token t0 + 64 wc + 16 j + c
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = row0 + 64 * wr + 16 * i + 4 * g;  // the 16-row tile never straddles N
+        const bool is_r = r >= p.n;
+        const int f = r - (is_r ? p.n : 0);
+        const int h = f / p.head_dim, e = f % p.head_dim;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = t0 + 64 * wc + 16 * j + c;
+            if (t >= T) continue;
+            const int64_t off = (int64_t)t * (is_r ? p.r_st : p.q_st) +
+                                (int64_t)h * (is_r ? p.r_sh : p.q_sh) + e;
+            const f32x4_t s = acc[i][j];
+            if constexpr (BF16OUT) {
+                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                const bf16x4_t v = {(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(is_r ? p.rho : p.q) + off) =
+                    __builtin_bit_cast(uint2, v);
+            } else {
+                *reinterpret_cast<float4 *>(static_cast<float *>(is_r ? p.rho : p.q) + off) =
+                    float4{s[0], s[1], s[2], s[3]};
+            }
+        }
+    }
+}
+
 }  // namespace
 
-// Token blocks of 16 up to 16 tokens (decode), else of 64 (each weight
-// element then serves 64 tokens per load).
+// Up to 16 tokens (decode): token blocks of 16 and the weight-streaming
+// kernel; up to 128: blocks of 64; beyond: the LDS-tiled GEMM.
 hipError_t launch_qr_projection(const ProjParams &p, hipStream_t stream) {
-    return p.tokens <= 16 ? launch_nt<1>(p, stream) : launch_nt<4>(p, stream);
+    if (p.tokens <= 16) return launch_nt<1>(p, stream);
+    if (p.tokens <= 128) return launch_nt<4>(p, stream);
+    const dim3 grid((unsigned)(2 * p.n / kTile), (unsigned)((p.tokens + kTile - 1) / kTile));
+    if (p.out_bf16)
+        hipLaunchKernelGGL(proj_tiled_kernel<true>, grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(proj_tiled_kernel<false>, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace plx
