@@ -108,3 +108,21 @@ def test_full_size_deterministic(gpu):
         plx.parallax_prefill(q, rho, k, v, scale=scale, out=out)
         torch.cuda.synchronize()
         assert torch.equal(out, first), f"launch {i} differs"
+
+
+def test_strided_views_equal_contiguous(gpu):
+    """q and rho as the two halves of one [B, S, 2, Hq, d] buffer (the layout
+    the stacked projection writes), k and v as halves of [B, S, 2, Hkv, d],
+    and out written into a wider buffer: the same bits as contiguous tensors."""
+    B, S, Hq, Hkv, d = 2, 300, 4, 2, 128
+    q, rho, k, v, scale = (t.to(gpu) if isinstance(t, torch.Tensor) else t
+                           for t in prefill_inputs(B, S, Hq, Hkv, d, seed=9))
+    want = run(q, rho, k, v, scale).clone()
+    qr = torch.stack([q, rho], dim=2)          # [B, S, 2, Hq, d]
+    kv = torch.stack([k, v], dim=2)            # [B, S, 2, Hkv, d]
+    wide = torch.full((B, S, Hq, 2 * d), float("nan"), dtype=torch.float32, device=gpu)
+    out = plx.parallax_prefill(qr[:, :, 0], qr[:, :, 1], kv[:, :, 0], kv[:, :, 1], scale=scale,
+                               out=wide[..., d:])
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
+    assert torch.isnan(wide[..., :d]).all()

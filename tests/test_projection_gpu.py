@@ -72,3 +72,30 @@ def test_deterministic(gpu):
         b = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=16)
         torch.cuda.synchronize()
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_projection_feeds_prefill(gpu):
+    """x -> (q, rho) in bf16 straight into one [T, 2, Hq, d] buffer -> causal
+    prefill through strided views, against the oracle chain (projection, then
+    prefill on the same bf16-rounded q and rho)."""
+    B, S, Hq, Hkv, d, D = 1, 200, 4, 2, 128, 512
+    x, w_q, w_r = weights(B * S, D, Hq * d, 74, gpu)
+    # rho ~ N(0, 0.1^2) as in the prefill workload (the prefill tolerance
+    # assumes a probe of that size)
+    w_r = (w_r.float() * 0.1).to(torch.bfloat16)
+    buf = torch.empty((B * S, 2, Hq, d), dtype=torch.bfloat16, device=gpu)
+    q, rho = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=Hq, out_dtype=torch.bfloat16,
+                                        q=buf[:, 0], rho=buf[:, 1])
+    g = torch.Generator(device="cpu").manual_seed(75)
+    k = torch.randn((B, S, Hkv, d), generator=g).to(torch.bfloat16).to(gpu)
+    v = torch.randn((B, S, Hkv, d), generator=g).to(torch.bfloat16).to(gpu)
+    out = plx.parallax_prefill(q.view(B, S, Hq, d), rho.view(B, S, Hq, d), k, v, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    rq, rr = oracle.qr_projection(host_array(x), host_array(w_q), host_array(w_r))
+    # the oracle prefill sees the projection rounded to bf16 as the kernel wrote it
+    qb = host_array(q.contiguous()).reshape(B, S, Hq, d)
+    rb = host_array(rho.contiguous()).reshape(B, S, Hq, d)
+    assert_parity(q.reshape(B * S, -1), rq, 2.0 ** -8, what="q")
+    assert_parity(rho.reshape(B * S, -1), rr, 2.0 ** -8, what="rho")
+    ref = oracle.prefill(qb, rb, host_array(k), host_array(v), d ** -0.5)
+    assert_parity(out, ref, TAU_BF16, 1e-2, what="prefill from projection")
