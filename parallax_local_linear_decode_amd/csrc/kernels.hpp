@@ -58,8 +58,8 @@ struct PrefillParams {
 };
 
 // Causal prefill backward.  rowstat is the workspace: one float4 per row
-// (b, h, i) at ((b * Hq + h) * S + i), holding (lse * log2 e, r, c, D) with
-// c = o_SA . dout and D = dout . out + r c.
+// (b, h, i) at ((b * Hq + h) * S + i), holding (lse * log2 e, 1 + r, c, D)
+// with c = o_SA . dout and D = dout . out + r c.
 struct PrefillBwdParams {
     const uint16_t *q;
     const uint16_t *rho;

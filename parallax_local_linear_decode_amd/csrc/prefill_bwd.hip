@@ -17,7 +17,7 @@
 //
 // Three kernels, all deterministic (fixed summation order, no atomics):
 //   prep  one 16-lane group per row: c = a.g and D = g.o + r c, stored with
-//         lse * log2(e) and r as one float4 per row (the workspace);
+//         lse * log2(e) and 1 + r as one float4 per row (the workspace);
 //   dq    query-major, the forward's structure: a workgroup holds 128 query
 //         rows of the G heads of one KV head, 32-key K/V tiles stream through
 //         LDS.  Score wave p recomputes S^T = K Q^T, T^T = K rho^T and
@@ -32,8 +32,13 @@
 //         dT in bf16; value wave: dv^T += dout^T W, dk^T += q^T dS + rho^T dT.
 // Tiles read by both roles live two epochs (score wave in epoch t, value
 // wave in epoch t + 1), so they are triple-buffered in LDS; each epoch ends
-// with one barrier, and global loads run two tiles ahead through two register
-// stages, issued unconditionally so the compiler's wait counts stay exact.
+// with one barrier.  The value waves, whose MFMAs end early in the epoch, do
+// all the staging (global loads into registers, then LDS stores), so the
+// score waves' MFMA and VALU work is the epoch's critical path: dq runs the
+// loads two tiles ahead through two register stages, dkv (more registers
+// live in its value waves) one tile ahead through one stage, stored at the
+// start of the next epoch.  Loads are issued unconditionally so the
+// compiler's wait counts stay exact.
 #include "kernels.hpp"
 
 #include <math.h>
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrefillBwdParams p) {
     }
     if (u < rows && part == 0) {
         const float r = p.rmean[uu];
-        p.rowstat[uu] = float4{p.lse[uu] * 1.4426950408889634f, r, ca, fmaf(r, ca, go)};
+        p.rowstat[uu] = float4{p.lse[uu] * 1.4426950408889634f, 1.0f + r, ca, fmaf(r, ca, go)};
     }
 }
 
@@ -178,14 +183,38 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
 
     const uint16_t *kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
     const uint16_t *vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
-    uint4 kst[2], vst[2];  // tile j in stage j & 1
-    auto issue = [&](int t, uint4 &kd, uint4 &vd) {
-        const int key = min(t * kBwTile + tid / 16, S - 1);
-        kd = ld16(kg + (int64_t)key * p.k_ss + 8 * (tid % 16));
-        vd = ld16(vg + (int64_t)key * p.v_ss + 8 * (tid % 16));
+    // Staging, value waves only: thread tv takes keys rv and rv + 16 of a
+    // tile, 16-byte piece cv of each row.
+    const int tv = tid - 64 * kBwPairs;
+    const int rv = (tv >> 4) & 15, cv = tv & 15;
+    const int64_t ko = (int64_t)rv * p.k_ss + 8 * cv, vo = (int64_t)rv * p.v_ss + 8 * cv;
+    struct Stage {
+        uint4 k[2], v[2];
+    } kst[2];  // tile j in stage j & 1
+    auto issue = [&](int t, Stage &st) {
+        const int key0 = min(t * kBwTile, S - 1);
+        const uint16_t *ks_ = kg + (int64_t)key0 * p.k_ss;
+        const uint16_t *vs_ = vg + (int64_t)key0 * p.v_ss;
+        if (key0 + kBwTile <= S) {
+            st.k[0] = ld16(ks_ + ko);
+            st.v[0] = ld16(vs_ + vo);
+            st.k[1] = ld16(ks_ + 16 * p.k_ss + ko);
+            st.v[1] = ld16(vs_ + 16 * p.v_ss + vo);
+        } else {  // a ragged last tile: keys past the end read key S - 1
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int kk = min(rv + 16 * i, S - 1 - key0);
+                st.k[i] = ld16(ks_ + (int64_t)kk * p.k_ss + 8 * cv);
+                st.v[i] = ld16(vs_ + (int64_t)kk * p.v_ss + 8 * cv);
+            }
+        }
     };
-    auto store = [&](unsigned char *tile, const uint4 &st) {
-        *reinterpret_cast<uint4 *>(tile + (tid / 16) * kBwRowBytes + 16 * (tid % 16)) = st;
+    auto store = [&](unsigned char *kt, unsigned char *vt, const Stage &st) {
+        const int off = rv * kBwRowBytes + 16 * cv;
+        *reinterpret_cast<uint4 *>(kt + off) = st.k[0];
+        *reinterpret_cast<uint4 *>(kt + off + 16 * kBwRowBytes) = st.k[1];
+        *reinterpret_cast<uint4 *>(vt + off) = st.v[0];
+        *reinterpret_cast<uint4 *>(vt + off + 16 * kBwRowBytes) = st.v[1];
     };
     // End of epoch t: K and V tile t + 1 go to LDS (K buffer (t+1) % 3 last
     // held tile t - 2, read by the value waves in epoch t - 1; V buffer
@@ -193,17 +222,15 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
     // their register stage takes the loads of tile t + 3.
     auto advance = [&](int t, auto par) {
         constexpr int P = decltype(par)::value;
-        store(ktile + slot3(t + 1), kst[1 - P]);
-        store(vtile[1 - P], vst[1 - P]);
-        issue(t + 3, kst[1 - P], vst[1 - P]);
+        store(ktile + slot3(t + 1), vtile[1 - P], kst[1 - P]);
+        issue(t + 3, kst[1 - P]);
         __syncthreads();
     };
     auto prologue = [&] {
-        issue(t_first, kst[0], vst[0]);
-        store(ktile + slot3(t_first), kst[0]);
-        store(vtile[0], vst[0]);
-        issue(t_first + 1, kst[1], vst[1]);
-        issue(t_first + 2, kst[0], vst[0]);
+        issue(t_first, kst[0]);
+        store(ktile + slot3(t_first), vtile[0], kst[0]);
+        issue(t_first + 1, kst[1]);
+        issue(t_first + 2, kst[0]);
         __syncthreads();
     };
 
@@ -267,7 +294,7 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc) {
                 const int qi = r0 + 16 * qc + c;
-                const float lse2 = st[qc].x, r1 = 1.0f + st[qc].y, cc = st[qc].z, dd = st[qc].w;
+                const float lse2 = st[qc].x, r1 = st[qc].y, cc = st[qc].z, dd = st[qc].w;
                 uint32_t sw[4], tw[4];
 #pragma unroll
                 for (int r = 0; r < 8; r += 2) {
@@ -283,8 +310,8 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
                             const int key = t * kBwTile + (rr < 4 ? 4 * g + rr : 16 + 4 * g + rr - 4);
                             pw = key <= qi && key < S && (W == 0 || key > qi - W) ? pw : 0.0f;
                         }
-                        const float dp = fmaf(uu, r1 - tt, cc * tt);
-                        ds2[h2] = pw * (dp - dd);
+                        // dL/dp - D = u (1 + r - t) + (c t - D)
+                        ds2[h2] = pw * fmaf(uu, r1 - tt, fmaf(tt, cc, -dd));
                         dt2[h2] = pw * (cc - uu);
                     }
                     sw[r / 2] = pack_bf16x2(ds2[0], ds2[1]);
@@ -305,12 +332,12 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
                     grads(t, d1, du, std::true_type{});
             }
         };
-        prologue();
+        __syncthreads();  // the value waves' prologue
         for (int t = t_first; t <= ntiles; t += 2) {
             score_step(t);
-            advance(t, std::integral_constant<int, 0>{});
+            __syncthreads();
             score_step(t + 1);
-            advance(t + 1, std::integral_constant<int, 1>{});
+            __syncthreads();
         }
     } else {
         // acc[db][cb]: rows d = 16db + 4g + j, column c of block cb (dS^T rows
@@ -406,53 +433,60 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
     auto tile_head = [&](int t) { return hk * G + t / nq; };
     auto tile_qt = [&](int t) { return qt_lo + t % nq; };
 
-    // Two register stages (named, not an array: the compiler may move an
-    // array it fails to keep in registers into LDS).
-    struct Stage {
-        uint4 q, r, g;
-        float4 s;
-    } stage0, stage1;
-    auto stage = [&](auto par) -> Stage & {
-        if constexpr (decltype(par)::value == 0) return stage0;
-        else return stage1;
-    };
-    // register stage P of tile t (P fixed at compile time: a runtime index
-    // into a register array would move it to scratch memory)
-    auto issue = [&](int t, auto par) {
-        Stage &st = stage(par);
+    // Staging, value waves only: thread tv takes rows rv and rv + 16 of a
+    // tile, 16-byte piece cv of each row, and float se of the tile's 128
+    // statistics floats (its 32 rows' float4s are contiguous).  One register
+    // stage: tile t + 1, loaded during epoch t - 1, goes to LDS at the start
+    // of epoch t (its slot and statistics row last held tile t - 2, read in
+    // epoch t - 1); after the value MFMAs of epoch t the stage takes the
+    // loads of tile t + 2.
+    const int tv = tid - 64 * kBwPairs;
+    const int rv = (tv >> 4) & 15, cv = tv & 15, se = tv & 127;
+    const int64_t qo = (int64_t)rv * p.q_ss + 8 * cv;
+    const int64_t ro = (int64_t)rv * p.r_ss + 8 * cv;
+    const int64_t go = (int64_t)rv * p.g_ss + 8 * cv;
+    struct {
+        uint4 q[2], r[2], g[2];
+        float s;
+    } st;
+    auto issue = [&](int t) {
         const int tt = min(t, ntiles - 1);
         const int h = tile_head(tt);
-        const int row = min(tile_qt(tt) * kBwTile + tid / 16, S - 1);
-        st.q = ld16(p.q + (int64_t)b * p.q_sb + (int64_t)row * p.q_ss + (int64_t)h * p.q_sh +
-                      8 * (tid % 16));
-        st.r = ld16(p.rho + (int64_t)b * p.r_sb + (int64_t)row * p.r_ss + (int64_t)h * p.r_sh +
-                      8 * (tid % 16));
-        st.g = ld16(p.dout + (int64_t)b * p.g_sb + (int64_t)row * p.g_ss + (int64_t)h * p.g_sh +
-                      8 * (tid % 16));
-        st.s = p.rowstat[((int64_t)b * p.num_q_heads + h) * S + row];
+        const int row0 = tile_qt(tt) * kBwTile;
+        const uint16_t *qs = p.q + (int64_t)b * p.q_sb + (int64_t)row0 * p.q_ss + (int64_t)h * p.q_sh;
+        const uint16_t *rs = p.rho + (int64_t)b * p.r_sb + (int64_t)row0 * p.r_ss + (int64_t)h * p.r_sh;
+        const uint16_t *gs = p.dout + (int64_t)b * p.g_sb + (int64_t)row0 * p.g_ss + (int64_t)h * p.g_sh;
+        const float *ss = reinterpret_cast<const float *>(p.rowstat + ((int64_t)b * p.num_q_heads + h) * S);
+        if (row0 + kBwTile <= S) {
+            st.q[0] = ld16(qs + qo);
+            st.r[0] = ld16(rs + ro);
+            st.g[0] = ld16(gs + go);
+            st.q[1] = ld16(qs + 16 * p.q_ss + qo);
+            st.r[1] = ld16(rs + 16 * p.r_ss + ro);
+            st.g[1] = ld16(gs + 16 * p.g_ss + go);
+        } else {  // a ragged last tile: rows past the end read row S - 1
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int64_t rr = min(rv + 16 * i, S - 1 - row0);
+                st.q[i] = ld16(qs + rr * p.q_ss + 8 * cv);
+                st.r[i] = ld16(rs + rr * p.r_ss + 8 * cv);
+                st.g[i] = ld16(gs + rr * p.g_ss + 8 * cv);
+            }
+        }
+        st.s = ss[4 * min(row0 + (se >> 2), S - 1) + (se & 3)];
     };
-    auto store = [&](int t, auto par) {
-        const Stage &st = stage(par);
-        const int off = slot3(t) + (tid / 16) * kBwRowBytes + 16 * (tid % 16);
-        *reinterpret_cast<uint4 *>(qtile + off) = st.q;
-        *reinterpret_cast<uint4 *>(rtile + off) = st.r;
-        *reinterpret_cast<uint4 *>(gtile + off) = st.g;
-        // the 16 threads of a row all store its statistics (same value): no
-        // lane condition, so no branch around a store that waits on a load
-        stile[t % 3][tid / 16] = st.s;
-    };
-    auto advance = [&](int t, auto par) {
-        constexpr int P = decltype(par)::value;
-        store(t + 1, std::integral_constant<int, 1 - P>{});
-        issue(t + 3, std::integral_constant<int, 1 - P>{});
-        __syncthreads();
-    };
-    auto prologue = [&] {
-        issue(0, std::integral_constant<int, 0>{});
-        store(0, std::integral_constant<int, 0>{});
-        issue(1, std::integral_constant<int, 1>{});
-        issue(2, std::integral_constant<int, 0>{});
-        __syncthreads();
+    auto store = [&](int t) {
+        const int off = slot3(t) + rv * kBwRowBytes + 16 * cv;
+        constexpr int O16 = 16 * kBwRowBytes;
+        *reinterpret_cast<uint4 *>(qtile + off) = st.q[0];
+        *reinterpret_cast<uint4 *>(rtile + off) = st.r[0];
+        *reinterpret_cast<uint4 *>(gtile + off) = st.g[0];
+        *reinterpret_cast<uint4 *>(qtile + off + O16) = st.q[1];
+        *reinterpret_cast<uint4 *>(rtile + off + O16) = st.r[1];
+        *reinterpret_cast<uint4 *>(gtile + off + O16) = st.g[1];
+        // threads tv and tv + 128 store the same statistics float: no lane
+        // condition, so no branch around a store that waits on a load
+        reinterpret_cast<float *>(stile[t % 3])[se] = st.s;
     };
     auto active = [&](int t) {
         if (t < 0 || t >= ntiles) return false;
@@ -534,9 +568,9 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
                                          ? pw
                                          : 0.0f;
                             }
-                            const float m1 = 1.0f + st.y - tt;
+                            const float m1 = st.y - tt;  // 1 + r - t
                             w2[h2] = pw * m1;
-                            ds2[h2] = p.scale * pw * (fmaf(uu, m1, st.z * tt) - st.w);
+                            ds2[h2] = (p.scale * pw) * fmaf(uu, m1, fmaf(tt, st.z, -st.w));
                             dt2[h2] = pw * (st.z - uu);
                         }
                         // k-slot 4rb + j of the value MFMAs' B operand
@@ -569,12 +603,10 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
                     grads(t, sd, td, ud, std::true_type{});
             }
         };
-        prologue();
-        for (int t = 0; t <= ntiles; t += 2) {
+        __syncthreads();  // the value waves' prologue
+        for (int t = 0; t < ntiles; ++t) {
             score_step(t);
-            advance(t, std::integral_constant<int, 0>{});
-            score_step(t + 1);
-            advance(t + 1, std::integral_constant<int, 1>{});
+            __syncthreads();
         }
     } else {
         // dvt[db][kc], dkt[db][kc]: rows d = 16db + 4g + j, key column c of
@@ -611,13 +643,17 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
             }
         };
 
-        prologue();
-        for (int t = 0; t <= ntiles; t += 2) {
+        issue(0);
+        store(0);
+        issue(1);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            store(t + 1);
             if (active(t - 1)) value_tile(t - 1);
-            advance(t, std::integral_constant<int, 0>{});
-            if (active(t)) value_tile(t);
-            advance(t + 1, std::integral_constant<int, 1>{});
+            issue(t + 2);
+            __syncthreads();
         }
+        if (active(ntiles - 1)) value_tile(ntiles - 1);
 
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
