@@ -147,122 +147,153 @@ hipError_t launch_nt(const ProjParams &p, hipStream_t stream) {
 
 // ---------------------------------------------------------------- tiled ---
 // Prefill sizes (many tokens): a plain GEMM C[t][n] = sum_k x[t][k] W[n][k]
-// with both operands contiguous in k.  Workgroup tile: 128 stacked weight
-// rows x 128 tokens, four waves of 64 x 64 (4 x 4 MFMA tiles each).  K
+// with both operands contiguous in k.  Workgroup tile: MT stacked weight rows
+// x NT tokens, WM x WN waves of 16 TI x 16 TJ (TI x TJ MFMA tiles each).  K
 // advances in chunks of 64 through a double-buffered LDS tile pair; each
-// chunk's global loads are issued one chunk ahead through registers (every
-// thread moves four 16-byte pieces of each operand).
-constexpr int kTile = 128;
+// chunk's global loads run one chunk ahead through registers (every thread
+// moves four 16-byte pieces of each operand), and both the loads and the
+// LDS stores are spread one or two at a time between the MFMAs, so the
+// matrix cores do not idle while a workgroup stages.  Per k the workgroup
+// loads (MT + NT) * 2 bytes for 2 MT NT flops: the 256 x 256 tile halves the
+// L2 traffic per flop of the 128 x 128 one.
 constexpr int kChunk = 64;                       // k per LDS chunk
+constexpr int kCUs = 256;                        // compute units of an MI355X
 constexpr int kLdsRow = kChunk * 2 + 16;         // 144-byte rows: 16 rows on distinct banks
-constexpr int kLdsTile = kTile * kLdsRow;
 
-template <bool BF16OUT>
-__global__ __launch_bounds__(256, 2) void proj_tiled_kernel(ProjParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char wt[2][kLdsTile];
-    __shared__ __attribute__((aligned(16))) unsigned char xt[2][kLdsTile];
+template <int WM_, int WN_, int TI_, int TJ_>
+struct TileCfg {
+    static constexpr int WM = WM_, WN = WN_, TI = TI_, TJ = TJ_;
+    static constexpr int kThreads = 64 * WM * WN;
+    static constexpr int kMT = 16 * TI * WM;  // stacked weight rows
+    static constexpr int kNT = 16 * TJ * WN;  // tokens
+    static constexpr int kLdsW = kMT * kLdsRow;
+    static constexpr int kLdsX = kNT * kLdsRow;
+    static constexpr int kStride = kThreads / 8;  // loader row stride
+    static_assert(kMT == 4 * kStride && kNT == 4 * kStride, "four pieces per thread and operand");
+};
+using Tile128 = TileCfg<2, 2, 4, 4>;
+using Tile256 = TileCfg<2, 4, 8, 4>;
+
+template <class C, bool BF16OUT>
+__global__ __launch_bounds__(C::kThreads) void proj_tiled_kernel(ProjParams p) {
+    constexpr int TI = C::TI, TJ = C::TJ, WM = C::WM;
+    __shared__ __attribute__((aligned(16))) unsigned char wt[2][C::kLdsW];
+    __shared__ __attribute__((aligned(16))) unsigned char xt[2][C::kLdsX];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int c = lane & 15;
     const int g = lane >> 4;
-    const int wr = wave & 1, wc = wave >> 1;  // wave's 64-row block (weights), 64-column block (tokens)
-    const int row0 = blockIdx.x * kTile;      // first stacked weight row
-    const int t0 = blockIdx.y * kTile;
+    const int wr = wave % WM, wc = wave / WM;  // wave's row block (weights), column block (tokens)
+    const int row0 = blockIdx.x * C::kMT;      // first stacked weight row
+    const int t0 = blockIdx.y * C::kNT;
     const int T = p.tokens;
 
-    // loader: thread tid moves row tid / 8 + 32 i, 16-byte piece tid % 8 of
-    // both operands; offsets from the operand bases (no pointer arrays: the
-    // compiler kept those in scratch memory)
+    // loader: thread tid moves row tid / 8 + kStride i, 16-byte piece tid % 8
+    // of both operands; offsets from the operand bases (no pointer arrays:
+    // the compiler kept those in scratch memory)
     const int lrow = tid / 8, lpc = tid % 8;
     int64_t woff[4], xoff[4];
     bool wr_is_r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = row0 + lrow + 32 * i;  // stacked row (always < 2N: 2N is a multiple of 128)
+        const int r = row0 + lrow + C::kStride * i;  // stacked row (< 2N: 2N is a multiple of kMT)
         wr_is_r[i] = r >= p.n;
         woff[i] = (int64_t)(wr_is_r[i] ? r - p.n : r) * p.w_sn + 8 * lpc;
-        xoff[i] = (int64_t)min(t0 + lrow + 32 * i, T - 1) * p.x_st + 8 * lpc;
+        xoff[i] = (int64_t)min(t0 + lrow + C::kStride * i, T - 1) * p.x_st + 8 * lpc;
     }
-    uint4 ws0, ws1, ws2, ws3, xs0, xs1, xs2, xs3;
-#define PLX_ISSUE(k0)                                                                          \
-    do {                                                                                       \
-        ws0 = *reinterpret_cast<const uint4 *>((wr_is_r[0] ? p.w_r : p.w_q) + woff[0] + (k0)); \
-        ws1 = *reinterpret_cast<const uint4 *>((wr_is_r[1] ? p.w_r : p.w_q) + woff[1] + (k0)); \
-        ws2 = *reinterpret_cast<const uint4 *>((wr_is_r[2] ? p.w_r : p.w_q) + woff[2] + (k0)); \
-        ws3 = *reinterpret_cast<const uint4 *>((wr_is_r[3] ? p.w_r : p.w_q) + woff[3] + (k0)); \
-        xs0 = *reinterpret_cast<const uint4 *>(p.x + xoff[0] + (k0));                         \
-        xs1 = *reinterpret_cast<const uint4 *>(p.x + xoff[1] + (k0));                         \
-        xs2 = *reinterpret_cast<const uint4 *>(p.x + xoff[2] + (k0));                         \
-        xs3 = *reinterpret_cast<const uint4 *>(p.x + xoff[3] + (k0));                         \
-    } while (0)
-#define PLX_STORE(buf)                                                                         \
-    do {                                                                                       \
-        unsigned char *wd = wt[buf] + lrow * kLdsRow + 16 * lpc;                               \
-        unsigned char *xd = xt[buf] + lrow * kLdsRow + 16 * lpc;                               \
-        *reinterpret_cast<uint4 *>(wd) = ws0;                                                  \
-        *reinterpret_cast<uint4 *>(wd + 32 * kLdsRow) = ws1;                                   \
-        *reinterpret_cast<uint4 *>(wd + 64 * kLdsRow) = ws2;                                   \
-        *reinterpret_cast<uint4 *>(wd + 96 * kLdsRow) = ws3;                                   \
-        *reinterpret_cast<uint4 *>(xd) = xs0;                                                  \
-        *reinterpret_cast<uint4 *>(xd + 32 * kLdsRow) = xs1;                                   \
-        *reinterpret_cast<uint4 *>(xd + 64 * kLdsRow) = xs2;                                   \
-        *reinterpret_cast<uint4 *>(xd + 96 * kLdsRow) = xs3;                                   \
-    } while (0)
+    uint4 ws0, ws1, ws2, ws3, xs0, xs1, xs2, xs3;  // staging registers, one chunk
+    // piece j (0-7) of the staging: j < 4 the weight rows, else the tokens
+    auto store_piece = [&](int j, int buf) __attribute__((always_inline)) {
+        constexpr int RS = C::kStride * kLdsRow;
+        unsigned char *d = (j < 4 ? wt[buf] : xt[buf]) + lrow * kLdsRow + 16 * lpc + (j & 3) * RS;
+        const uint4 v = j == 0 ? ws0 : j == 1 ? ws1 : j == 2 ? ws2 : j == 3 ? ws3
+                      : j == 4 ? xs0 : j == 5 ? xs1 : j == 6 ? xs2 : xs3;
+        *reinterpret_cast<uint4 *>(d) = v;
+    };
+    auto issue_piece = [&](int j, int k0) __attribute__((always_inline)) {
+        if (j < 4) {
+            const uint4 v = *reinterpret_cast<const uint4 *>((wr_is_r[j] ? p.w_r : p.w_q) + woff[j] + k0);
+            if (j == 0) ws0 = v;
+            else if (j == 1) ws1 = v;
+            else if (j == 2) ws2 = v;
+            else ws3 = v;
+        } else {
+            const uint4 v = *reinterpret_cast<const uint4 *>(p.x + xoff[j - 4] + k0);
+            if (j == 4) xs0 = v;
+            else if (j == 5) xs1 = v;
+            else if (j == 6) xs2 = v;
+            else xs3 = v;
+        }
+    };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int nchunks = p.model_dim / kChunk;
-    PLX_ISSUE(0);
-    PLX_STORE(0);
-    if (nchunks > 1) PLX_ISSUE(kChunk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue_piece(j, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) store_piece(j, 0);
+    if (nchunks > 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue_piece(j, kChunk);
     __syncthreads();
     for (int ch = 0; ch < nchunks; ++ch) {
         const int buf = ch & 1;
+        // Chunk ch + 1 (loaded during chunk ch - 1) goes to the other buffer,
+        // free since the barrier that ended chunk ch - 1, in the first k half;
+        // the registers take chunk ch + 2 in the second.  Both are spread
+        // over the MFMAs.  On the last chunks the loads repeat the last chunk
+        // and the stores hit a buffer nobody reads again.
+        const int k2 = min(ch + 2, nchunks - 1) * kChunk;
 #pragma unroll
         for (int kk = 0; kk < kChunk / 32; ++kk) {
-            bf16x8_t a[4], b[4];
+            bf16x8_t b[TJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[i] = __builtin_bit_cast(
+            for (int j = 0; j < TJ; ++j)
+                b[j] = __builtin_bit_cast(
                     bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                  wt[buf] + (64 * wr + 16 * i + c) * kLdsRow + 64 * kk + 16 * g));
-                b[i] = __builtin_bit_cast(
+                                  xt[buf] + (16 * TJ * wc + 16 * j + c) * kLdsRow + 64 * kk + 16 * g));
+            auto aread = [&](int i) __attribute__((always_inline)) {
+                return __builtin_bit_cast(
                     bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                  xt[buf] + (64 * wc + 16 * i + c) * kLdsRow + 64 * kk + 16 * g));
+                                  wt[buf] + (16 * TI * wr + 16 * i + c) * kLdsRow + 64 * kk + 16 * g));
+            };
+            bf16x8_t a = aread(0);
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const bf16x8_t an = aread(i + 1 < TI ? i + 1 : i);
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < 8 / TI; ++q) {
+                    if (kk == 0) store_piece(i * (8 / TI) + q, 1 - buf);
+                    else issue_piece(i * (8 / TI) + q, k2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                a = an;
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        // the next chunk (loaded during this one) goes to the other buffer,
-        // free since the barrier that ended chunk ch - 1
-        if (ch + 1 < nchunks) {
-            PLX_STORE(1 - buf);
-            if (ch + 2 < nchunks) PLX_ISSUE((ch + 2) * kChunk);
         }
         __syncthreads();
     }
-#undef PLX_ISSUE
-#undef PLX_STORE
 
-    // acc[i][j]: lane (c, g) holds stacked rows row0 + 64 wr + 16 i + 4g + (0..3)
-    // of token t0 + 64 wc + 16 j + c
+    // acc[i][j]: lane (c, g) holds stacked rows row0 + 16 TI wr + 16 i + 4g +
+    // (0..3) of token t0 + 16 TJ wc + 16 j + c
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = row0 + 64 * wr + 16 * i + 4 * g;  // the 16-row tile never straddles N
+    for (int i = 0; i < TI; ++i) {
+        const int r = row0 + 16 * TI * wr + 16 * i + 4 * g;  // the 16-row tile never straddles N
         const bool is_r = r >= p.n;
         const int f = r - (is_r ? p.n : 0);
         const int h = f / p.head_dim, e = f % p.head_dim;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = t0 + 64 * wc + 16 * j + c;
+        for (int j = 0; j < TJ; ++j) {
+            const int t = t0 + 16 * TJ * wc + 16 * j + c;
             if (t >= T) continue;
             const int64_t off = (int64_t)t * (is_r ? p.r_st : p.q_st) +
                                 (int64_t)h * (is_r ? p.r_sh : p.q_sh) + e;
@@ -280,19 +311,28 @@ __global__ __launch_bounds__(256, 2) void proj_tiled_kernel(ProjParams p) {
     }
 }
 
+template <class C>
+hipError_t launch_tiled(const ProjParams &p, hipStream_t stream) {
+    const dim3 grid((unsigned)(2 * p.n / C::kMT), (unsigned)((p.tokens + C::kNT - 1) / C::kNT));
+    if (p.out_bf16)
+        hipLaunchKernelGGL((proj_tiled_kernel<C, true>), grid, dim3(C::kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((proj_tiled_kernel<C, false>), grid, dim3(C::kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Up to 16 tokens (decode): token blocks of 16 and the weight-streaming
-// kernel; up to 128: blocks of 64; beyond: the LDS-tiled GEMM.
+// kernel; up to 128: blocks of 64; beyond: the LDS-tiled GEMM, with 256 x 256
+// tiles when 2N is a multiple of 256 and that grid fills the CUs, else with
+// 128 x 128 tiles (2N is always a multiple of 128: head_dim is 64 or 128).
 hipError_t launch_qr_projection(const ProjParams &p, hipStream_t stream) {
     if (p.tokens <= 16) return launch_nt<1>(p, stream);
     if (p.tokens <= 128) return launch_nt<4>(p, stream);
-    const dim3 grid((unsigned)(2 * p.n / kTile), (unsigned)((p.tokens + kTile - 1) / kTile));
-    if (p.out_bf16)
-        hipLaunchKernelGGL(proj_tiled_kernel<true>, grid, dim3(256), 0, stream, p);
-    else
-        hipLaunchKernelGGL(proj_tiled_kernel<false>, grid, dim3(256), 0, stream, p);
-    return hipGetLastError();
+    const int64_t big = (int64_t)(2 * p.n / Tile256::kMT) * ((p.tokens + Tile256::kNT - 1) / Tile256::kNT);
+    if ((2 * p.n) % Tile256::kMT == 0 && big >= kCUs) return launch_tiled<Tile256>(p, stream);
+    return launch_tiled<Tile128>(p, stream);
 }
 
 }  // namespace plx

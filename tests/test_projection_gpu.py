@@ -41,6 +41,26 @@ def test_every_element(gpu, T, D, Hq, d, out_dtype):
     assert_parity(rho.reshape(T, -1), rr, tau, what="rho")
 
 
+@pytest.mark.parametrize("T,D,Hq,d", [(4096, 2048, 16, 128), (4100, 1024, 16, 128),
+                                      (8200, 512, 8, 128), (4100, 256, 1, 64)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_prefill_token_counts(gpu, T, D, Hq, d, out_dtype):
+    """Token counts of prefill (the LDS-tiled GEMM: 256 x 256 tiles where 2N
+    is a multiple of 256 and the grid fills the device, 128 x 128 tiles for
+    Hq = 1, d = 64; ragged last token tiles): sampled rows against the oracle,
+    the first and last tiles and rows across tile edges."""
+    x, w_q, w_r = weights(T, D, Hq * d, T + D + Hq, gpu)
+    q, rho = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=Hq, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    rows = sorted(set(range(64)) | set(range(250, 262)) | set(range(2040, 2060)) |
+                  set(range(T - 70, T)))
+    idx = torch.tensor(rows)
+    rq, rr = oracle.qr_projection(host_array(x[idx.to(gpu)]), host_array(w_q), host_array(w_r))
+    tau = 1e-5 if out_dtype == torch.float32 else 2.0 ** -8
+    assert_parity(q[idx.to(gpu)].reshape(len(rows), -1), rq, tau, what="q")
+    assert_parity(rho[idx.to(gpu)].reshape(len(rows), -1), rr, tau, what="rho")
+
+
 def test_zero_probe_weights_give_zero_rho(gpu):
     x, w_q, w_r = weights(8, 2048, 2048, 70, gpu)
     _, rho = plx.parallax_qr_projection(x, w_q, torch.zeros_like(w_r), num_q_heads=16)
