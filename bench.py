@@ -44,8 +44,10 @@ _COMMON = ["parallax_local_linear_decode_amd/csrc/kernels.hpp",
            "parallax_local_linear_decode_amd/csrc/api.hip",
            "parallax_local_linear_decode_amd/build.py"]
 KERNEL_SOURCES = {  # what the kernels of a workload are built from
-    "decode": ["parallax_local_linear_decode_amd/csrc/decode.hip"] + _COMMON,
-    "paged": ["parallax_local_linear_decode_amd/csrc/decode.hip"] + _COMMON,
+    "decode": ["parallax_local_linear_decode_amd/csrc/decode.hip",
+               "parallax_local_linear_decode_amd/csrc/lla_row.hpp"] + _COMMON,
+    "paged": ["parallax_local_linear_decode_amd/csrc/decode.hip",
+              "parallax_local_linear_decode_amd/csrc/lla_row.hpp"] + _COMMON,
     "prefill": ["parallax_local_linear_decode_amd/csrc/prefill.hip"] + _COMMON,
     "prefill_bwd": ["parallax_local_linear_decode_amd/csrc/prefill_bwd.hip"] + _COMMON,
 }

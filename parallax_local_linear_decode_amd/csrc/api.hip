@@ -465,19 +465,17 @@ PLX_EXPORT parallax_status_t parallax_decode_lla(const parallax_decode_args_t *d
     lpar.d = dec->head_dim;
     lpar.lambda = lla->lambda;
 
-    auto run_decode = [&](const plx::DecodeParams &dp) {
+    auto run_decode = [&](const plx::DecodeParams &dp, const plx::LlaParams *step) {
         return plx::launch_decode(dp, dec->kv_dtype, dec->head_dim, lp.dplan.group, lp.dplan.paged,
-                                  dec->batch, stream);
+                                  dec->batch, stream, step);
     };
     hipError_t e = plx::launch_lla_zero(dir, n, stream);  // rho = 0: the sweep gives kbar
-    if (e == hipSuccess) e = run_decode(sweep);
+    if (e == hipSuccess) e = run_decode(sweep, nullptr);
     if (e == hipSuccess) e = plx::launch_lla_init(lpar, stream);
     sweep.out = ok;
-    for (int it = 0; it < lla->iterations && e == hipSuccess; ++it) {
-        e = run_decode(sweep);
-        if (e == hipSuccess) e = plx::launch_lla_step(lpar, stream);
-    }
-    if (e == hipSuccess) e = run_decode(fin);
+    // each iteration: the sweep, then the step inside its merge kernel
+    for (int it = 0; it < lla->iterations && e == hipSuccess; ++it) e = run_decode(sweep, &lpar);
+    if (e == hipSuccess) e = run_decode(fin, nullptr);
     if (e == hipSuccess) e = plx::launch_lla_finish(lpar, stream);
     return hip_status(e, "lla launch");
 }

@@ -45,6 +45,7 @@
 //   load covers whole rows; per-token dot products are summed across the row
 //   with DPP butterflies; values accumulate with fp32 FMA.
 #include "kernels.hpp"
+#include "lla_row.hpp"
 
 #include <math.h>
 
@@ -624,54 +625,75 @@ __global__ __launch_bounds__(64 * kValuWaves) void decode_valu_kernel(DecodePara
 // ================================================================ merge ===
 
 // One workgroup per (batch, KV head): combine the split records of rows
-// that used more than one split and write o.
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
+// that used more than one split and write o.  LLA: the decode is a sweep of
+// the solved probe's conjugate gradients (keys as values, rho = the search
+// direction); the rows' outputs stay in LDS (a single-split unit's are read
+// back from where the split kernel wrote them) and one wave per row runs the
+// step right away, for every unit, saving a launch per iteration.
+template <int D, int G, bool PAGED, bool LLA>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, LlaParams lq) {
     constexpr int REC = partial_floats(D);
+    // LLA: the rows' sweep outputs stay here for the conjugate-gradient step
+    __shared__ float osh[LLA ? G : 1][D];
     const int unit = blockIdx.x;
     const int b = unit / p.num_kv_heads;
     const int hk = unit % p.num_kv_heads;
     int L, tb, tbase, nsp;
     row_extent<PAGED>(p, b, L, tb, tbase, nsp);
-    if (nsp <= 1) return;  // written by the split kernel
-    const float *recs = p.partials + (int64_t)unit * p.nsplit * G * REC;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-        const int g = idx / D, e = idx % D;
-        float M = -INFINITY, Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
-        for (int c0 = 0; c0 < nsp; c0 += 4) {  // four records' loads in flight at once
-            float mm[4], zz[4], rr[4], aa[4], bb[4];
+    if (nsp <= 1) {  // written by the split kernel
+        if constexpr (!LLA) return;
+        for (int idx = threadIdx.x; idx < G * D; idx += 256)
+            osh[idx / D][idx % D] =
+                p.out[b * p.out_sb + (int64_t)(hk * G + idx / D) * p.out_sh + idx % D];
+    } else {
+        const float *recs = p.partials + (int64_t)unit * p.nsplit * G * REC;
+        for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+            const int g = idx / D, e = idx % D;
+            float M = -INFINITY, Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
+            for (int c0 = 0; c0 < nsp; c0 += 4) {  // four records' loads in flight at once
+                float mm[4], zz[4], rr[4], aa[4], bb[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float *rec = recs + (min(c0 + i, nsp - 1) * G + g) * REC;
-                const bool live = c0 + i < nsp;
-                mm[i] = live ? rec[2 * D] : -INFINITY;
-                zz[i] = rec[2 * D + 1];
-                rr[i] = rec[2 * D + 2];
-                aa[i] = rec[e];
-                bb[i] = rec[D + e];
-            }
-            const float Mn = fmaxf(fmaxf(M, fmaxf(mm[0], mm[1])), fmaxf(mm[2], mm[3]));
-            const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-            Z *= sc;
-            R *= sc;
-            A *= sc;
-            B *= sc;
+                for (int i = 0; i < 4; ++i) {
+                    const float *rec = recs + (min(c0 + i, nsp - 1) * G + g) * REC;
+                    const bool live = c0 + i < nsp;
+                    mm[i] = live ? rec[2 * D] : -INFINITY;
+                    zz[i] = rec[2 * D + 1];
+                    rr[i] = rec[2 * D + 2];
+                    aa[i] = rec[e];
+                    bb[i] = rec[D + e];
+                }
+                const float Mn = fmaxf(fmaxf(M, fmaxf(mm[0], mm[1])), fmaxf(mm[2], mm[3]));
+                const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+                Z *= sc;
+                R *= sc;
+                A *= sc;
+                B *= sc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float al = mm[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[i] - Mn);
-                Z += al * zz[i];
-                R += al * rr[i];
-                A += al * aa[i];
-                B += al * bb[i];
+                for (int i = 0; i < 4; ++i) {
+                    const float al = mm[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[i] - Mn);
+                    Z += al * zz[i];
+                    R += al * rr[i];
+                    A += al * aa[i];
+                    B += al * bb[i];
+                }
+                M = Mn;
             }
-            M = Mn;
+            const float o = finish(A, B, Z, R);
+            if constexpr (LLA) osh[g][e] = o;
+            else p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = o;
         }
-        p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = finish(A, B, Z, R);
+    }
+    if constexpr (LLA) {
+        __syncthreads();
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        for (int g = wave; g < G; g += 4)
+            lla_step_row(lq, (int64_t)b * lq.num_q_heads + hk * G + g, true, lane, osh[g]);
     }
 }
 
 template <int D, int G, bool PAGED>
-hipError_t launch_all(const DecodeParams &p, bool bf16, int batch, hipStream_t stream) {
+hipError_t launch_all(const DecodeParams &p, bool bf16, int batch, hipStream_t stream,
+                      const LlaParams *lla) {
     // Workgroup w takes split w / units of unit w % units.  Consecutive
     // workgroups are dealt round-robin to the eight XCDs, so in this order
     // every XCD gets every eighth unit with all of its splits; in unit-major
@@ -696,25 +718,31 @@ hipError_t launch_all(const DecodeParams &p, bool bf16, int batch, hipStream_t s
         hipLaunchKernelGGL((decode_valu_kernel<D, G, PAGED>), grid, dim3(64 * kValuWaves), 0,
                            stream, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.nsplit == 1) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<D, G, PAGED>), dim3(units), dim3(256), 0, stream, p);
+    if (e != hipSuccess) return e;
+    if (lla != nullptr)
+        hipLaunchKernelGGL((decode_merge_kernel<D, G, PAGED, true>), dim3(units), dim3(256), 0,
+                           stream, p, *lla);
+    else if (p.nsplit > 1)
+        hipLaunchKernelGGL((decode_merge_kernel<D, G, PAGED, false>), dim3(units), dim3(256), 0,
+                           stream, p, LlaParams{});
     return hipGetLastError();
 }
 
 template <int D, int G>
-hipError_t launch_g(const DecodeParams &p, bool bf16, bool paged, int batch, hipStream_t s) {
-    return paged ? launch_all<D, G, true>(p, bf16, batch, s)
-                 : launch_all<D, G, false>(p, bf16, batch, s);
+hipError_t launch_g(const DecodeParams &p, bool bf16, bool paged, int batch, hipStream_t s,
+                    const LlaParams *lla) {
+    return paged ? launch_all<D, G, true>(p, bf16, batch, s, lla)
+                 : launch_all<D, G, false>(p, bf16, batch, s, lla);
 }
 
 template <int D>
 hipError_t launch_d(const DecodeParams &p, bool bf16, int group, bool paged, int batch,
-                    hipStream_t s) {
+                    hipStream_t s, const LlaParams *lla) {
     switch (group) {
-        case 1: return launch_g<D, 1>(p, bf16, paged, batch, s);
-        case 2: return launch_g<D, 2>(p, bf16, paged, batch, s);
-        case 4: return launch_g<D, 4>(p, bf16, paged, batch, s);
-        case 8: return launch_g<D, 8>(p, bf16, paged, batch, s);
+        case 1: return launch_g<D, 1>(p, bf16, paged, batch, s, lla);
+        case 2: return launch_g<D, 2>(p, bf16, paged, batch, s, lla);
+        case 4: return launch_g<D, 4>(p, bf16, paged, batch, s, lla);
+        case 8: return launch_g<D, 8>(p, bf16, paged, batch, s, lla);
         default: return hipErrorInvalidValue;
     }
 }
@@ -722,10 +750,10 @@ hipError_t launch_d(const DecodeParams &p, bool bf16, int group, bool paged, int
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams &p, int kv_dtype, int d, int group, bool paged,
-                         int batch, hipStream_t stream) {
+                         int batch, hipStream_t stream, const LlaParams *lla) {
     const bool bf16 = kv_dtype == 1;
-    if (d == 128) return launch_d<128>(p, bf16, group, paged, batch, stream);
-    if (d == 64) return launch_d<64>(p, bf16, group, paged, batch, stream);
+    if (d == 128) return launch_d<128>(p, bf16, group, paged, batch, stream, lla);
+    if (d == 64) return launch_d<64>(p, bf16, group, paged, batch, stream, lla);
     return hipErrorInvalidValue;
 }
 

@@ -123,13 +123,15 @@ struct ProjParams {
 
 // Launchers (defined next to their kernels).  They return the HIP status of
 // the launch.
+// lla: the decode is a sweep of the solved probe's conjugate gradients
+// (keys as values, rho = the search direction); the merge kernel then also
+// runs one step on every row (and runs even when no row has two splits).
 hipError_t launch_decode(const DecodeParams &p, int kv_dtype, int d, int group, bool paged,
-                         int batch, hipStream_t stream);
+                         int batch, hipStream_t stream, const LlaParams *lla = nullptr);
 hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream);
 hipError_t launch_prefill_backward(const PrefillBwdParams &p, int d, hipStream_t stream);
 hipError_t launch_lla_zero(float *a, int64_t n, hipStream_t stream);
 hipError_t launch_lla_init(const LlaParams &p, hipStream_t stream);
-hipError_t launch_lla_step(const LlaParams &p, hipStream_t stream);
 hipError_t launch_lla_finish(const LlaParams &p, hipStream_t stream);
 hipError_t launch_qr_projection(const ProjParams &p, hipStream_t stream);
 

@@ -1,17 +1,18 @@
 // lla.hip -- per-row vector kernels of local linear attention's solved probe
 // (page "Parallax: Parameterized Local Linear Attention Gives Transformers a
 // 'Second Eye'", section 1.2: each token solves S x = mu by conjugate
-// gradients, every iteration one sweep over the KV cache).
+// gradients, every iteration one sweep over the KV cache).  The step itself
+// (lla_row.hpp) runs inside the decode merge kernel after each sweep.
 //
 // For decode row (b, h) with softmax weights p over its keys the system is
 // (S_KK + lam I) x = mu, mu = kbar - q, S_KK = sum p_j (k_j - kbar)(k_j - kbar)^T.
 // The sweep is the decode kernel itself with the keys passed as values: its
 // output with probe y is kbar - S_KK y, so S_KK y = kbar - o(V = K, rho = y),
-// and kbar = o(V = K, rho = 0).  These kernels hold the conjugate-gradient
-// state between sweeps: one 64-lane wave per row, head-dim element e in lane
-// e % 64 (two per lane at d = 128); dot products reduce across the wave and
-// every lane takes lane 0's sum, so the update is the same on every lane.
+// and kbar = o(V = K, rho = 0).  These kernels set up and read out the
+// conjugate-gradient state: one 64-lane wave per row, head-dim element e in
+// lane e % 64 (two per lane at d = 128).
 #include "kernels.hpp"
+#include "lla_row.hpp"
 
 #include <algorithm>
 
@@ -19,12 +20,6 @@ namespace plx {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wave per row
-
-__device__ __forceinline__ float wave_sum(float s) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-    return __shfl(s, 0);
-}
 
 struct RowView {
     int64_t u;  // row index b * Hq + h
@@ -66,60 +61,11 @@ __global__ __launch_bounds__(256) void lla_init_kernel(LlaParams p) {
         }
         s += mu * mu;
     }
-    s = wave_sum(s);
+    s = lla_wave_sum(s);
     if (rv.live && lane == 0) {
         p.rs[2 * rv.u] = s;
         p.rs[2 * rv.u + 1] = s;
     }
-}
-
-// One conjugate-gradient step after the sweep o_k = o(V = K, rho = dir):
-// A dir = (kbar - o_k) + lam dir; alpha = rs / dir.A dir; x += alpha dir;
-// r -= alpha A dir; beta = |r|^2 / rs; dir = r + beta dir.
-__global__ __launch_bounds__(256) void lla_step_kernel(LlaParams p) {
-    const RowView rv = row_of(p);
-    const int lane = threadIdx.x % 64;
-    const int64_t off = rv.u * p.d;
-    constexpr int kMaxPer = 2;  // d <= 128
-    float ap[kMaxPer], dv[kMaxPer];
-    float pap = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-        const int e = lane + 64 * i;
-        ap[i] = dv[i] = 0.0f;
-        if (e < p.d) {
-            dv[i] = p.dir[off + e];
-            ap[i] = (p.kbar[off + e] - p.ok[off + e]) + p.lambda * dv[i];
-            pap += dv[i] * ap[i];
-        }
-    }
-    pap = wave_sum(pap);
-    const float rs = p.rs[2 * rv.u];
-    const float alpha = pap > 0.0f && rs > 0.0f ? rs / pap : 0.0f;
-    float rr[kMaxPer];
-    float rsn = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-        const int e = lane + 64 * i;
-        rr[i] = 0.0f;
-        if (e < p.d) {
-            rr[i] = p.r[off + e] - alpha * ap[i];
-            rsn += rr[i] * rr[i];
-        }
-    }
-    rsn = wave_sum(rsn);
-    const float beta = rs > 0.0f ? rsn / rs : 0.0f;
-    if (!rv.live) return;
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-        const int e = lane + 64 * i;
-        if (e < p.d) {
-            p.x[off + e] += alpha * dv[i];
-            p.r[off + e] = rr[i];
-            p.dir[off + e] = rr[i] + beta * dv[i];
-        }
-    }
-    if (lane == 0) p.rs[2 * rv.u] = rsn;
 }
 
 // rho_out = x; resid = |r| / |mu| (0 for a row with mu = 0).
@@ -151,11 +97,6 @@ hipError_t launch_lla_zero(float *a, int64_t n, hipStream_t stream) {
 
 hipError_t launch_lla_init(const LlaParams &p, hipStream_t stream) {
     hipLaunchKernelGGL(lla_init_kernel, dim3(row_blocks(p)), dim3(64 * kRowsPerBlock), 0, stream, p);
-    return hipGetLastError();
-}
-
-hipError_t launch_lla_step(const LlaParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL(lla_step_kernel, dim3(row_blocks(p)), dim3(64 * kRowsPerBlock), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -61,6 +61,20 @@ def test_prefill_token_counts(gpu, T, D, Hq, d, out_dtype):
     assert_parity(rho[idx.to(gpu)].reshape(len(rows), -1), rr, tau, what="rho")
 
 
+def test_prefill_token_counts_into_strided_views(gpu):
+    """The 256 x 256 tiled GEMM writing bf16 q and rho into the two halves of
+    one [T, 2, Hq, d] buffer (row stride 2 Hq d): equal to contiguous outputs."""
+    T, D, Hq, d = 4200, 1024, 16, 128
+    x, w_q, w_r = weights(T, D, Hq * d, 76, gpu)
+    buf = torch.full((T, 2, Hq, d), float("nan"), dtype=torch.bfloat16, device=gpu)
+    q, rho = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=Hq, out_dtype=torch.bfloat16,
+                                        q=buf[:, 0], rho=buf[:, 1])
+    qc, rc = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=Hq, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(q, qc) and torch.equal(rho, rc)
+    assert not torch.isnan(buf.float()).any()
+
+
 def test_zero_probe_weights_give_zero_rho(gpu):
     x, w_q, w_r = weights(8, 2048, 2048, 70, gpu)
     _, rho = plx.parallax_qr_projection(x, w_q, torch.zeros_like(w_r), num_q_heads=16)
