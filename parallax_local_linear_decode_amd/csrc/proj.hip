@@ -8,14 +8,15 @@
 // outputs, and the results land directly in the strided [T, Hq, d] layouts
 // the attention kernels read (fp32 for decode, bf16 for prefill).
 //
-// Workgroup: 32 stacked weight rows x 16 * NT tokens; its eight waves split
+// Workgroup: 16 RT stacked weight rows x 16 NT tokens; its eight waves split
 // the model dimension D into eighths, each accumulating partial 16 x 16
-// tiles (two row tiles per token block, so one token load serves two weight
-// loads) with 16x16x32 bf16 MFMAs and fp32 accumulation; the partials are
-// summed in LDS in wave order.  At decode sizes (a few tokens) the product is
-// bound by streaming the weights from HBM: a wave issues all loads of its
-// eighth before the MFMAs, and the grid has 2N / 32 workgroups of eight
-// waves, so the whole weight set is requested at once.
+// tiles with 16x16x32 bf16 MFMAs and fp32 accumulation; the partials are
+// summed in LDS in wave order.  At decode sizes (up to 64 tokens) the product
+// is bound by streaming the weights from HBM: one row tile per workgroup
+// (2N / 16 workgroups, 256 for 2N = 4096, so every CU streams), and a wave
+// issues all loads of its eighth of D before the MFMAs, so the whole weight
+// set is requested at once.  From 65 to 128 tokens two row tiles per
+// workgroup let one token load serve two weight loads.
 #include "kernels.hpp"
 
 #include <type_traits>
@@ -31,10 +32,10 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t *p) {
 }
 
 constexpr int kWaves = 8;  // waves per workgroup, each one eighth of D
-constexpr int kRows = 32;  // stacked weight rows per workgroup (two 16-row tiles)
 
-template <int NT, bool BF16OUT>
+template <int RT, int NT, bool BF16OUT>
 __global__ __launch_bounds__(64 * kWaves) void proj_kernel(ProjParams p) {
+    constexpr int kRows = 16 * RT;  // stacked weight rows per workgroup
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop
     const int c = lane & 15;
@@ -47,9 +48,9 @@ __global__ __launch_bounds__(64 * kWaves) void proj_kernel(ProjParams p) {
 
     // A operands: weight rows f0 + 16 rt + c, model dims k + 8g .. k + 8g + 7;
     // B operands: token rows t0 + 16 nt + c, the same model dims.
-    const uint16_t *w[2];
+    const uint16_t *w[RT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
         w[rt] = (is_r ? p.w_r : p.w_q) + (int64_t)(f0 + 16 * rt + c) * p.w_sn + 8 * g;
     const uint16_t *xr[NT];
 #pragma unroll
@@ -59,22 +60,22 @@ __global__ __launch_bounds__(64 * kWaves) void proj_kernel(ProjParams p) {
     const int kq = p.model_dim / kWaves;
     const int k_begin = wave * kq;
     const int steps = kq / 32;
-    f32x4_t acc[2][NT];
+    f32x4_t acc[RT][NT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // CH steps' loads are issued together, then their MFMAs: at decode sizes
-    // (NT = 1) a wave's whole eighth of D = 2048 is in flight per lane
-    constexpr int CH = NT == 1 ? 8 : 2;
+    // CH steps' loads are issued together, then their MFMAs: with one row
+    // tile a wave's whole eighth of D = 2048 is in flight per lane
+    constexpr int CH = RT == 1 ? 8 : 2;
     int st = 0;
     for (; st + CH <= steps; st += CH) {
-        bf16x8_t a[CH][2], b[CH][NT];
+        bf16x8_t a[CH][RT], b[CH][NT];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int k = k_begin + 32 * (st + i);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) a[i][rt] = ld_bf16x8(w[rt] + k);
+            for (int rt = 0; rt < RT; ++rt) a[i][rt] = ld_bf16x8(w[rt] + k);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) b[i][nt] = ld_bf16x8(xr[nt] + k);
         }
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(64 * kWaves) void proj_kernel(ProjParams p) {
 #pragma unroll
         for (int i = 0; i < CH; ++i)
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
                     acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][rt], b[i][nt],
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(64 * kWaves) void proj_kernel(ProjParams p) {
     for (; st < steps; ++st) {
         const int k = k_begin + 32 * st;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
             const bf16x8_t a = ld_bf16x8(w[rt] + k);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
@@ -102,9 +103,9 @@ __global__ __launch_bounds__(64 * kWaves) void proj_kernel(ProjParams p) {
         }
     }
 
-    __shared__ f32x4_t red[kWaves][2][NT][64];
+    __shared__ f32x4_t red[kWaves][RT][NT][64];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) red[wave][rt][nt][lane] = acc[rt][nt];
     __syncthreads();
@@ -112,8 +113,8 @@ __global__ __launch_bounds__(64 * kWaves) void proj_kernel(ProjParams p) {
     // wave w finishes tiles u = w, w + 8, ... of the 2 NT (row tile, token
     // block) pairs; lane (c, g) holds features f0 + 16 rt + 4g + j (j = 0..3)
     // of token t0 + 16 nt + c
-    for (int u = wave; u < 2 * NT; u += kWaves) {
-        const int rt = u % 2, nt = u / 2;
+    for (int u = wave; u < RT * NT; u += kWaves) {
+        const int rt = u % RT, nt = u / RT;
         const int t = t0 + 16 * nt + c;
         if (t >= T) continue;
         f32x4_t s = red[0][rt][nt][lane];
@@ -135,13 +136,13 @@ __global__ __launch_bounds__(64 * kWaves) void proj_kernel(ProjParams p) {
     }
 }
 
-template <int NT>
+template <int RT, int NT>
 hipError_t launch_nt(const ProjParams &p, hipStream_t stream) {
-    const dim3 grid((unsigned)(2 * p.n / kRows), (unsigned)((p.tokens + 16 * NT - 1) / (16 * NT)));
+    const dim3 grid((unsigned)(2 * p.n / (16 * RT)), (unsigned)((p.tokens + 16 * NT - 1) / (16 * NT)));
     if (p.out_bf16)
-        hipLaunchKernelGGL((proj_kernel<NT, true>), grid, dim3(64 * kWaves), 0, stream, p);
+        hipLaunchKernelGGL((proj_kernel<RT, NT, true>), grid, dim3(64 * kWaves), 0, stream, p);
     else
-        hipLaunchKernelGGL((proj_kernel<NT, false>), grid, dim3(64 * kWaves), 0, stream, p);
+        hipLaunchKernelGGL((proj_kernel<RT, NT, false>), grid, dim3(64 * kWaves), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -324,12 +325,14 @@ hipError_t launch_tiled(const ProjParams &p, hipStream_t stream) {
 }  // namespace
 
 // Up to 16 tokens (decode): token blocks of 16 and the weight-streaming
-// kernel; up to 128: blocks of 64; beyond: the LDS-tiled GEMM, with 256 x 256
+// kernel; up to 64: blocks of 64; up to 128: blocks of 64 with two row tiles
+// per workgroup (one row tile doubled the weight re-reads there); beyond: the LDS-tiled GEMM, with 256 x 256
 // tiles when 2N is a multiple of 256 and that grid fills the CUs, else with
 // 128 x 128 tiles (2N is always a multiple of 128: head_dim is 64 or 128).
 hipError_t launch_qr_projection(const ProjParams &p, hipStream_t stream) {
-    if (p.tokens <= 16) return launch_nt<1>(p, stream);
-    if (p.tokens <= 128) return launch_nt<4>(p, stream);
+    if (p.tokens <= 16) return launch_nt<1, 1>(p, stream);
+    if (p.tokens <= 64) return launch_nt<1, 4>(p, stream);
+    if (p.tokens <= 128) return launch_nt<2, 4>(p, stream);
     const int64_t big = (int64_t)(2 * p.n / Tile256::kMT) * ((p.tokens + Tile256::kNT - 1) / Tile256::kNT);
     if ((2 * p.n) % Tile256::kMT == 0 && big >= kCUs) return launch_tiled<Tile256>(p, stream);
     return launch_tiled<Tile128>(p, stream);
