@@ -101,6 +101,24 @@ def time_launches(torch, launch, n_bufs, steps, warmup):
     return start.elapsed_time(end) / 1000.0  # seconds
 
 
+def single_call_us(torch, launch, n_bufs, calls=50):
+    """Latency of one isolated call: events around it, the device idle
+    before it (synchronised), cold input copy each time; median in us."""
+    stream = torch.cuda.current_stream()
+    ts = []
+    for i in range(calls):
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        launch(i % n_bufs)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ts.append(start.elapsed_time(end) * 1e3)
+    ts.sort()
+    return round(ts[len(ts) // 2], 2)
+
+
 def make_decode_launcher(torch, plx, sets, out, split, window=0):
     """Pre-marshalled C-ABI calls, one per input copy, so the host loop is a
     single ctypes call per step."""
@@ -204,6 +222,7 @@ def run_decode(args, torch, plx):
     secs = time_launches(torch, launch, n_bufs, args.steps, args.warmup)
     per = secs / args.steps
     warm = time_launches(torch, launch, 1, args.steps, args.warmup) / args.steps
+    single = single_call_us(torch, launch, n_bufs)
     gbps = nbytes / per / 1e9
     traffic = traffic_for("decode") if W <= 0 else None
     stream_ref = read_stream(torch, plx, kv_bytes, n_bufs, args.steps, args.warmup)
@@ -219,6 +238,7 @@ def run_decode(args, torch, plx):
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s": B / per, "kv_tokens_per_s": B * Lw / per,
         "warm_cache_gbps": round(nbytes / warm / 1e9, 2),
+        "single_call_us": single,
         "read_stream": stream_ref,
         "frac_of_read_stream": None if not stream_ref else round(gbps / stream_ref["gbps"], 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
@@ -708,7 +728,7 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": rec["dtype"], "data": "synthetic (seeded N(0,1) q/k/v, N(0,0.1^2) rho)",
             "config": rec["config"]}
-    for k in ("pct_hbm_peak", "tokens_per_s", "kv_tokens_per_s", "warm_cache_gbps",
+    for k in ("pct_hbm_peak", "tokens_per_s", "kv_tokens_per_s", "warm_cache_gbps", "single_call_us",
               "read_stream", "frac_of_read_stream", "mfma_util", "max_rel_residual",
               "parallax_ms_per_step", "lla_over_parallax_time", "sweep_bytes_per_s_gb"):
         if k in rec:
