@@ -481,9 +481,40 @@ def parallax_prefill_backward(q, rho, k, v, dout, out, o_sa, lse, rmean, *, scal
     return dq, drho, dk, dv
 
 
+class _PrefillFunction(torch.autograd.Function):
+    """parallax_prefill forward (keeping the per-row statistics) with
+    parallax_prefill_backward as its gradient, for torch autograd."""
+
+    @staticmethod
+    def forward(ctx, q, rho, k, v, scale, window):
+        out, lse, rmean, o_sa = parallax_prefill(q, rho, k, v, scale=scale, window=window,
+                                                 return_stats=True)
+        ctx.save_for_backward(q, rho, k, v, out, o_sa, lse, rmean)
+        ctx.scale, ctx.window = scale, window
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, rho, k, v, out, o_sa, lse, rmean = ctx.saved_tensors
+        # the kernels take dout in bf16, like the other inputs
+        dq, drho, dk, dv = parallax_prefill_backward(
+            q, rho, k, v, dout.to(torch.bfloat16), out, o_sa, lse, rmean, scale=ctx.scale,
+            window=ctx.window)
+        return (dq.to(q.dtype), drho.to(rho.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None)
+
+
+def parallax_prefill_attention(q, rho, k, v, *, scale=None, window=0):
+    """Differentiable causal Parallax prefill: parallax_prefill in the
+    forward, parallax_prefill_backward in the backward (upstream gradients
+    are rounded to bf16 for it, and the input gradients come back in the
+    inputs' dtype).  Same tensors and layouts as parallax_prefill."""
+    return _PrefillFunction.apply(q, rho, k, v, scale, window)
+
+
 __all__ = [
     "parallax_decode", "parallax_decode_workspace_size", "parallax_prefill",
-    "parallax_prefill_backward", "PrefillBackwardArgs", "parallax_decode_lla", "LlaArgs",
+    "parallax_prefill_backward", "parallax_prefill_attention", "PrefillBackwardArgs",
+    "parallax_decode_lla", "LlaArgs",
     "parallax_qr_projection", "ProjectionArgs",
     "parallax_status_string", "parallax_last_error", "parallax_abi_version", "load_library",
     "DecodeArgs", "PrefillArgs", "ParallaxError",

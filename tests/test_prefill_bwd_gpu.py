@@ -200,6 +200,29 @@ def test_full_size_window(gpu):
                   what="window dv")
 
 
+@pytest.mark.parametrize("window", [0, 40])
+def test_autograd_function(gpu, window):
+    """parallax_prefill_attention under torch autograd: the forward equals
+    parallax_prefill, and loss.backward() gives exactly the C ABI backward's
+    gradients (in the inputs' bf16) for the loss sum(dout * out); the oracle
+    checks them too."""
+    q, rho, k, v, dout, scale = case(2, 150, 4, 2, 61, gpu)
+    leaves = [t.clone().requires_grad_(True) for t in (q, rho, k, v)]
+    out = plx.parallax_prefill_attention(*leaves, scale=scale, window=window)
+    (out * dout.float()).sum().backward()
+    torch.cuda.synchronize()
+    stats, grads = forward_backward(q, rho, k, v, dout, scale, window)
+    assert torch.equal(out.detach(), stats[0])
+    for leaf, g in zip(leaves, grads):
+        assert leaf.grad.dtype == torch.bfloat16
+        assert torch.equal(leaf.grad, g.to(torch.bfloat16))
+    h = [host_array(t) for t in (q, rho, k, v, dout)]
+    ref = oracle.prefill_backward(*h[:4], h[4], scale, window=window)
+    for leaf, r, name in zip(leaves, ref, ("dq", "drho", "dk", "dv")):
+        # one more bf16 rounding of the gradient itself: 2^-9 relative
+        assert_parity(leaf.grad, r, TAU_BWD, RMS_BWD, what=f"autograd {name}")
+
+
 def test_graph_replay(gpu):
     """Forward with statistics plus backward captured in one HIP graph
     replays to the eager result, with eager calls in between."""
