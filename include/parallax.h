@@ -222,7 +222,7 @@ parallax_status_t parallax_qr_projection(const parallax_qr_projection_args_t *ar
  * Causal prefill: row i of (b, h) attends to keys 0..i of KV head
  * h / (Hq/Hkv) -- with a local window W >= 1 (see decode) to keys
  * max(0, i-W+1) .. i only.  q, rho bf16 [B, S, Hq, d]; k, v bf16 [B, S, Hkv, d];
- * out fp32 [B, S, Hq, d].  causal must be 1; head_dim must be 128; the GQA
+ * out fp32 [B, S, Hq, d].  causal must be 1; head_dim must be 64 or 128; the GQA
  * group Hq/Hkv must be 1, 2 or 4 (else PARALLAX_ERR_UNSUPPORTED).  Products
  * run on the bf16 matrix cores with fp32 accumulation; the softmax
  * numerators e^{s} and e^{s} t are rounded to bf16 before they multiply V.

@@ -155,8 +155,9 @@ parallax_status_t check_prefill(const parallax_prefill_args_t *a) {
     if (a->causal != 1)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: only causal = 1 is supported");
     if (a->window < 0) return fail(PARALLAX_ERR_INVALID_ARG, "prefill: window must be >= 0");
-    if (a->head_dim != 128)
-        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 128)", a->head_dim);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 64, 128)",
+                    a->head_dim);
     const int group = a->num_q_heads / a->num_kv_heads;
     if (group != 1 && group != 2 && group != 4)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: GQA group %d (supported: 1, 2, 4)", group);

@@ -50,14 +50,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kPfPairs = 4;               // score/value wave pairs per workgroup
 constexpr int kPfRows = 32;               // query rows per pair
 constexpr int kPfKeys = 32;               // keys per tile
-constexpr int kPfD = 128;                 // head dim
-// LDS bytes per tile row.  K rows are read 16 bytes per lane, one row per
-// lane of a 16-lane group: a 16-byte pad puts the 16 rows on distinct banks.
-// V is read through ds_read_b64_tr_b16 (8 bytes per lane, 8 rows per 32
-// lanes): a 32-byte pad puts those rows 8 banks apart, conflict free (with 16
-// bytes they overlapped in pairs; +2% at batch 4 x 8192).
-constexpr int kPfRowBytes = 2 * kPfD + 16;
-constexpr int kPfVRowBytes = 2 * kPfD + 32;
+// LDS bytes per tile row (head dim D = 64 or 128).  K rows are read 16
+// bytes per lane, one row per lane of a 16-lane group: a 16-byte pad puts the
+// 16 rows on distinct banks (strides of 68 and 36 banks).  V is read through
+// ds_read_b64_tr_b16 (8 bytes per lane, 8 rows per 32 lanes): a 32-byte pad
+// puts those rows on distinct bank pairs (strides of 72 and 40 banks; with
+// 16 bytes they overlapped in pairs; +2% at batch 4 x 8192, D = 128).
+template <int D>
+constexpr int pf_row_bytes() { return 2 * D + 16; }
+template <int D>
+constexpr int pf_vrow_bytes() { return 2 * D + 32; }
 constexpr float kSlack = 8.0f;            // base-2 headroom before a row's reference max moves
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -82,17 +84,22 @@ __device__ __forceinline__ float group_max(float x) {
 // attention carries none of its index arithmetic).  STATS: also write lse, r
 // and o_SA for a backward pass (separately too: the plain forward keeps the
 // code it had without them).
-template <int G, bool WIN, bool STATS>
-__global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p) {
-    constexpr int D = kPfD;
+// D = 64: at most 128 registers (a few spill), so two workgroups share a CU
+// (four waves per SIMD; LDS 54 KB each): 703 -> 846 TFLOP/s at batch 4 x 8192.
+template <int D, int G, bool WIN, bool STATS>
+__global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kernel(PrefillParams p) {
     constexpr int KS = D / 32;                      // score MFMAs per 16-key block
     constexpr int DB = D / 16;                      // 16-row blocks of the value sums
+    constexpr int DQ = D / 4;                       // head-dim values per lane group (scores)
+    constexpr int RB = pf_row_bytes<D>(), VRB = pf_vrow_bytes<D>();
+    constexpr int PB = 2 * D * kPfKeys / (128 * kPfPairs);  // tile bytes per thread (16 or 8)
     constexpr int PPH = kPfPairs / G;               // pairs per query head
     constexpr int QB = kPfRows * PPH;               // query rows per head per workgroup
-    constexpr int TILE = kPfKeys * kPfRowBytes;
+    constexpr int TILE = kPfKeys * RB;
+    using Piece = std::conditional_t<PB == 16, uint4, uint2>;
 
     __shared__ __attribute__((aligned(16))) unsigned char ktile[2][TILE];
-    __shared__ __attribute__((aligned(16))) unsigned char vtile[2][kPfKeys * kPfVRowBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char vtile[2][kPfKeys * VRB];
     __shared__ uint4 pbuf[2][kPfPairs][4][64];     // P operands, in value-MFMA lane layout
     __shared__ float abuf[2][kPfPairs][2][16];      // per-row rescale factors
     __shared__ float mfin[kPfPairs][2][16];         // final reference max per row
@@ -125,25 +132,38 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
     const int t_first = (W > 0 ? max(0, qb * QB - W + 1) / kPfKeys : 0) & ~1;
     const int pair_lo = W > 0 ? max(0, r0 - W + 1) / kPfKeys : 0;  // first tile of this pair
 
-    // ---- cooperative tile loads: thread t moves 16 bytes (chunk t%16) of key
+    // ---- cooperative tile loads: thread t moves PB bytes (piece t%16) of key
     // t/16.  Tiles travel through two register stages per operand, so a K or V
     // tile load is issued two iterations before its LDS store.
     const uint16_t *kg = p.k + (int64_t)b * p.k_sb + (int64_t)hk * p.k_sh;
     const uint16_t *vg = p.v + (int64_t)b * p.v_sb + (int64_t)hk * p.v_sh;
-    uint4 kst[2], vst[2];  // K tile j in kst[j & 1], V tile j in vst[j & 1]
-    auto issue_k = [&](int t, uint4 &dst) {
+    // K tile j in register stage kst<j & 1>, V tile j in vst<j & 1>: named
+    // registers picked at compile time (an array of stages was kept in
+    // scratch memory when the compiler indexed it at run time)
+    Piece k0, k1, v0, v1;
+    auto kst = [&](auto par) -> Piece & {
+        if constexpr (decltype(par)::value == 0) return k0;
+        else return k1;
+    };
+    auto vst = [&](auto par) -> Piece & {
+        if constexpr (decltype(par)::value == 0) return v0;
+        else return v1;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto issue_k = [&](int t, Piece &dst) {
         const int key = min(t * kPfKeys + tid / 16, S - 1);
-        dst = ld16(kg + (int64_t)key * p.k_ss + 8 * (tid % 16));
+        dst = *reinterpret_cast<const Piece *>(kg + (int64_t)key * p.k_ss + PB / 2 * (tid % 16));
     };
-    auto issue_v = [&](int t, uint4 &dst) {
+    auto issue_v = [&](int t, Piece &dst) {
         const int key = min(t * kPfKeys + tid / 16, S - 1);
-        dst = ld16(vg + (int64_t)key * p.v_ss + 8 * (tid % 16));
+        dst = *reinterpret_cast<const Piece *>(vg + (int64_t)key * p.v_ss + PB / 2 * (tid % 16));
     };
-    auto store = [&](unsigned char *tile, const uint4 &st) {
-        *reinterpret_cast<uint4 *>(tile + (tid / 16) * kPfRowBytes + 16 * (tid % 16)) = st;
+    auto store = [&](unsigned char *tile, const Piece &st) {
+        *reinterpret_cast<Piece *>(tile + (tid / 16) * RB + PB * (tid % 16)) = st;
     };
-    auto vstore = [&](unsigned char *tile, const uint4 &st) {
-        *reinterpret_cast<uint4 *>(tile + (tid / 16) * kPfVRowBytes + 16 * (tid % 16)) = st;
+    auto vstore = [&](unsigned char *tile, const Piece &st) {
+        *reinterpret_cast<Piece *>(tile + (tid / 16) * VRB + PB * (tid % 16)) = st;
     };
     // End of iteration t (P = t & 1): K tile t+1 replaces tile t-1 (read by
     // the score waves in iteration t-1), V tile t replaces tile t-2 (read by
@@ -156,28 +176,29 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
     // them, the newest included).
     auto advance = [&](int t, auto par) {
         constexpr int P = decltype(par)::value;
-        store(ktile[1 - P], kst[1 - P]);
-        vstore(vtile[P], vst[P]);
-        issue_k(t + 3, kst[1 - P]);
-        issue_v(t + 2, vst[P]);
+        using Q = std::integral_constant<int, 1 - P>;
+        store(ktile[1 - P], kst(Q{}));
+        vstore(vtile[P], vst(par));
+        issue_k(t + 3, kst(Q{}));
+        issue_v(t + 2, vst(par));
         __syncthreads();
     };
     // Prologue, common to both roles (after the score waves' q / rho loads):
     // K tile 0 into LDS; K tiles 1, 2 and V tiles 0, 1 in flight, in the
     // order the loop keeps them.
     auto prologue = [&] {
-        issue_k(t_first, kst[0]);
-        store(ktile[0], kst[0]);
-        issue_k(t_first + 1, kst[1]);
-        issue_v(t_first, vst[0]);
-        issue_k(t_first + 2, kst[0]);
-        issue_v(t_first + 1, vst[1]);
+        issue_k(t_first, kst(I0{}));
+        store(ktile[0], kst(I0{}));
+        issue_k(t_first + 1, kst(I1{}));
+        issue_v(t_first, vst(I0{}));
+        issue_k(t_first + 2, kst(I0{}));
+        issue_v(t_first + 1, vst(I1{}));
         __syncthreads();
     };
 
     if (score_wave) {
         // ---- query-side operands: column block cb < 2 holds q rows r0 + 16cb + c,
-        // cb >= 2 the rho rows of the same queries; head-dim value 32g + 8ks + i
+        // cb >= 2 the rho rows of the same queries; head-dim value DQ g + 8ks + i
         // sits in k-slot 8g + i of score MFMA ks (the slots the K operand uses)
         bf16x8_t xop[4][KS];
 #pragma unroll
@@ -189,7 +210,7 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
                                                (int64_t)head * p.r_sh;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                xop[cb][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + 32 * g + 8 * ks));
+                xop[cb][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + DQ * g + 8 * ks));
         }
         float mref[2] = {-INFINITY, -INFINITY};  // base-2 reference max per query row
 
@@ -204,7 +225,7 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const bf16x8_t kop = __builtin_bit_cast(
-                        bf16x8_t, ld16(kt + (16 * rb + c) * kPfRowBytes + 64 * g + 16 * ks));
+                        bf16x8_t, ld16(kt + (16 * rb + c) * RB + 2 * DQ * g + 16 * ks));
 #pragma unroll
                     for (int cb = 0; cb < 4; ++cb)
                         d1[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, xop[cb][ks],
@@ -335,8 +356,8 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
             for (int db = 0; db < DB; ++db) {
                 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
                 const int col = 16 * db + 4 * (c % 4);
-                const unsigned char *a0 = vt + (4 * g + c / 4) * kPfVRowBytes + 2 * col;
-                const unsigned char *a1 = vt + (16 + 4 * g + c / 4) * kPfVRowBytes + 2 * col;
+                const unsigned char *a0 = vt + (4 * g + c / 4) * VRB + 2 * col;
+                const unsigned char *a1 = vt + (16 + 4 * g + c / 4) * VRB + 2 * col;
                 const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a0);
                 const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -406,10 +427,8 @@ __global__ __launch_bounds__(128 * kPfPairs) void prefill_kernel(PrefillParams p
     }
 }
 
-}  // namespace
-
-hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream) {
-    if (d != kPfD) return hipErrorInvalidValue;
+template <int D>
+hipError_t launch_prefill_d(const PrefillParams &p, hipStream_t stream) {
     const int G = p.num_q_heads / p.num_kv_heads;
     const int units = p.batch * p.num_kv_heads;
     const int qb_rows = kPfRows * kPfPairs / G;
@@ -419,7 +438,7 @@ hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream) {
     const bool stats = p.lse != nullptr || p.rmean != nullptr || p.o_sa != nullptr;
 #define PLX_PREFILL_CASE(G_, W_, S_)                                                         \
     case G_ * 4 + W_ * 2 + S_:                                                               \
-        hipLaunchKernelGGL((prefill_kernel<G_, W_, S_>), grid, block, 0, stream, p);         \
+        hipLaunchKernelGGL((prefill_kernel<D, G_, W_, S_>), grid, block, 0, stream, p);      \
         break;
     switch (G * 4 + (win ? 2 : 0) + (stats ? 1 : 0)) {
         PLX_PREFILL_CASE(1, 0, 0) PLX_PREFILL_CASE(1, 0, 1)
@@ -432,6 +451,14 @@ hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream) {
     }
 #undef PLX_PREFILL_CASE
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams &p, int d, hipStream_t stream) {
+    if (d == 128) return launch_prefill_d<128>(p, stream);
+    if (d == 64) return launch_prefill_d<64>(p, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace plx

@@ -158,7 +158,7 @@ def good_prefill(**over):
     (dict(rho=None), INVALID, "non-NULL"),
     (dict(k_stride_s=-1), INVALID, "non-negative"),
     (dict(causal=0), UNSUPP, "causal"),
-    (dict(head_dim=64), UNSUPP, "head_dim"),
+    (dict(head_dim=96), UNSUPP, "head_dim"),
     (dict(v=FAKE + 2), UNSUPP, "aligned"),
     (dict(q_stride_s=2052), UNSUPP, "16 bytes"),
     (dict(out_stride_h=130), UNSUPP, "16 bytes"),

@@ -29,13 +29,27 @@ def host(*ts):
     return [host_array(t) for t in ts]
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("S", [1, 17, 31, 32, 33, 64, 100, 257])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2), (8, 2)])
-def test_small_all_rows(gpu, S, Hq, Hkv):
-    q, rho, k, v, scale = prefill_inputs(2, S, Hq, Hkv, 128, seed=S * 10 + Hq)
+def test_small_all_rows(gpu, S, Hq, Hkv, d):
+    q, rho, k, v, scale = prefill_inputs(2, S, Hq, Hkv, d, seed=S * 10 + Hq + d)
     ref = oracle.prefill(*host(q, rho, k, v), scale)
     out = run(*(t.to(gpu) for t in (q, rho, k, v)), scale)
-    assert_parity(out, ref, TAU_BF16, RMS_PREFILL, what=f"S={S} {Hq}/{Hkv}")
+    assert_parity(out, ref, TAU_BF16, RMS_PREFILL, what=f"d={d} S={S} {Hq}/{Hkv}")
+
+
+def test_head_dim_64_larger(gpu):
+    """d = 64 over several query blocks and K/V tiles (1000 tokens, 16/8
+    heads), every row, plus the rho = 0 softmax case."""
+    q, rho, k, v, scale = prefill_inputs(2, 1000, 16, 8, 64, seed=64)
+    ref = oracle.prefill(*host(q, rho, k, v), scale)
+    out = run(*(t.to(gpu) for t in (q, rho, k, v)), scale)
+    assert_parity(out, ref, TAU_BF16, RMS_PREFILL, what="d=64 S=1000")
+    zero = torch.zeros_like(rho)
+    ref0 = oracle.prefill(*host(q, zero, k, v), scale)
+    out0 = run(*(t.to(gpu) for t in (q, zero, k, v)), scale)
+    assert_parity(out0, ref0, TAU_BF16, RMS_PREFILL, what="d=64 rho=0")
 
 
 def test_first_row_is_first_value(gpu):

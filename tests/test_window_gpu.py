@@ -108,10 +108,11 @@ def test_window_paged(gpu, kv_dtype):
         assert_parity(out, ref, tau, rms, what=f"paged window={W}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("S", [1, 33, 100, 300])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (8, 2)])
-def test_window_prefill(gpu, S, Hq, Hkv):
-    q, rho, k, v, scale = prefill_inputs(2, S, Hq, Hkv, 128, seed=S + Hq)
+def test_window_prefill(gpu, S, Hq, Hkv, d):
+    q, rho, k, v, scale = prefill_inputs(2, S, Hq, Hkv, d, seed=S + Hq + d)
     hq, hr, hk, hv = (host_array(t) for t in (q, rho, k, v))
     dq, dr, dk, dv = (t.to(gpu) for t in (q, rho, k, v))
     for W in [1, 5, 31, 32, 33, 64, 100]:
