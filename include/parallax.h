@@ -285,7 +285,7 @@ parallax_status_t parallax_prefill(const parallax_prefill_args_t *args, void *hi
  * products run on the bf16 matrix cores with fp32 accumulation; the weights
  * (1 + r - t) p, ds and dt are rounded to bf16 before they meet dout, q, rho
  * and k.  Deterministic: no atomics, fixed summation order.
- * Supported: causal = 1, head_dim 128, GQA group 1, 2 or 4 (else
+ * Supported: causal = 1, head_dim 64 or 128, GQA group 1, 2 or 4 (else
  * PARALLAX_ERR_UNSUPPORTED).  Workspace: parallax_prefill_backward_workspace_size
  * bytes (16 per query row), 16-byte aligned, owned by the caller; its
  * contents on entry do not matter.

@@ -208,8 +208,8 @@ parallax_status_t check_prefill_backward(const parallax_prefill_backward_args_t 
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill backward: only causal = 1 is supported");
     if (a->window < 0)
         return fail(PARALLAX_ERR_INVALID_ARG, "prefill backward: window must be >= 0");
-    if (a->head_dim != 128)
-        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill backward: head_dim %d (supported: 128)",
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill backward: head_dim %d (supported: 64, 128)",
                     a->head_dim);
     const int group = a->num_q_heads / a->num_kv_heads;
     if (group != 1 && group != 2 && group != 4)

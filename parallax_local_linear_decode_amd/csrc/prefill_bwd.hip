@@ -56,15 +56,24 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBwPairs = 4;                 // score/value wave pairs per workgroup
 constexpr int kBwRows = 32;                 // query rows (dq) or keys (dkv) per pair
 constexpr int kBwTile = 32;                 // rows of a streamed tile
-constexpr int kBwD = 128;                   // head dim
-// LDS bytes per tile row.  Tiles here are read both row-wise (16 bytes per
-// lane) and transposed (ds_read_b64_tr_b16, 8 bytes per lane); a 32-byte pad
-// keeps the transposed reads conflict free (the row-wise reads then pair up
-// on banks).  Measured alternatives: a 16-byte pad, and an XOR swizzle that
-// is conflict free for both patterns, ran within 1% (the swizzle's address
-// arithmetic cost what its conflict-free reads saved).
-constexpr int kBwRowBytes = 2 * kBwD + 32;
-constexpr int kBwTileBytes = kBwTile * kBwRowBytes;
+// LDS bytes per tile row (head dim D = 64 or 128).  Tiles here are read both
+// row-wise (16 bytes per lane) and transposed (ds_read_b64_tr_b16, 8 bytes
+// per lane); a 32-byte pad keeps the transposed reads conflict free (the
+// row-wise reads then pair up on banks).  Measured alternatives at D = 128: a
+// 16-byte pad, and an XOR swizzle that is conflict free for both patterns,
+// ran within 1% (the swizzle's address arithmetic cost what its
+// conflict-free reads saved).
+template <int D>
+constexpr int bw_row_bytes() { return 2 * D + 32; }
+template <int D>
+constexpr int bw_tile_bytes() { return kBwTile * bw_row_bytes<D>(); }
+// One thread's piece of a tile row (16 per row): 16 bytes at D = 128, 8 at 64.
+template <int D>
+using BwPiece = std::conditional_t<D == 128, uint4, uint2>;
+template <int D>
+__device__ __forceinline__ BwPiece<D> ldp(const uint16_t *p) {
+    return *reinterpret_cast<const BwPiece<D> *>(p);
+}
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -83,8 +92,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
 // the loop optimizer treats it as an opaque value: otherwise it turns every
 // LDS address derived from it into an induction variable of its own, which
 // costs dozens of registers.
+template <int D>
 __device__ __forceinline__ int slot3(int t) {
-    return __builtin_amdgcn_readfirstlane((t % 3) * kBwTileBytes);
+    return __builtin_amdgcn_readfirstlane((t % 3) * bw_tile_bytes<D>());
 }
 
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t &a, const bf16x8_t &b, const f32x4_t &c) {
@@ -94,11 +104,13 @@ __device__ __forceinline__ f32x4_t mfma(const bf16x8_t &a, const bf16x8_t &b, co
 // A operand of a 16x16x32 MFMA holding the transpose of a 32-row LDS tile:
 // row 16db + (lane % 16) of the result is head-dim column 16db + lane % 16
 // of the tile, k-slot r is tile row 4g + r (r < 4) or 16 + 4g + r - 4.
+template <int D>
 __device__ __forceinline__ bf16x8_t tr_operand(const unsigned char *tile, int db, int c, int g) {
     typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    constexpr int RB = bw_row_bytes<D>();
     const int col = 16 * db + 4 * (c % 4);
-    const unsigned char *a0 = tile + (4 * g + c / 4) * kBwRowBytes + 2 * col;
-    const unsigned char *a1 = tile + (16 + 4 * g + c / 4) * kBwRowBytes + 2 * col;
+    const unsigned char *a0 = tile + (4 * g + c / 4) * RB + 2 * col;
+    const unsigned char *a1 = tile + (16 + 4 * g + c / 4) * RB + 2 * col;
     const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_i16x4 *)(__attribute__((address_space(3))) unsigned char *)a0);
     const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -108,7 +120,10 @@ __device__ __forceinline__ bf16x8_t tr_operand(const unsigned char *tile, int db
 }
 
 // ------------------------------------------------------------------ prep ---
+// 16 lanes per row, EL = D / 16 head-dim values each.
+template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(PrefillBwdParams p) {
+    constexpr int EL = D / 16;
     const int64_t rows = (int64_t)p.batch * p.num_q_heads * p.seq_len;
     const int64_t u = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
     const int part = threadIdx.x % 16;
@@ -116,22 +131,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrefillBwdParams p) {
     const int i = (int)(uu % p.seq_len);
     const int h = (int)((uu / p.seq_len) % p.num_q_heads);
     const int b = (int)(uu / ((int64_t)p.seq_len * p.num_q_heads));
-    const uint4 gw = ld16(p.dout + (int64_t)b * p.g_sb + (int64_t)i * p.g_ss + (int64_t)h * p.g_sh +
-                          8 * part);
-    const int64_t ooff = (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh + 8 * part;
-    const float4 o0 = *reinterpret_cast<const float4 *>(p.out + ooff);
-    const float4 o1 = *reinterpret_cast<const float4 *>(p.out + ooff + 4);
-    const float4 a0 = *reinterpret_cast<const float4 *>(p.o_sa + ooff);
-    const float4 a1 = *reinterpret_cast<const float4 *>(p.o_sa + ooff + 4);
-    const float gv[8] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y),
-                         bf16_lo(gw.z), bf16_hi(gw.z), bf16_lo(gw.w), bf16_hi(gw.w)};
-    const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const BwPiece<D> gw = ldp<D>(p.dout + (int64_t)b * p.g_sb + (int64_t)i * p.g_ss +
+                                 (int64_t)h * p.g_sh + EL * part);
+    const uint32_t *gwords = reinterpret_cast<const uint32_t *>(&gw);
+    const int64_t ooff = (int64_t)b * p.o_sb + (int64_t)i * p.o_ss + (int64_t)h * p.o_sh + EL * part;
     float ca = 0.f, go = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        ca = fmaf(av[e], gv[e], ca);
-        go = fmaf(ov[e], gv[e], go);
+    for (int e4 = 0; e4 < EL / 4; ++e4) {
+        const float4 o = *reinterpret_cast<const float4 *>(p.out + ooff + 4 * e4);
+        const float4 a = *reinterpret_cast<const float4 *>(p.o_sa + ooff + 4 * e4);
+        const float gv[4] = {bf16_lo(gwords[2 * e4]), bf16_hi(gwords[2 * e4]),
+                             bf16_lo(gwords[2 * e4 + 1]), bf16_hi(gwords[2 * e4 + 1])};
+        const float ov[4] = {o.x, o.y, o.z, o.w};
+        const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ca = fmaf(av[e], gv[e], ca);
+            go = fmaf(ov[e], gv[e], go);
+        }
     }
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) {
@@ -145,15 +162,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrefillBwdParams p) {
 }
 
 // -------------------------------------------------------------------- dq ---
-template <int G, bool WIN>
+template <int D, int G, bool WIN>
 __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams p) {
-    constexpr int KS = kBwD / 32;          // score MFMAs per 16-key block
-    constexpr int DB = kBwD / 16;          // 16-row blocks of the gradient sums
+    constexpr int KS = D / 32;             // score MFMAs per 16-key block
+    constexpr int DB = D / 16;             // 16-row blocks of the gradient sums
+    constexpr int DQ = D / 4;              // head-dim values per lane group (scores)
+    constexpr int RB = bw_row_bytes<D>(), TB = bw_tile_bytes<D>();
+    constexpr int PE = D / 16;             // elements per tile piece
     constexpr int PPH = kBwPairs / G;      // pairs per query head
     constexpr int QB = kBwRows * PPH;      // query rows per head per workgroup
 
-    __shared__ __attribute__((aligned(16))) unsigned char ktile[3 * kBwTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char vtile[2][kBwTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char ktile[3 * TB];
+    __shared__ __attribute__((aligned(16))) unsigned char vtile[2][TB];
     __shared__ uint4 pbuf[2][kBwPairs][4][64];  // dS^T (qc 0, 1), dT^T (qc 0, 1), B-operand layout
 
     const int tid = threadIdx.x;
@@ -187,34 +207,35 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
     // tile, 16-byte piece cv of each row.
     const int tv = tid - 64 * kBwPairs;
     const int rv = (tv >> 4) & 15, cv = tv & 15;
-    const int64_t ko = (int64_t)rv * p.k_ss + 8 * cv, vo = (int64_t)rv * p.v_ss + 8 * cv;
+    const int64_t ko = (int64_t)rv * p.k_ss + PE * cv, vo = (int64_t)rv * p.v_ss + PE * cv;
     struct Stage {
-        uint4 k[2], v[2];
+        BwPiece<D> k[2], v[2];
     } kst[2];  // tile j in stage j & 1
     auto issue = [&](int t, Stage &st) {
         const int key0 = min(t * kBwTile, S - 1);
         const uint16_t *ks_ = kg + (int64_t)key0 * p.k_ss;
         const uint16_t *vs_ = vg + (int64_t)key0 * p.v_ss;
         if (key0 + kBwTile <= S) {
-            st.k[0] = ld16(ks_ + ko);
-            st.v[0] = ld16(vs_ + vo);
-            st.k[1] = ld16(ks_ + 16 * p.k_ss + ko);
-            st.v[1] = ld16(vs_ + 16 * p.v_ss + vo);
+            st.k[0] = ldp<D>(ks_ + ko);
+            st.v[0] = ldp<D>(vs_ + vo);
+            st.k[1] = ldp<D>(ks_ + 16 * p.k_ss + ko);
+            st.v[1] = ldp<D>(vs_ + 16 * p.v_ss + vo);
         } else {  // a ragged last tile: keys past the end read key S - 1
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int kk = min(rv + 16 * i, S - 1 - key0);
-                st.k[i] = ld16(ks_ + (int64_t)kk * p.k_ss + 8 * cv);
-                st.v[i] = ld16(vs_ + (int64_t)kk * p.v_ss + 8 * cv);
+                st.k[i] = ldp<D>(ks_ + (int64_t)kk * p.k_ss + PE * cv);
+                st.v[i] = ldp<D>(vs_ + (int64_t)kk * p.v_ss + PE * cv);
             }
         }
     };
     auto store = [&](unsigned char *kt, unsigned char *vt, const Stage &st) {
-        const int off = rv * kBwRowBytes + 16 * cv;
-        *reinterpret_cast<uint4 *>(kt + off) = st.k[0];
-        *reinterpret_cast<uint4 *>(kt + off + 16 * kBwRowBytes) = st.k[1];
-        *reinterpret_cast<uint4 *>(vt + off) = st.v[0];
-        *reinterpret_cast<uint4 *>(vt + off + 16 * kBwRowBytes) = st.v[1];
+        using P = BwPiece<D>;
+        const int off = rv * RB + 2 * PE * cv;
+        *reinterpret_cast<P *>(kt + off) = st.k[0];
+        *reinterpret_cast<P *>(kt + off + 16 * RB) = st.k[1];
+        *reinterpret_cast<P *>(vt + off) = st.v[0];
+        *reinterpret_cast<P *>(vt + off + 16 * RB) = st.v[1];
     };
     // End of epoch t: K and V tile t + 1 go to LDS (K buffer (t+1) % 3 last
     // held tile t - 2, read by the value waves in epoch t - 1; V buffer
@@ -222,13 +243,13 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
     // their register stage takes the loads of tile t + 3.
     auto advance = [&](int t, auto par) {
         constexpr int P = decltype(par)::value;
-        store(ktile + slot3(t + 1), vtile[1 - P], kst[1 - P]);
+        store(ktile + slot3<D>(t + 1), vtile[1 - P], kst[1 - P]);
         issue(t + 3, kst[1 - P]);
         __syncthreads();
     };
     auto prologue = [&] {
         issue(t_first, kst[0]);
-        store(ktile + slot3(t_first), vtile[0], kst[0]);
+        store(ktile + slot3<D>(t_first), vtile[0], kst[0]);
         issue(t_first + 1, kst[1]);
         issue(t_first + 2, kst[0]);
         __syncthreads();
@@ -250,7 +271,7 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
                                                (int64_t)head * p.r_sh;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                xop[cb][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + 32 * g + 8 * ks));
+                xop[cb][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + DQ * g + 8 * ks));
         }
 #pragma unroll
         for (int qc = 0; qc < 2; ++qc) {
@@ -259,14 +280,14 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
                 p.dout + (int64_t)b * p.g_sb + (int64_t)row * p.g_ss + (int64_t)head * p.g_sh;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                gop[qc][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + 32 * g + 8 * ks));
+                gop[qc][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + DQ * g + 8 * ks));
             st[qc] = p.rowstat[((int64_t)b * p.num_q_heads + head) * S + row];
         }
 
         // d1[rb][cb]: lane (c, g) = query column c of block cb, keys
         // 32t + 16rb + 4g + j; du[rb][qc] the same for U^T.
         auto scores = [&](int t, f32x4_t (&d1)[2][4], f32x4_t (&du)[2][2]) {
-            const unsigned char *kt = ktile + slot3(t);
+            const unsigned char *kt = ktile + slot3<D>(t);
             const unsigned char *vt = vtile[t & 1];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
@@ -276,9 +297,9 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const bf16x8_t kop = __builtin_bit_cast(
-                        bf16x8_t, ld16(kt + (16 * rb + c) * kBwRowBytes + 64 * g + 16 * ks));
+                        bf16x8_t, ld16(kt + (16 * rb + c) * RB + 2 * DQ * g + 16 * ks));
                     const bf16x8_t vop = __builtin_bit_cast(
-                        bf16x8_t, ld16(vt + (16 * rb + c) * kBwRowBytes + 64 * g + 16 * ks));
+                        bf16x8_t, ld16(vt + (16 * rb + c) * RB + 2 * DQ * g + 16 * ks));
 #pragma unroll
                     for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = mfma(kop, xop[cb][ks], d1[rb][cb]);
 #pragma unroll
@@ -353,10 +374,10 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
                 pop[cb] = __builtin_bit_cast(bf16x8_t, pbuf[u & 1][pair][cb][lane]);
-            const unsigned char *kt = ktile + slot3(u);
+            const unsigned char *kt = ktile + slot3<D>(u);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16x8_t kop = tr_operand(kt, db, c, g);
+                const bf16x8_t kop = tr_operand<D>(kt, db, c, g);
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) acc[db][cb] = mfma(kop, pop[cb], acc[db][cb]);
             }
@@ -389,15 +410,18 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
 }
 
 // ------------------------------------------------------------------- dkv ---
-template <int G, bool WIN>
+template <int D, int G, bool WIN>
 __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParams p) {
-    constexpr int KS = kBwD / 32;
-    constexpr int DB = kBwD / 16;
+    constexpr int KS = D / 32;
+    constexpr int DB = D / 16;
+    constexpr int DQ = D / 4;
+    constexpr int RB = bw_row_bytes<D>(), TB = bw_tile_bytes<D>();
+    constexpr int PE = D / 16;
     constexpr int KB = kBwRows * kBwPairs;  // keys per workgroup
 
-    __shared__ __attribute__((aligned(16))) unsigned char qtile[3 * kBwTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char rtile[3 * kBwTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char gtile[3 * kBwTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char qtile[3 * TB];
+    __shared__ __attribute__((aligned(16))) unsigned char rtile[3 * TB];
+    __shared__ __attribute__((aligned(16))) unsigned char gtile[3 * TB];
     __shared__ float4 stile[3][kBwTile];          // row statistics of the tile's rows
     __shared__ uint4 pbuf[2][kBwPairs][6][64];    // W, scale dS, dT (key blocks 0, 1)
 
@@ -434,7 +458,7 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
     auto tile_qt = [&](int t) { return qt_lo + t % nq; };
 
     // Staging, value waves only: thread tv takes rows rv and rv + 16 of a
-    // tile, 16-byte piece cv of each row, and float se of the tile's 128
+    // tile, piece cv (of 16) of each row, and float se of the tile's 128
     // statistics floats (its 32 rows' float4s are contiguous).  One register
     // stage: tile t + 1, loaded during epoch t - 1, goes to LDS at the start
     // of epoch t (its slot and statistics row last held tile t - 2, read in
@@ -442,11 +466,11 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
     // loads of tile t + 2.
     const int tv = tid - 64 * kBwPairs;
     const int rv = (tv >> 4) & 15, cv = tv & 15, se = tv & 127;
-    const int64_t qo = (int64_t)rv * p.q_ss + 8 * cv;
-    const int64_t ro = (int64_t)rv * p.r_ss + 8 * cv;
-    const int64_t go = (int64_t)rv * p.g_ss + 8 * cv;
+    const int64_t qo = (int64_t)rv * p.q_ss + PE * cv;
+    const int64_t ro = (int64_t)rv * p.r_ss + PE * cv;
+    const int64_t go = (int64_t)rv * p.g_ss + PE * cv;
     struct {
-        uint4 q[2], r[2], g[2];
+        BwPiece<D> q[2], r[2], g[2];
         float s;
     } st;
     auto issue = [&](int t) {
@@ -458,32 +482,33 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
         const uint16_t *gs = p.dout + (int64_t)b * p.g_sb + (int64_t)row0 * p.g_ss + (int64_t)h * p.g_sh;
         const float *ss = reinterpret_cast<const float *>(p.rowstat + ((int64_t)b * p.num_q_heads + h) * S);
         if (row0 + kBwTile <= S) {
-            st.q[0] = ld16(qs + qo);
-            st.r[0] = ld16(rs + ro);
-            st.g[0] = ld16(gs + go);
-            st.q[1] = ld16(qs + 16 * p.q_ss + qo);
-            st.r[1] = ld16(rs + 16 * p.r_ss + ro);
-            st.g[1] = ld16(gs + 16 * p.g_ss + go);
+            st.q[0] = ldp<D>(qs + qo);
+            st.r[0] = ldp<D>(rs + ro);
+            st.g[0] = ldp<D>(gs + go);
+            st.q[1] = ldp<D>(qs + 16 * p.q_ss + qo);
+            st.r[1] = ldp<D>(rs + 16 * p.r_ss + ro);
+            st.g[1] = ldp<D>(gs + 16 * p.g_ss + go);
         } else {  // a ragged last tile: rows past the end read row S - 1
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int64_t rr = min(rv + 16 * i, S - 1 - row0);
-                st.q[i] = ld16(qs + rr * p.q_ss + 8 * cv);
-                st.r[i] = ld16(rs + rr * p.r_ss + 8 * cv);
-                st.g[i] = ld16(gs + rr * p.g_ss + 8 * cv);
+                st.q[i] = ldp<D>(qs + rr * p.q_ss + PE * cv);
+                st.r[i] = ldp<D>(rs + rr * p.r_ss + PE * cv);
+                st.g[i] = ldp<D>(gs + rr * p.g_ss + PE * cv);
             }
         }
         st.s = ss[4 * min(row0 + (se >> 2), S - 1) + (se & 3)];
     };
     auto store = [&](int t) {
-        const int off = slot3(t) + rv * kBwRowBytes + 16 * cv;
-        constexpr int O16 = 16 * kBwRowBytes;
-        *reinterpret_cast<uint4 *>(qtile + off) = st.q[0];
-        *reinterpret_cast<uint4 *>(rtile + off) = st.r[0];
-        *reinterpret_cast<uint4 *>(gtile + off) = st.g[0];
-        *reinterpret_cast<uint4 *>(qtile + off + O16) = st.q[1];
-        *reinterpret_cast<uint4 *>(rtile + off + O16) = st.r[1];
-        *reinterpret_cast<uint4 *>(gtile + off + O16) = st.g[1];
+        using P = BwPiece<D>;
+        const int off = slot3<D>(t) + rv * RB + 2 * PE * cv;
+        constexpr int O16 = 16 * RB;
+        *reinterpret_cast<P *>(qtile + off) = st.q[0];
+        *reinterpret_cast<P *>(rtile + off) = st.r[0];
+        *reinterpret_cast<P *>(gtile + off) = st.g[0];
+        *reinterpret_cast<P *>(qtile + off + O16) = st.q[1];
+        *reinterpret_cast<P *>(rtile + off + O16) = st.r[1];
+        *reinterpret_cast<P *>(gtile + off + O16) = st.g[1];
         // threads tv and tv + 128 store the same statistics float: no lane
         // condition, so no branch around a store that waits on a load
         reinterpret_cast<float *>(stile[t % 3])[se] = st.s;
@@ -496,7 +521,7 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
 
     if (score_wave) {
         // Key-side B operands: column c of block kc is key kp + 16kc + c;
-        // head-dim value 32g + 8ks + i in k-slot 8g + i of MFMA ks.
+        // head-dim value DQ g + 8ks + i in k-slot 8g + i of MFMA ks.
         bf16x8_t kop[2][KS], vop[2][KS];
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
@@ -505,15 +530,15 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
             const uint16_t *vs_ = p.v + (int64_t)b * p.v_sb + (int64_t)key * p.v_ss + (int64_t)hk * p.v_sh;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                kop[kc][ks] = __builtin_bit_cast(bf16x8_t, ld16(ks_ + 32 * g + 8 * ks));
-                vop[kc][ks] = __builtin_bit_cast(bf16x8_t, ld16(vs_ + 32 * g + 8 * ks));
+                kop[kc][ks] = __builtin_bit_cast(bf16x8_t, ld16(ks_ + DQ * g + 8 * ks));
+                vop[kc][ks] = __builtin_bit_cast(bf16x8_t, ld16(vs_ + DQ * g + 8 * ks));
             }
         }
 
         // sd/td/ud[rb][kc]: lane (c, g) = key column c of block kc, tile rows
         // 16rb + 4g + j.
         auto scores = [&](int t, f32x4_t (&sd)[2][2], f32x4_t (&td)[2][2], f32x4_t (&ud)[2][2]) {
-            const int buf = slot3(t);
+            const int buf = slot3<D>(t);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
@@ -521,7 +546,7 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
                     sd[rb][kc] = td[rb][kc] = ud[rb][kc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int off = (16 * rb + c) * kBwRowBytes + 64 * g + 16 * ks;
+                    const int off = (16 * rb + c) * RB + 2 * DQ * g + 16 * ks;
                     const bf16x8_t qa = __builtin_bit_cast(bf16x8_t, ld16(qtile + buf + off));
                     const bf16x8_t ra = __builtin_bit_cast(bf16x8_t, ld16(rtile + buf + off));
                     const bf16x8_t ga = __builtin_bit_cast(bf16x8_t, ld16(gtile + buf + off));
@@ -625,12 +650,12 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
                 ps[kc] = __builtin_bit_cast(bf16x8_t, pbuf[u & 1][pair][2 + kc][lane]);
                 pt[kc] = __builtin_bit_cast(bf16x8_t, pbuf[u & 1][pair][4 + kc][lane]);
             }
-            const int buf = slot3(u);
+            const int buf = slot3<D>(u);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16x8_t ga = tr_operand(gtile + buf, db, c, g);
-                const bf16x8_t qa = tr_operand(qtile + buf, db, c, g);
-                const bf16x8_t ra = tr_operand(rtile + buf, db, c, g);
+                const bf16x8_t ga = tr_operand<D>(gtile + buf, db, c, g);
+                const bf16x8_t qa = tr_operand<D>(qtile + buf, db, c, g);
+                const bf16x8_t ra = tr_operand<D>(rtile + buf, db, c, g);
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
                     dvt[db][kc] = mfma(ga, pw[kc], dvt[db][kc]);
@@ -671,38 +696,44 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
     }
 }
 
-template <int G, bool WIN>
+template <int D, int G, bool WIN>
 hipError_t launch_bwd(const PrefillBwdParams &p, hipStream_t stream) {
     const int units = p.batch * p.num_kv_heads;
     const int qb_rows = kBwRows * kBwPairs / G;
     const int nqb = (p.seq_len + qb_rows - 1) / qb_rows;
     const int nkb = (p.seq_len + kBwRows * kBwPairs - 1) / (kBwRows * kBwPairs);
-    hipLaunchKernelGGL((bwd_dq_kernel<G, WIN>), dim3((unsigned)(units * nqb)), dim3(128 * kBwPairs),
+    hipLaunchKernelGGL((bwd_dq_kernel<D, G, WIN>), dim3((unsigned)(units * nqb)), dim3(128 * kBwPairs),
                        0, stream, p);
-    hipLaunchKernelGGL((bwd_dkv_kernel<G, WIN>), dim3((unsigned)(units * nkb)),
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, G, WIN>), dim3((unsigned)(units * nkb)),
                        dim3(128 * kBwPairs), 0, stream, p);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_prefill_backward(const PrefillBwdParams &p, int d, hipStream_t stream) {
-    if (d != kBwD) return hipErrorInvalidValue;
+template <int D>
+hipError_t launch_prefill_backward_d(const PrefillBwdParams &p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.batch * p.num_q_heads * p.seq_len;
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int G = p.num_q_heads / p.num_kv_heads;
     const bool win = p.window > 0 && p.window < p.seq_len;
     switch (G * 2 + (win ? 1 : 0)) {
-        case 2: return launch_bwd<1, false>(p, stream);
-        case 3: return launch_bwd<1, true>(p, stream);
-        case 4: return launch_bwd<2, false>(p, stream);
-        case 5: return launch_bwd<2, true>(p, stream);
-        case 8: return launch_bwd<4, false>(p, stream);
-        case 9: return launch_bwd<4, true>(p, stream);
+        case 2: return launch_bwd<D, 1, false>(p, stream);
+        case 3: return launch_bwd<D, 1, true>(p, stream);
+        case 4: return launch_bwd<D, 2, false>(p, stream);
+        case 5: return launch_bwd<D, 2, true>(p, stream);
+        case 8: return launch_bwd<D, 4, false>(p, stream);
+        case 9: return launch_bwd<D, 4, true>(p, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_backward(const PrefillBwdParams &p, int d, hipStream_t stream) {
+    if (d == 128) return launch_prefill_backward_d<128>(p, stream);
+    if (d == 64) return launch_prefill_backward_d<64>(p, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace plx

@@ -237,7 +237,7 @@ def test_backward_workspace_size(lib):
     (dict(dk_stride_s=-4), INVALID, "non-negative"),
     (dict(window=-1), INVALID, "window"),
     (dict(causal=0), UNSUPP, "causal"),
-    (dict(head_dim=64), UNSUPP, "head_dim"),
+    (dict(head_dim=96), UNSUPP, "head_dim"),
     (dict(num_q_heads=64), UNSUPP, "GQA group"),
     (dict(rmean=FAKE + 8), UNSUPP, "aligned"),
     (dict(dout_stride_h=132), UNSUPP, "16 bytes"),

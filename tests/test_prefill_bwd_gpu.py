@@ -5,7 +5,8 @@ through the C ABI.
 The GPU backward consumes the GPU forward's own outputs (out, o_sa, lse, r);
 the oracle recomputes everything from the inputs, so these tests check the
 whole training step.  Small cases compare every element (ragged lengths
-around the 32-row tiles and 128-row blocks, GQA groups 1/2/4, local windows);
+around the 32-row tiles and 128-row blocks, GQA groups 1/2/4, local windows,
+head dims 128 and 64);
 the full-size workload (batch 4 x 8192 tokens, 16 query / 8 KV heads, d 128)
 compares sampled rows of dq and drho, the last 64 keys' dk and dv (exact for
 them: no earlier row sees those keys), and two properties that hold at any
@@ -38,9 +39,9 @@ def forward_backward(q, rho, k, v, dout, scale, window=0):
     return (out, lse, rmean, o_sa), grads
 
 
-def case(B, S, Hq, Hkv, seed, device):
-    q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, 128, seed=seed, device=device)
-    dout = prefill_dout(B, S, Hq, 128, seed=seed + 7919, device=device)
+def case(B, S, Hq, Hkv, seed, device, d=128):
+    q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, d, seed=seed, device=device)
+    dout = prefill_dout(B, S, Hq, d, seed=seed + 7919, device=device)
     return q, rho, k, v, dout, scale
 
 
@@ -58,27 +59,51 @@ def check_stats(stats, q, rho, k, v, scale, window=0, rows=None, what=""):
     assert_parity(o_sa[:, sel], ref_a, TAU_BF16, RMS_PREFILL, what=f"{what} o_sa")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("S", [1, 17, 31, 32, 33, 64, 100, 129, 257])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2), (8, 2)])
-def test_small_every_gradient(gpu, S, Hq, Hkv):
-    q, rho, k, v, dout, scale = case(2, S, Hq, Hkv, S * 10 + Hq, gpu)
+def test_small_every_gradient(gpu, S, Hq, Hkv, d):
+    q, rho, k, v, dout, scale = case(2, S, Hq, Hkv, S * 10 + Hq + d, gpu, d)
     stats, grads = forward_backward(q, rho, k, v, dout, scale)
-    check_stats(stats, q, rho, k, v, scale, what=f"S={S} {Hq}/{Hkv}")
+    what = f"S={S} {Hq}/{Hkv} d={d}"
+    check_stats(stats, q, rho, k, v, scale, what=what)
     ref = oracle.prefill_backward(*(host_array(t) for t in (q, rho, k, v, dout)), scale)
     for name, g, r in zip(("dq", "drho", "dk", "dv"), grads, ref):
-        assert_parity(g, r, TAU_BWD, RMS_BWD, what=f"S={S} {Hq}/{Hkv} {name}")
+        assert_parity(g, r, TAU_BWD, RMS_BWD, what=f"{what} {name}")
 
 
 @pytest.mark.parametrize("W", [1, 5, 31, 32, 33, 100])
-@pytest.mark.parametrize("S,Hq,Hkv", [(100, 4, 2), (300, 2, 1), (257, 8, 2)])
-def test_window_every_gradient(gpu, S, Hq, Hkv, W):
-    q, rho, k, v, dout, scale = case(1, S, Hq, Hkv, S + W, gpu)
+@pytest.mark.parametrize("S,Hq,Hkv,d", [(100, 4, 2, 128), (300, 2, 1, 128), (257, 8, 2, 128),
+                                        (300, 4, 2, 64)])
+def test_window_every_gradient(gpu, S, Hq, Hkv, d, W):
+    q, rho, k, v, dout, scale = case(1, S, Hq, Hkv, S + W, gpu, d)
     stats, grads = forward_backward(q, rho, k, v, dout, scale, window=W)
-    check_stats(stats, q, rho, k, v, scale, window=W, what=f"S={S} W={W}")
+    what = f"S={S} W={W} d={d}"
+    check_stats(stats, q, rho, k, v, scale, window=W, what=what)
     ref = oracle.prefill_backward(*(host_array(t) for t in (q, rho, k, v, dout)), scale,
                                   window=W)
     for name, g, r in zip(("dq", "drho", "dk", "dv"), grads, ref):
-        assert_parity(g, r, TAU_BWD, RMS_BWD, what=f"S={S} W={W} {name}")
+        assert_parity(g, r, TAU_BWD, RMS_BWD, what=f"{what} {name}")
+
+
+def test_head_dim_64_larger(gpu):
+    """d 64 over several 128-key blocks: batch 2 x 1500 tokens, 8 query / 2
+    KV heads; sampled rows of dq and drho, the last 64 keys' dk and dv."""
+    B, S, Hq, Hkv = 2, 1500, 8, 2
+    q, rho, k, v, dout, scale = case(B, S, Hq, Hkv, 64, gpu, 64)
+    stats, (dq, drho, dk, dv) = forward_backward(q, rho, k, v, dout, scale)
+    rows = np.array([0, 1, 31, 32, 127, 128, 700, 1023, 1024] + list(range(S - 64, S)),
+                    dtype=np.int32)
+    h = [host_array(t) for t in (q, rho, k, v, dout)]
+    check_stats(stats, q, rho, k, v, scale, rows=rows, what="d=64")
+    r_dq, r_drho, r_dk, r_dv = oracle.prefill_backward(*h, scale, rows=rows)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    assert_parity(dq[:, sel], r_dq, TAU_BWD, RMS_BWD, what="d=64 dq")
+    assert_parity(drho[:, sel], r_drho, TAU_BWD, RMS_BWD, what="d=64 drho")
+    assert_parity(dk[:, S - 64:], r_dk[:, S - 64:], TAU_BWD, RMS_BWD, what="d=64 dk tail")
+    assert_parity(dv[:, S - 64:], r_dv[:, S - 64:], TAU_BWD, RMS_BWD, what="d=64 dv tail")
+    g_sum = dout.double().reshape(B, S, Hkv, Hq // Hkv, 64).sum(dim=(1, 3)).cpu().numpy()
+    assert_parity(dv.double().sum(dim=1), g_sum, TAU_BWD, RMS_BWD, what="d=64 sum dv")
 
 
 def test_window_at_least_the_sequence_is_full(gpu):
@@ -200,13 +225,13 @@ def test_full_size_window(gpu):
                   what="window dv")
 
 
-@pytest.mark.parametrize("window", [0, 40])
-def test_autograd_function(gpu, window):
+@pytest.mark.parametrize("window,d", [(0, 128), (40, 128), (0, 64)])
+def test_autograd_function(gpu, window, d):
     """parallax_prefill_attention under torch autograd: the forward equals
     parallax_prefill, and loss.backward() gives exactly the C ABI backward's
     gradients (in the inputs' bf16) for the loss sum(dout * out); the oracle
     checks them too."""
-    q, rho, k, v, dout, scale = case(2, 150, 4, 2, 61, gpu)
+    q, rho, k, v, dout, scale = case(2, 150, 4, 2, 61, gpu, d)
     leaves = [t.clone().requires_grad_(True) for t in (q, rho, k, v)]
     out = plx.parallax_prefill_attention(*leaves, scale=scale, window=window)
     (out * dout.float()).sum().backward()
