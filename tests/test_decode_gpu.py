@@ -5,6 +5,7 @@ d = 64, 128 tokens; also rho = 0 and a single token), the 1.7B-like GQA shape
 (batch 8, 16 query / 8 KV heads, d = 128, 4096 tokens, bf16 cache), ragged
 lengths around wave/page/split boundaries, empty rows, and the paged cache.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -113,6 +114,30 @@ def test_gqa_bf16_rho_zero_is_softmax(gpu):
     inp = to(decode_inputs(8, 16, 8, 128, 4096, seed=0, rho_zero=True), gpu)
     ref = oracle_decode(inp)
     assert_parity(run(inp), ref, TAU_BF16, RMS_DECODE_BF16, what="rho=0")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("B,L", [(1024, 32768), (2048, 8192), (2048, 128), (1, 32768)])
+def test_sweep_corners_sampled(gpu, B, L):
+    """Corners of the batch x context sweep (16/8 heads, d 128, bf16 KV) in
+    the launch configuration the bench times (the library's split choice):
+    the largest cache (1024 x 32768 tokens, 137 GB), the most rows (2048 at
+    8192 and at 128 tokens) and one long row.  Sampled sequences, including
+    the first and last, against the oracle."""
+    kv = B * 8 * L * 128 * 2 * 2
+    if kv * 1.1 > torch.cuda.mem_get_info()[0]:
+        pytest.skip(f"needs {kv / 1e9:.0f} GB of free HBM")
+    inp = decode_inputs(B, 16, 8, 128, L, seed=B + L, device=gpu)
+    out = run(inp)
+    rng = np.random.default_rng(B + L)
+    rows = sorted({0, B - 1, *(int(x) for x in rng.integers(0, B, 6))})
+    sel = torch.as_tensor(rows, dtype=torch.long, device=gpu)
+    sub = dataclasses.replace(inp, q=inp.q[sel], rho=inp.rho[sel], k=inp.k[sel], v=inp.v[sel])
+    ref = oracle_decode(sub)
+    got = out[sel]
+    del inp, out, sub
+    torch.cuda.empty_cache()
+    assert_parity(got, ref, TAU_BF16, RMS_DECODE_BF16, what=f"sweep {B} x {L}")
 
 
 # ------------------------------------------------------------------ edges ---
