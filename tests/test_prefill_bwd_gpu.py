@@ -193,6 +193,25 @@ def test_full_size(gpu):
 
 
 @pytest.mark.slow
+def test_long_sequence(gpu):
+    """One sequence of 32768 tokens (16/8 heads, d 128): sampled rows of dq
+    and drho, the last 32 keys' dk and dv (exact from the last 32 rows)."""
+    B, S, Hq, Hkv = 1, 32768, 16, 8
+    q, rho, k, v, dout, scale = case(B, S, Hq, Hkv, 22, gpu)
+    _, (dq, drho, dk, dv) = forward_backward(q, rho, k, v, dout, scale)
+    rng = np.random.default_rng(22)
+    rows = np.array(sorted(set([0, 127, 128, 16384] + list(rng.integers(0, S - 32, 4)) +
+                               list(range(S - 32, S)))), dtype=np.int32)
+    h = [host_array(t) for t in (q, rho, k, v, dout)]
+    r_dq, r_drho, r_dk, r_dv = oracle.prefill_backward(*h, scale, rows=rows)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    assert_parity(dq[:, sel], r_dq, TAU_BWD, RMS_BWD, what="32768 dq")
+    assert_parity(drho[:, sel], r_drho, TAU_BWD, RMS_BWD, what="32768 drho")
+    assert_parity(dk[:, S - 32:], r_dk[:, S - 32:], TAU_BWD, RMS_BWD, what="32768 dk tail")
+    assert_parity(dv[:, S - 32:], r_dv[:, S - 32:], TAU_BWD, RMS_BWD, what="32768 dv tail")
+
+
+@pytest.mark.slow
 def test_full_size_deterministic(gpu):
     q, rho, k, v, dout, scale = case(4, 8192, 16, 8, 16, gpu)
     stats, first = forward_backward(q, rho, k, v, dout, scale)

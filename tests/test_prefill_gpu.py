@@ -109,6 +109,19 @@ def test_full_size_sampled_rows(gpu):
 
 
 @pytest.mark.slow
+def test_long_sequence_sampled_rows(gpu):
+    """One sequence of 32768 tokens (16/8 heads, d 128): rows at tile and
+    block edges, the last rows and random rows, against the oracle."""
+    B, S, Hq, Hkv = 1, 32768, 16, 8
+    q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, 128, seed=21, device=gpu)
+    out = run(q, rho, k, v, scale)
+    rng = np.random.default_rng(21)
+    rows = sorted(set([0, 127, 128, 16383, 16384, 32640, 32767] + list(rng.integers(0, S, 9))))
+    ref = oracle.prefill(*host(q, rho, k, v), scale, rows=np.array(rows, dtype=np.int32))
+    assert_parity(out[:, rows], ref, TAU_BF16, RMS_PREFILL, what="prefill 32768 tokens")
+
+
+@pytest.mark.slow
 def test_full_size_deterministic(gpu):
     """Repeated launches at batch 4 x 8192 tokens return identical bits: the
     K/V tiles and the score-to-value hand-off in LDS are race-free under a
