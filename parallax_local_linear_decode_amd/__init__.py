@@ -241,6 +241,11 @@ def _workspace(device, stream, nbytes):
     key = (str(device), stream.value)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            # the old buffer goes back to torch's allocator, which only orders
+            # its reuse after torch's own stream: let work queued on `stream`
+            # finish with it first (growth happens a few times per process)
+            torch.cuda.synchronize(device)
         ws = torch.zeros(max(nbytes, 1 << 16), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
@@ -471,11 +476,11 @@ def parallax_prefill_backward(q, rho, k, v, dout, out, o_sa, lse, rmean, *, scal
     st = lib.parallax_prefill_backward_workspace_size(ctypes.byref(a), ctypes.byref(need))
     if st != PARALLAX_OK:
         _raise(st, lib)
-    if workspace is None:
-        workspace = torch.empty(max(int(need.value), 16), dtype=torch.uint8, device=q.device)
+    s = _stream_handle(q, stream)
+    if workspace is None:  # the per-stream buffer: no temporary freed while the launch runs
+        workspace = _workspace(q.device, s, max(int(need.value), 16))
     st = lib.parallax_prefill_backward(ctypes.byref(a), _ptr(workspace),
-                                       workspace.numel() * workspace.element_size(),
-                                       _stream_handle(q, stream))
+                                       workspace.numel() * workspace.element_size(), s)
     if st != PARALLAX_OK:
         _raise(st, lib)
     return dq, drho, dk, dv
