@@ -70,14 +70,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// Max over the four 16-lane groups (lanes c, c+16, c+32, c+48).
+// Max over the four 16-lane groups (lanes c, c+16, c+32, c+48).  A compare
+// and select per step: fmaxf on the swapped values first quiets both inputs
+// (two more instructions), and the scores are never NaN.
 __device__ __forceinline__ float group_max(float x) {
     const int xi = __builtin_bit_cast(int, x);
     auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);  // rows 0<->1, 2<->3
-    x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
+    const float a0 = __builtin_bit_cast(float, (int)a[0]), a1 = __builtin_bit_cast(float, (int)a[1]);
+    x = a0 > a1 ? a0 : a1;
     const int yi = __builtin_bit_cast(int, x);
     auto b2 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);  // halves 0<->1
-    return fmaxf(__builtin_bit_cast(float, (int)b2[0]), __builtin_bit_cast(float, (int)b2[1]));
+    const float b0 = __builtin_bit_cast(float, (int)b2[0]), b1 = __builtin_bit_cast(float, (int)b2[1]);
+    return b0 > b1 ? b0 : b1;
 }
 
 // WIN: the local-window form (instantiated separately, so full causal
