@@ -48,6 +48,10 @@ struct PrefillParams {
     int64_t v_sb, v_ss, v_sh;
     int64_t o_sb, o_ss, o_sh;
     int32_t batch, seq_len, num_q_heads, num_kv_heads;
+    // workgroup head blocks per KV head, set by the launcher: a workgroup
+    // serves the kernel's G query heads hb*G .. hb*G + G - 1 of KV head
+    // hb / head_blocks (1 unless a GQA group is split over workgroups)
+    int32_t head_blocks;
     float scale_log2;
     int32_t window;  // 0: keys 0..i; W >= 1: keys max(0, i-W+1)..i
     // optional outputs for a backward pass (each may be null): natural-log
@@ -84,6 +88,7 @@ struct PrefillBwdParams {
     int64_t dq_sb, dq_ss, dq_sh; // dq and drho
     int64_t dk_sb, dk_ss, dk_sh; // dk and dv
     int32_t batch, seq_len, num_q_heads, num_kv_heads;
+    int32_t head_blocks;  // as in PrefillParams (query-side dq kernel only)
     float scale;       // natural logit scale
     float scale_log2;  // scale * log2(e)
     int32_t window;

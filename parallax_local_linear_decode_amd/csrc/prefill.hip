@@ -118,13 +118,15 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
     const bool score_wave = wave < kPfPairs;
     const int pair = wave % kPfPairs;
 
-    const int units = p.batch * p.num_kv_heads;
+    const int nhb = p.num_kv_heads * p.head_blocks;  // blocks of G query heads
+    const int units = p.batch * nhb;
     const int nqb = (S + QB - 1) / QB;
     const int qb = nqb - 1 - (int)(blockIdx.x / units);  // longest causal rows first
     const int unit = blockIdx.x % units;
-    const int b = unit / p.num_kv_heads;
-    const int hk = unit % p.num_kv_heads;
-    const int head = hk * G + pair / PPH;
+    const int b = unit / nhb;
+    const int hb = unit % nhb;
+    const int hk = hb / p.head_blocks;  // the KV head of query heads hb*G .. hb*G + G - 1
+    const int head = hb * G + pair / PPH;
     const int r0 = qb * QB + (pair % PPH) * kPfRows;  // first query row of this pair
     const int key_end = min(S, (qb + 1) * QB);        // keys this workgroup needs
     const int ntiles = (key_end + kPfKeys - 1) / kPfKeys;
@@ -431,10 +433,15 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
     }
 }
 
+// GQA group 8: two workgroups of four query heads each per KV head (each
+// loads the KV tiles once for its four heads).
 template <int D>
-hipError_t launch_prefill_d(const PrefillParams &p, hipStream_t stream) {
-    const int G = p.num_q_heads / p.num_kv_heads;
-    const int units = p.batch * p.num_kv_heads;
+hipError_t launch_prefill_d(const PrefillParams &pin, hipStream_t stream) {
+    PrefillParams p = pin;
+    const int group = p.num_q_heads / p.num_kv_heads;
+    const int G = group > 4 ? 4 : group;  // query heads per workgroup
+    p.head_blocks = group / G;
+    const int units = p.batch * p.num_kv_heads * p.head_blocks;
     const int qb_rows = kPfRows * kPfPairs / G;
     const dim3 grid((unsigned)(units * ((p.seq_len + qb_rows - 1) / qb_rows)));
     const dim3 block(128 * kPfPairs);

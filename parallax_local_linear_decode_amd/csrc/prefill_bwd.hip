@@ -186,13 +186,15 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
     const bool score_wave = wave < kBwPairs;
     const int pair = wave % kBwPairs;
 
-    const int units = p.batch * p.num_kv_heads;
+    const int nhb = p.num_kv_heads * p.head_blocks;  // blocks of G query heads
+    const int units = p.batch * nhb;
     const int nqb = (S + QB - 1) / QB;
     const int qb = nqb - 1 - (int)(blockIdx.x / units);  // longest causal rows first
     const int unit = blockIdx.x % units;
-    const int b = unit / p.num_kv_heads;
-    const int hk = unit % p.num_kv_heads;
-    const int head = hk * G + pair / PPH;
+    const int b = unit / nhb;
+    const int hb = unit % nhb;
+    const int hk = hb / p.head_blocks;  // the KV head of query heads hb*G .. hb*G + G - 1
+    const int head = hb * G + pair / PPH;
     const int r0 = qb * QB + (pair % PPH) * kBwRows;  // first query row of this pair
     const int key_end = min(S, (qb + 1) * QB);
     const int ntiles = (key_end + kBwTile - 1) / kBwTile;
@@ -696,14 +698,19 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
     }
 }
 
+// GQA group 8: the dq kernel runs two workgroups of four query heads per KV
+// head; the dk/dv kernel streams all eight heads' rows past each key block.
 template <int D, int G, bool WIN>
-hipError_t launch_bwd(const PrefillBwdParams &p, hipStream_t stream) {
+hipError_t launch_bwd(const PrefillBwdParams &pin, hipStream_t stream) {
+    constexpr int GQ = G > 4 ? 4 : G;  // query heads per dq workgroup
+    PrefillBwdParams p = pin;
+    p.head_blocks = G / GQ;
     const int units = p.batch * p.num_kv_heads;
-    const int qb_rows = kBwRows * kBwPairs / G;
+    const int qb_rows = kBwRows * kBwPairs / GQ;
     const int nqb = (p.seq_len + qb_rows - 1) / qb_rows;
     const int nkb = (p.seq_len + kBwRows * kBwPairs - 1) / (kBwRows * kBwPairs);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, G, WIN>), dim3((unsigned)(units * nqb)), dim3(128 * kBwPairs),
-                       0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, GQ, WIN>), dim3((unsigned)(units * p.head_blocks * nqb)),
+                       dim3(128 * kBwPairs), 0, stream, p);
     hipLaunchKernelGGL((bwd_dkv_kernel<D, G, WIN>), dim3((unsigned)(units * nkb)),
                        dim3(128 * kBwPairs), 0, stream, p);
     return hipGetLastError();
@@ -724,6 +731,8 @@ hipError_t launch_prefill_backward_d(const PrefillBwdParams &p, hipStream_t stre
         case 5: return launch_bwd<D, 2, true>(p, stream);
         case 8: return launch_bwd<D, 4, false>(p, stream);
         case 9: return launch_bwd<D, 4, true>(p, stream);
+        case 16: return launch_bwd<D, 8, false>(p, stream);
+        case 17: return launch_bwd<D, 8, true>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

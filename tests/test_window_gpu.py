@@ -110,7 +110,7 @@ def test_window_paged(gpu, kv_dtype):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("S", [1, 33, 100, 300])
-@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (8, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (8, 2), (16, 2)])
 def test_window_prefill(gpu, S, Hq, Hkv, d):
     q, rho, k, v, scale = prefill_inputs(2, S, Hq, Hkv, d, seed=S + Hq + d)
     hq, hr, hk, hv = (host_array(t) for t in (q, rho, k, v))
