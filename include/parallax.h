@@ -223,7 +223,7 @@ parallax_status_t parallax_qr_projection(const parallax_qr_projection_args_t *ar
  * h / (Hq/Hkv) -- with a local window W >= 1 (see decode) to keys
  * max(0, i-W+1) .. i only.  q, rho bf16 [B, S, Hq, d]; k, v bf16 [B, S, Hkv, d];
  * out fp32 [B, S, Hq, d].  causal must be 1; head_dim must be 64 or 128; the GQA
- * group Hq/Hkv must be 1, 2, 4 or 8 (else PARALLAX_ERR_UNSUPPORTED).  Products
+ * group Hq/Hkv must be 1, 2, 4, 8 or 16 (else PARALLAX_ERR_UNSUPPORTED).  Products
  * run on the bf16 matrix cores with fp32 accumulation; the softmax
  * numerators e^{s} and e^{s} t are rounded to bf16 before they multiply V.
  */
@@ -285,7 +285,7 @@ parallax_status_t parallax_prefill(const parallax_prefill_args_t *args, void *hi
  * products run on the bf16 matrix cores with fp32 accumulation; the weights
  * (1 + r - t) p, ds and dt are rounded to bf16 before they meet dout, q, rho
  * and k.  Deterministic: no atomics, fixed summation order.
- * Supported: causal = 1, head_dim 64 or 128, GQA group 1, 2, 4 or 8 (else
+ * Supported: causal = 1, head_dim 64 or 128, GQA group 1, 2, 4, 8 or 16 (else
  * PARALLAX_ERR_UNSUPPORTED).  Workspace: parallax_prefill_backward_workspace_size
  * bytes (16 per query row), 16-byte aligned, owned by the caller; its
  * contents on entry do not matter.

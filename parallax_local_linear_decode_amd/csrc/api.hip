@@ -159,8 +159,9 @@ parallax_status_t check_prefill(const parallax_prefill_args_t *a) {
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 64, 128)",
                     a->head_dim);
     const int group = a->num_q_heads / a->num_kv_heads;
-    if (group != 1 && group != 2 && group != 4 && group != 8)
-        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: GQA group %d (supported: 1, 2, 4, 8)", group);
+    if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: GQA group %d (supported: 1, 2, 4, 8, 16)",
+                    group);
     if ((int64_t)a->batch * a->num_q_heads * ((a->seq_len + 31) / 32) > 0x7fffffffLL)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: grid too large");
     if (!aligned16(a->q) || !aligned16(a->rho) || !aligned16(a->k) || !aligned16(a->v) ||
@@ -212,9 +213,9 @@ parallax_status_t check_prefill_backward(const parallax_prefill_backward_args_t 
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill backward: head_dim %d (supported: 64, 128)",
                     a->head_dim);
     const int group = a->num_q_heads / a->num_kv_heads;
-    if (group != 1 && group != 2 && group != 4 && group != 8)
+    if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
         return fail(PARALLAX_ERR_UNSUPPORTED,
-                    "prefill backward: GQA group %d (supported: 1, 2, 4, 8)", group);
+                    "prefill backward: GQA group %d (supported: 1, 2, 4, 8, 16)", group);
     if ((int64_t)a->batch * a->num_q_heads * ((a->seq_len + 31) / 32) > 0x7fffffffLL ||
         (int64_t)a->batch * a->num_q_heads * a->seq_len > 0x7fffffffLL * 16LL)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill backward: grid too large");

@@ -27,7 +27,7 @@
 // one wave's MFMAs overlap the other's VALU work (a single wave per SIMD keeps
 // the matrix core about a third busy).  The pairs cover 128/G rows of each of
 // the G query heads of one KV head, so every 32-key K/V tile in LDS serves the
-// whole GQA group.  K and V tiles of 32 keys are double-buffered in LDS with
+// whole GQA group (G <= 4; larger groups run as blocks of four heads).  K and V tiles of 32 keys are double-buffered in LDS with
 // one barrier per tile: in the epoch where the score waves work on tile t and
 // the value waves on tile t - 1, K tile t + 1 and V tile t are written to LDS;
 // global loads run two tiles ahead of those stores.  V reaches the MFMA
@@ -433,8 +433,8 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
     }
 }
 
-// GQA group 8: two workgroups of four query heads each per KV head (each
-// loads the KV tiles once for its four heads).
+// GQA groups 8 and 16: G / 4 workgroups of four query heads each per KV head
+// (each loads the KV tiles once for its four heads).
 template <int D>
 hipError_t launch_prefill_d(const PrefillParams &pin, hipStream_t stream) {
     PrefillParams p = pin;

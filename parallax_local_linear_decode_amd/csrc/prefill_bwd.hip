@@ -698,8 +698,9 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
     }
 }
 
-// GQA group 8: the dq kernel runs two workgroups of four query heads per KV
-// head; the dk/dv kernel streams all eight heads' rows past each key block.
+// GQA groups 8 and 16: the dq kernel runs G / 4 workgroups of four query
+// heads per KV head; the dk/dv kernel streams all G heads' rows past each
+// key block.
 template <int D, int G, bool WIN>
 hipError_t launch_bwd(const PrefillBwdParams &pin, hipStream_t stream) {
     constexpr int GQ = G > 4 ? 4 : G;  // query heads per dq workgroup
@@ -733,6 +734,8 @@ hipError_t launch_prefill_backward_d(const PrefillBwdParams &p, hipStream_t stre
         case 9: return launch_bwd<D, 4, true>(p, stream);
         case 16: return launch_bwd<D, 8, false>(p, stream);
         case 17: return launch_bwd<D, 8, true>(p, stream);
+        case 32: return launch_bwd<D, 16, false>(p, stream);
+        case 33: return launch_bwd<D, 16, true>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }

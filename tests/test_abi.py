@@ -159,7 +159,7 @@ def good_prefill(**over):
     (dict(k_stride_s=-1), INVALID, "non-negative"),
     (dict(causal=0), UNSUPP, "causal"),
     (dict(head_dim=96), UNSUPP, "head_dim"),
-    (dict(num_q_heads=128), UNSUPP, "GQA group"),
+    (dict(num_q_heads=256), UNSUPP, "GQA group"),
     (dict(num_q_heads=24), UNSUPP, "GQA group"),
     (dict(v=FAKE + 2), UNSUPP, "aligned"),
     (dict(q_stride_s=2052), UNSUPP, "16 bytes"),
@@ -240,7 +240,7 @@ def test_backward_workspace_size(lib):
     (dict(window=-1), INVALID, "window"),
     (dict(causal=0), UNSUPP, "causal"),
     (dict(head_dim=96), UNSUPP, "head_dim"),
-    (dict(num_q_heads=128), UNSUPP, "GQA group"),
+    (dict(num_q_heads=256), UNSUPP, "GQA group"),
     (dict(rmean=FAKE + 8), UNSUPP, "aligned"),
     (dict(dout_stride_h=132), UNSUPP, "16 bytes"),
     (dict(dq_stride_s=2050), UNSUPP, "16 bytes"),

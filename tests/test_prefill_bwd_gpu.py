@@ -5,7 +5,7 @@ through the C ABI.
 The GPU backward consumes the GPU forward's own outputs (out, o_sa, lse, r);
 the oracle recomputes everything from the inputs, so these tests check the
 whole training step.  Small cases compare every element (ragged lengths
-around the 32-row tiles and 128-row blocks, GQA groups 1/2/4/8, local windows,
+around the 32-row tiles and 128-row blocks, GQA groups 1/2/4/8/16, local windows,
 head dims 128 and 64);
 the full-size workload (batch 4 x 8192 tokens, 16 query / 8 KV heads, d 128)
 compares sampled rows of dq and drho, the last 64 keys' dk and dv (exact for
@@ -61,7 +61,7 @@ def check_stats(stats, q, rho, k, v, scale, window=0, rows=None, what=""):
 
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("S", [1, 17, 31, 32, 33, 64, 100, 129, 257])
-@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2), (8, 2), (8, 1), (16, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2), (8, 2), (8, 1), (16, 2), (16, 1)])
 def test_small_every_gradient(gpu, S, Hq, Hkv, d):
     q, rho, k, v, dout, scale = case(2, S, Hq, Hkv, S * 10 + Hq + d, gpu, d)
     stats, grads = forward_backward(q, rho, k, v, dout, scale)
@@ -74,7 +74,7 @@ def test_small_every_gradient(gpu, S, Hq, Hkv, d):
 
 @pytest.mark.parametrize("W", [1, 5, 31, 32, 33, 100])
 @pytest.mark.parametrize("S,Hq,Hkv,d", [(100, 4, 2, 128), (300, 2, 1, 128), (257, 8, 2, 128),
-                                        (300, 4, 2, 64), (200, 16, 2, 128)])
+                                        (300, 4, 2, 64), (200, 16, 2, 128), (150, 16, 1, 64)])
 def test_window_every_gradient(gpu, S, Hq, Hkv, d, W):
     q, rho, k, v, dout, scale = case(1, S, Hq, Hkv, S + W, gpu, d)
     stats, grads = forward_backward(q, rho, k, v, dout, scale, window=W)

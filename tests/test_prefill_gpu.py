@@ -31,7 +31,7 @@ def host(*ts):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("S", [1, 17, 31, 32, 33, 64, 100, 257])
-@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2), (8, 2), (8, 1), (16, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 1), (4, 2), (2, 2), (8, 2), (8, 1), (16, 2), (16, 1)])
 def test_small_all_rows(gpu, S, Hq, Hkv, d):
     q, rho, k, v, scale = prefill_inputs(2, S, Hq, Hkv, d, seed=S * 10 + Hq + d)
     ref = oracle.prefill(*host(q, rho, k, v), scale)
