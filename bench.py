@@ -508,7 +508,7 @@ def run_prefill(args, torch, plx):
     import numpy as np
     import oracle
     from parallax_local_linear_decode_amd.workloads import host_array, prefill_inputs
-    B, S, Hq, Hkv, d = 4, 8192, 16, 8, args.head_dim
+    B, S, Hq, Hkv, d = 4, 8192, args.q_heads, args.kv_heads, args.head_dim
     dev = torch.device("cuda:0")
     q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, d, seed=0, device=dev)
     out = torch.empty((B, S, Hq, d), dtype=torch.float32, device=dev)
@@ -567,14 +567,14 @@ def run_prefill(args, torch, plx):
     return {
         "metric": "Parallax causal prefill TFLOP/s (% of bf16 MFMA peak)", "value": round(tflops, 1),
         "unit": "TFLOP/s", "ms_per_step": per * 1e3, "dtype": "bf16",
-        "config": {"workload": f"causal prefill: batch 4, seq 8192, 16 query / 8 KV heads, d {d}, "
-                               f"bf16 q/rho/k/v, fp32 out{wtxt}", "batch": B, "seq_len": S,
-                   "head_dim": d, "window": W},
+        "config": {"workload": f"causal prefill: batch 4, seq 8192, {Hq} query / {Hkv} KV heads, "
+                               f"d {d}, bf16 q/rho/k/v, fp32 out{wtxt}", "batch": B, "seq_len": S,
+                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d, "window": W},
         "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "tokens_per_s": B * S / per,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_for("prefill") if W <= 0 and d == 128 else None},
+                     "traffic": traffic_for("prefill") if (W, d, Hq, Hkv) == (0, 128, 16, 8) else None},
         "cpu_baseline": cpu,
     }
 
@@ -593,7 +593,7 @@ def run_prefill_bwd(args, torch, plx):
     import oracle
     from parallax_local_linear_decode_amd.workloads import (host_array, prefill_dout,
                                                             prefill_inputs)
-    B, S, Hq, Hkv, d = 4, 8192, 16, 8, args.head_dim
+    B, S, Hq, Hkv, d = 4, 8192, args.q_heads, args.kv_heads, args.head_dim
     W = args.window
     dev = torch.device("cuda:0")
     q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, d, seed=0, device=dev)
@@ -662,13 +662,15 @@ def run_prefill_bwd(args, torch, plx):
         "metric": "Parallax causal prefill backward TFLOP/s (% of bf16 MFMA peak)",
         "value": round(tflops, 1), "unit": "TFLOP/s", "ms_per_step": per * 1e3, "dtype": "bf16",
         "config": {"workload": "causal prefill backward (dq, drho, dk, dv): batch 4, seq 8192, "
-                               f"16 query / 8 KV heads, d {d}, bf16 inputs and dout{wtxt}",
-                   "batch": B, "seq_len": S, "head_dim": d, "window": W},
+                               f"{Hq} query / {Hkv} KV heads, d {d}, bf16 inputs and dout{wtxt}",
+                   "batch": B, "seq_len": S, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": d, "window": W},
         "mfma_util": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "tokens_per_s": B * S / per,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic_for("prefill_bwd") if W <= 0 and d == 128 else None},
+                     "traffic": (traffic_for("prefill_bwd")
+                                 if (W, d, Hq, Hkv) == (0, 128, 16, 8) else None)},
         "cpu_baseline": cpu,
     }
 
@@ -697,6 +699,8 @@ def main():
                     help="local window for decode / prefill (0 = full attention)")
     ap.add_argument("--head-dim", type=int, default=128, choices=(64, 128),
                     help="head dim (workloads prefill and prefill_bwd)")
+    ap.add_argument("--q-heads", type=int, default=16, help="query heads (prefill, prefill_bwd)")
+    ap.add_argument("--kv-heads", type=int, default=8, help="KV heads (prefill, prefill_bwd)")
     ap.add_argument("--tokens", type=int, default=8, help="token rows (workload qr_proj)")
     ap.add_argument("--model-dim", type=int, default=2048, help="model dim (workload qr_proj)")
     ap.add_argument("--lla-lambda", type=float, default=0.5, help="LLA ridge term (workload lla)")
