@@ -214,12 +214,28 @@ def test_full_size_deterministic(gpu):
 
 def test_workspace_reuse_across_shapes(gpu):
     """One workspace, filled with garbage first, serves calls of different
-    shapes back to back (arrival words from other calls count as zero)."""
+    shapes back to back (its contents on entry never matter)."""
     ws = torch.randint(0, 256, (1 << 24,), dtype=torch.uint8, device=gpu)
     for i, (B, L) in enumerate([(2, 700), (8, 4096), (2, 700), (12, 3000), (5, 1500)]):
         inp = to(decode_inputs(B, 16, 8, 128, L, seed=20 + i), gpu)
         out = run(inp, workspace=ws)
         assert_parity(out, oracle_decode(inp), TAU_BF16, RMS_DECODE_BF16, what=f"reuse {i}")
+
+
+def test_side_stream_calls_grow_their_workspace(gpu):
+    """Calls on a side stream, each larger than the last, so the binding's
+    per-stream workspace grows while earlier launches may still be queued:
+    the same bits as the same calls on the default stream."""
+    shapes = [(1, 300), (4, 2000), (8, 4096), (16, 8192)]
+    inps = [to(decode_inputs(B, 16, 8, 128, L, seed=30 + i), gpu) for i, (B, L) in enumerate(shapes)]
+    want = [run(inp).clone() for inp in inps]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = [plx.parallax_decode(inp.q, inp.rho, inp.k, inp.v, scale=inp.scale) for inp in inps]
+    torch.cuda.synchronize()
+    for i, (w, g) in enumerate(zip(want, got)):
+        assert torch.equal(w, g), f"shape {shapes[i]}"
 
 
 def test_graph_replay(gpu):
