@@ -97,7 +97,7 @@ typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t head_dim;
-    float scale; /* logit scale, usually 1/sqrt(head_dim) */
+    float scale; /* logit scale, any finite value (usually 1/sqrt(head_dim)) */
 
     const float *q;
     int64_t q_stride_b, q_stride_h;
@@ -234,7 +234,8 @@ typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t head_dim;
-    float scale;
+    float scale; /* logit scale, any finite value (usually 1/sqrt(head_dim); 0 gives
+                    uniform weights over a row's keys); else PARALLAX_ERR_INVALID_ARG */
     int32_t causal;
 
     const void *q;
@@ -297,7 +298,7 @@ typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t head_dim;
-    float scale;
+    float scale; /* as the forward's: any finite value */
     int32_t causal;
     int32_t window; /* as parallax_prefill_args_t */
 

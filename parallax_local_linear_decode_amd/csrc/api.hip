@@ -9,6 +9,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+
 #include "kernels.hpp"
 
 #define PLX_EXPORT extern "C" __attribute__((visibility("default")))
@@ -535,7 +536,10 @@ PLX_EXPORT parallax_status_t parallax_prefill(const parallax_prefill_args_t *a, 
     p.seq_len = a->seq_len;
     p.num_q_heads = a->num_q_heads;
     p.num_kv_heads = a->num_kv_heads;
-    p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
+    // the kernel multiplies raw scores by a positive factor (masking and the
+    // row max rely on it); the sign of the scale moves into the query operand
+    p.q_sign = a->scale > 0.0f ? 0 : (a->scale < 0.0f ? 1 : 2);
+    p.scale_log2 = (float)(a->scale != 0.0f ? fabs((double)a->scale) * 1.4426950408889634 : 1.0);
     p.window = a->window;
     p.lse = a->lse;
     p.rmean = a->rmean;

@@ -52,7 +52,13 @@ struct PrefillParams {
     // serves the kernel's G query heads hb*G .. hb*G + G - 1 of KV head
     // hb / head_blocks (1 unless a GQA group is split over workgroups)
     int32_t head_blocks;
+    // |scale| * log2(e) (1 for scale 0): positive, so the row max of the raw
+    // scores is the row max of the logits
     float scale_log2;
+    // how the query operand enters the score products so that the logits
+    // stay scale * q.k with the positive factor above: 0 as it is (scale > 0),
+    // 1 negated (scale < 0), 2 zeroed (scale = 0: every logit 0)
+    int32_t q_sign;
     int32_t window;  // 0: keys 0..i; W >= 1: keys max(0, i-W+1)..i
     // optional outputs for a backward pass (each may be null): natural-log
     // softmax denominator and r per row, [B, Hq, S]; o_SA with out's strides

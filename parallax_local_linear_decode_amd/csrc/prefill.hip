@@ -215,8 +215,19 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
                                          : p.rho + (int64_t)b * p.r_sb + (int64_t)row * p.r_ss +
                                                (int64_t)head * p.r_sh;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                xop[cb][ks] = __builtin_bit_cast(bf16x8_t, ld16(src + DQ * g + 8 * ks));
+            for (int ks = 0; ks < KS; ++ks) {
+                uint4 w = ld16(src + DQ * g + 8 * ks);
+                // the masked scores below are set to -inf and the row max is
+                // taken on raw scores, so the factor applied to them must be
+                // positive: a negative scale negates q, a zero scale zeroes it
+                if (cb < 2 && p.q_sign != 0) {
+                    const uint32_t x = p.q_sign == 1 ? 0x80008000u : 0u;
+                    const uint32_t keep = p.q_sign == 1 ? 0xffffffffu : 0u;
+                    w = uint4{(w.x & keep) ^ x, (w.y & keep) ^ x, (w.z & keep) ^ x,
+                              (w.w & keep) ^ x};
+                }
+                xop[cb][ks] = __builtin_bit_cast(bf16x8_t, w);
+            }
         }
         float mref[2] = {-INFINITY, -INFINITY};  // base-2 reference max per query row
 

@@ -295,3 +295,31 @@ def test_graph_replay(gpu):
         for a, b in zip(want, outs):
             assert torch.equal(a, b), f"replay {r}"
         forward_backward(*other[:5], other[5])
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.4])
+@pytest.mark.parametrize("d,W", [(128, 0), (64, 0), (128, 37)])
+def test_any_finite_scale(gpu, scale, d, W):
+    """The logit scale may be zero (uniform weights over each row's keys) or
+    negative: every row of the forward, its statistics and the four
+    gradients against the oracle at the same scale."""
+    S, Hq, Hkv = 100, 4, 2
+    q, rho, k, v, dout, _ = case(1, S, Hq, Hkv, 11, gpu, d)
+    stats, grads = forward_backward(q, rho, k, v, dout, scale, window=W)
+    what = f"scale={scale} d={d} W={W}"
+    ref = oracle.prefill(*(host_array(t) for t in (q, rho, k, v)), scale, window=W)
+    assert_parity(stats[0], ref, TAU_BF16, RMS_PREFILL, what=f"{what} out")
+    check_stats(stats, q, rho, k, v, scale, window=W, what=what)
+    ref = oracle.prefill_backward(*(host_array(t) for t in (q, rho, k, v, dout)), scale,
+                                  window=W)
+    for name, g, r in zip(("dq", "drho", "dk", "dv"), grads, ref):
+        assert_parity(g, r, TAU_BWD, RMS_BWD, what=f"{what} {name}")
+    if scale == 0.0:  # uniform weights: o_SA is the mean of the row's values, dq = 0
+        vv = v.double()[0].cpu()
+        for i in (0, 1, 36, 37, 99):
+            lo = max(0, i - W + 1) if W else 0
+            want = vv[lo:i + 1].mean(0)
+            for h in range(Hq):
+                got = stats[3][0, i, h].double().cpu()
+                assert float((got - want[h // 2]).abs().max()) < 2e-2
+        assert float(grads[0].abs().max()) == 0.0

@@ -43,7 +43,7 @@ def test_window_decode(gpu, kv_dtype, d, G):
     inp = decode_inputs(B, Hkv * G, Hkv, d, Lcap, kv_dtype=kv_dtype, seed=G * 7 + d)
     inp.seq_lens = torch.tensor(lens, dtype=torch.int32)
     k0, v0 = inp.k.clone(), inp.v.clone()
-    tau = TAU_F32 * 5 if kv_dtype == torch.float32 else TAU_BF16
+    tau = TAU_F32 if kv_dtype == torch.float32 else TAU_BF16
     rms = None if kv_dtype == torch.float32 else RMS_DECODE_BF16
     dev_lens = inp.seq_lens.to(gpu)
     for W in WINDOWS:
@@ -84,7 +84,7 @@ def test_window_paged(gpu, kv_dtype):
     first page are NaN too."""
     inp = paged_inputs(20, 16, 8, 128, ctx_lo=1, ctx_hi=1500, seed=42, rho_zero_rows=2,
                        kv_dtype=kv_dtype)
-    tau = TAU_F32 * 5 if kv_dtype == torch.float32 else TAU_BF16
+    tau = TAU_F32 if kv_dtype == torch.float32 else TAU_BF16
     rms = None if kv_dtype == torch.float32 else RMS_DECODE_BF16
     NB = inp.k.shape[0] - 1  # the all-NaN page
     for W in (1, 17, 100, 1000):
