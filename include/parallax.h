@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 3
+#define PARALLAX_ABI_VERSION 4 /* 4 added parallax_decode_no_alloc */
 
 typedef enum {
     PARALLAX_OK = 0,
@@ -139,6 +139,31 @@ parallax_status_t parallax_decode_workspace_size(const parallax_decode_args_t *a
 /* Enqueue a decode.  workspace may be NULL only if the required size is 0. */
 parallax_status_t parallax_decode(const parallax_decode_args_t *args, void *workspace,
                                   size_t workspace_bytes, void *hip_stream);
+
+/*
+ * parallax_decode without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the split partials go to a scratch array that the
+ * library owns on each device, PARALLAX_NO_ALLOC_SCRATCH_BYTES bytes, held
+ * from the library's first use on that device until the process ends.  The
+ * caller still provides every input and the output.  No call here allocates
+ * or frees memory; the first call on a device looks up the array's address
+ * there (a device's code is loaded by its first launch, as for any entry
+ * point).
+ *   - Same arguments, kernels and results as parallax_decode while the
+ *     partials of the library's split choice fit the scratch (bit for bit).
+ *     Beyond that, with split_tokens = 0 the call takes fewer, longer splits
+ *     (down to one, which needs no partials), so results then differ from
+ *     parallax_decode's by fp32 rounding only; with an explicit split_tokens
+ *     whose partials exceed the scratch it returns PARALLAX_ERR_WORKSPACE.
+ *   - Every call on a device shares that device's scratch, and nothing in it
+ *     has to be cleared between calls: two calls that can overlap on one
+ *     device (different streams, concurrently replayed graphs) race and may
+ *     return wrong results.  Serialise them, or use parallax_decode with
+ *     separate workspaces.
+ */
+#define PARALLAX_NO_ALLOC_SCRATCH_BYTES (64u << 20)
+parallax_status_t parallax_decode_no_alloc(const parallax_decode_args_t *args, void *hip_stream);
 
 /* --------------------------------------------- LLA solved-probe decode --- */
 /*

@@ -30,7 +30,9 @@ PARALLAX_ERR_WORKSPACE = 3
 PARALLAX_ERR_HIP = 4
 PARALLAX_F32 = 0
 PARALLAX_BF16 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
+# bytes of the library-owned scratch parallax_decode_no_alloc uses per device
+NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
 _i32, _i64, _u32, _f32, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float,
                                ctypes.c_void_p)
@@ -128,6 +130,8 @@ def load_library():
                                                    ctypes.POINTER(ctypes.c_size_t)]
     lib.parallax_decode.restype = ctypes.c_int
     lib.parallax_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp, ctypes.c_size_t, _vp]
+    lib.parallax_decode_no_alloc.restype = ctypes.c_int
+    lib.parallax_decode_no_alloc.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
     lib.parallax_prefill.restype = ctypes.c_int
     lib.parallax_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
     lib.parallax_decode_lla_workspace_size.restype = ctypes.c_int
@@ -292,6 +296,22 @@ def parallax_decode(q, rho, k, v, *, scale=None, seq_lens=None, block_table=None
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.parallax_decode(ctypes.byref(a), ws_ptr, ws_bytes, s)
+    if st != PARALLAX_OK:
+        _raise(st, lib)
+    return out
+
+
+def parallax_decode_no_alloc(q, rho, k, v, out, *, scale=None, seq_lens=None, block_table=None,
+                             max_seq_len=None, split_tokens=0, window=0, stream=None):
+    """parallax_decode without a workspace: the split partials live in the
+    library's per-device scratch (NO_ALLOC_SCRATCH_BYTES), so neither this
+    call nor the library allocates; `out` (float32 [B, Hq, d]) must be given.
+    Calls that may overlap on one device race on that scratch.  Same
+    arguments as parallax_decode otherwise; returns out."""
+    lib = load_library()
+    a = _decode_args(q, rho, k, v, out, scale, seq_lens, block_table, max_seq_len, split_tokens,
+                     window)
+    st = lib.parallax_decode_no_alloc(ctypes.byref(a), _stream_handle(q, stream))
     if st != PARALLAX_OK:
         _raise(st, lib)
     return out
@@ -517,7 +537,8 @@ def parallax_prefill_attention(q, rho, k, v, *, scale=None, window=0):
 
 
 __all__ = [
-    "parallax_decode", "parallax_decode_workspace_size", "parallax_prefill",
+    "parallax_decode", "parallax_decode_workspace_size", "parallax_decode_no_alloc",
+    "parallax_prefill",
     "parallax_prefill_backward", "parallax_prefill_attention", "PrefillBackwardArgs",
     "parallax_decode_lla", "LlaArgs",
     "parallax_qr_projection", "ProjectionArgs",

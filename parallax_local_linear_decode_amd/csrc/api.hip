@@ -9,6 +9,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -360,6 +362,78 @@ parallax_status_t hip_status(hipError_t e, const char *what) {
     return fail(PARALLAX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ---- the no-allocation decode's scratch ----------------------------------
+// Its split partials live in a library-owned device array instead of a
+// caller workspace.  In host code `scratch` names a host-side shadow, not the
+// device memory: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is used.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[PARALLAX_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the device `stream` belongs to (the current
+// device for the null stream).
+parallax_status_t scratch_address(hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_status(e, "decode (no alloc): device of the stream");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PARALLAX_ERR_UNSUPPORTED, "decode (no alloc): device %d beyond %d", dev,
+                    kMaxDevices);
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr != nullptr) {
+        *out = ptr;
+        return PARALLAX_OK;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return hip_status(e, "decode (no alloc): scratch address");
+        if (ptr == nullptr)
+            return fail(PARALLAX_ERR_HIP, "decode (no alloc): scratch address is NULL");
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return PARALLAX_OK;
+}
+
+// The decode plan, with the split raised (fewer splits, smaller partials)
+// when the library's choice needs more than the scratch holds.
+parallax_status_t plan_decode_no_alloc(const parallax_decode_args_t *a, DecodePlan *pl) {
+    parallax_status_t s = plan_decode(a, pl);
+    if (s != PARALLAX_OK || pl->workspace_bytes <= PARALLAX_NO_ALLOC_SCRATCH_BYTES) return s;
+    if (a->split_tokens > 0)
+        return fail(PARALLAX_ERR_WORKSPACE,
+                    "decode (no alloc): split_tokens %d needs %zu bytes of partials, above the "
+                    "%zu-byte scratch",
+                    a->split_tokens, pl->workspace_bytes, (size_t)PARALLAX_NO_ALLOC_SCRATCH_BYTES);
+    const int64_t units = (int64_t)a->batch * a->num_kv_heads;
+    const int64_t per_split = units * pl->group * plx::partial_floats(a->head_dim) * 4;
+    const int64_t fit = (int64_t)PARALLAX_NO_ALLOC_SCRATCH_BYTES / per_split;  // splits that fit
+    const int span = a->window > 0 && a->window < a->max_seq_len - 31 ? a->window + 31
+                                                                      : a->max_seq_len;
+    int split = (int)round_up(span, kSplitQuantum);  // one split: no partials at all
+    if (fit >= 2) split = (int)round_up((span + fit - 1) / fit, kSplitQuantum);
+    pl->split = split;
+    pl->nsplit = (span + split - 1) / split;
+    pl->workspace_bytes = pl->nsplit > 1 ? (size_t)(per_split * pl->nsplit) : 0;
+    return PARALLAX_OK;
+}
+
 }  // namespace
 
 PLX_EXPORT int parallax_abi_version(void) { return PARALLAX_ABI_VERSION; }
@@ -402,6 +476,23 @@ PLX_EXPORT parallax_status_t parallax_decode(const parallax_decode_args_t *a, vo
     plx::DecodeParams p = decode_params(a, pl, workspace);
     return hip_status(plx::launch_decode(p, a->kv_dtype, a->head_dim, pl.group, pl.paged, a->batch,
                                          static_cast<hipStream_t>(hip_stream)),
+                      "decode launch");
+}
+
+PLX_EXPORT parallax_status_t parallax_decode_no_alloc(const parallax_decode_args_t *a,
+                                                      void *hip_stream) {
+    DecodePlan pl;
+    parallax_status_t s = plan_decode_no_alloc(a, &pl);
+    if (s != PARALLAX_OK) return s;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    void *ws = nullptr;
+    if (pl.workspace_bytes > 0) {
+        s = scratch_address(stream, &ws);
+        if (s != PARALLAX_OK) return s;
+    }
+    plx::DecodeParams p = decode_params(a, pl, ws);
+    return hip_status(plx::launch_decode(p, a->kv_dtype, a->head_dim, pl.group, pl.paged, a->batch,
+                                         stream),
                       "decode launch");
 }
 

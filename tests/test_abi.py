@@ -23,6 +23,7 @@ def test_exports_every_declared_function(lib):
     text = open(HEADER).read()
     names = set(re.findall(r"\b(parallax_[a-z_]+)\s*\(", text))
     assert {"parallax_decode", "parallax_prefill", "parallax_decode_workspace_size",
+            "parallax_decode_no_alloc",
             "parallax_prefill_backward", "parallax_prefill_backward_workspace_size",
             "parallax_decode_lla", "parallax_decode_lla_workspace_size", "parallax_qr_projection",
             "parallax_status_string", "parallax_last_error", "parallax_abi_version"} <= names
@@ -112,6 +113,24 @@ def test_decode_rejects(lib, over, status, needle):
     assert needle in plx.parallax_last_error()
     st = lib.parallax_decode(ctypes.byref(a), FAKE, 1 << 30, None)
     assert st == status
+    # the no-allocation variant runs the same checks, also before any HIP call
+    assert lib.parallax_decode_no_alloc(ctypes.byref(a), None) == status
+    assert needle in plx.parallax_last_error()
+
+
+def test_decode_no_alloc_rejects_an_explicit_split_beyond_its_scratch(lib):
+    """2048 sequences x 8 KV heads x 2 query heads in 256-token splits of
+    32768 tokens: 128 splits of 1040-byte records per head are 4.4 GB, far
+    beyond the library's scratch, so an explicit split is refused (on the
+    host, before any HIP call)."""
+    a = good_decode(batch=2048, max_seq_len=32768, split_tokens=256,
+                    k_stride_0=8 * 32768 * 128, k_stride_h=32768 * 128,
+                    v_stride_0=8 * 32768 * 128, v_stride_h=32768 * 128)
+    st, need = ws_size(lib, a)
+    assert st == 0 and need > plx.NO_ALLOC_SCRATCH_BYTES
+    assert lib.parallax_decode_no_alloc(ctypes.byref(a), None) == plx.PARALLAX_ERR_WORKSPACE
+    assert "scratch" in plx.parallax_last_error()
+    assert lib.parallax_decode_no_alloc(None, None) == INVALID
 
 
 def test_decode_null_args(lib):
