@@ -129,9 +129,13 @@ typedef struct {
  * Bytes of device workspace parallax_decode needs for these arguments
  * (written to *bytes; 0 when one split covers every sequence).  The
  * workspace holds one partial record (running max, Z, R, A, B) per split
- * and query head; a second, small kernel on the same stream merges them.
- * Its contents before the call do not matter.  Two calls that can run
- * concurrently need separate workspaces.  16-byte alignment is required.
+ * and query head, then one 8-byte arrival flag per split: the split that
+ * finds every flag of its sequence set merges the records, in the same
+ * launch.  A flag is set to a 64-bit tag drawn fresh for every call, and
+ * the merging split clears them to 0; any other content counts as not
+ * arrived unless it equals this call's tag (a 2^-64 chance per flag), so the
+ * workspace's contents before the call do not matter.  Two calls that can
+ * run concurrently need separate workspaces.  16-byte alignment is required.
  */
 parallax_status_t parallax_decode_workspace_size(const parallax_decode_args_t *args,
                                                  size_t *bytes);

@@ -9,6 +9,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <time.h>
+#include <unistd.h>
+
 #include <atomic>
 #include <mutex>
 
@@ -51,6 +54,35 @@ struct DecodePlan {
 };
 
 int64_t round_up(int64_t x, int64_t q) { return ((x + q - 1) / q) * q; }
+
+// Workspace of a decode plan: the split records, then one arrival word per
+// (batch, KV head) unit for the in-kernel merge; nothing for a single split.
+size_t decode_ws_bytes(int64_t units, int group, int d, int nsplit) {
+    if (nsplit <= 1) return 0;
+    return (size_t)(units * nsplit * group * plx::partial_floats(d) * 4) +
+           (size_t)plx::arrival_bytes(units, nsplit);
+}
+
+// A fresh tag per decode launch, telling this call's arrival flags from
+// whatever a workspace held before: a process-wide count, mixed with the
+// process id and start time so that the tags of different processes (and
+// bytes a workspace happened to hold) match only by chance, 1 in 2^64.
+std::atomic<unsigned long long> g_epoch{0};
+unsigned long long next_epoch() {
+    static const unsigned long long salt = [] {
+        unsigned long long x = (unsigned long long)getpid() * 0x9E3779B97F4A7C15ull;
+        x ^= (unsigned long long)time(nullptr) * 0xC2B2AE3D27D4EB4Full;
+        return x;
+    }();
+    for (;;) {
+        // splitmix64 of (salt + count): distinct counts give distinct tags
+        unsigned long long z = salt + 0x9E3779B97F4A7C15ull * (g_epoch.fetch_add(1) + 1);
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        z ^= z >> 31;
+        if (z != 0) return z;
+    }
+}
 
 int choose_split(int64_t units, int max_len) {
     int64_t split = round_up((max_len * units + kTargetWorkgroups - 1) / kTargetWorkgroups,
@@ -132,8 +164,7 @@ parallax_status_t plan_decode(const parallax_decode_args_t *a, DecodePlan *pl) {
     pl->paged = paged;
     pl->split = split;
     pl->nsplit = nsplit;
-    pl->workspace_bytes =
-        nsplit > 1 ? (size_t)units * nsplit * group * plx::partial_floats(a->head_dim) * 4 : 0;
+    pl->workspace_bytes = decode_ws_bytes(units, group, a->head_dim, nsplit);
     return PARALLAX_OK;
 }
 
@@ -273,6 +304,14 @@ plx::DecodeParams decode_params(const parallax_decode_args_t *a, const DecodePla
     p.scale_log2 = (float)((double)a->scale * 1.4426950408889634);
     p.partials = pl.workspace_bytes > 0 ? static_cast<float *>(workspace) : nullptr;
     p.window = a->window;
+    // the split records are merged by the last arriving split of each row
+    const int64_t units = (int64_t)a->batch * a->num_kv_heads;
+    p.arrivals = pl.workspace_bytes > 0
+                     ? reinterpret_cast<unsigned long long *>(
+                           static_cast<unsigned char *>(workspace) + pl.workspace_bytes -
+                           plx::arrival_bytes(units, pl.nsplit))
+                     : nullptr;
+    p.epoch = next_epoch();
     return p;
 }
 
@@ -423,14 +462,15 @@ parallax_status_t plan_decode_no_alloc(const parallax_decode_args_t *a, DecodePl
                     a->split_tokens, pl->workspace_bytes, (size_t)PARALLAX_NO_ALLOC_SCRATCH_BYTES);
     const int64_t units = (int64_t)a->batch * a->num_kv_heads;
     const int64_t per_split = units * pl->group * plx::partial_floats(a->head_dim) * 4;
-    const int64_t fit = (int64_t)PARALLAX_NO_ALLOC_SCRATCH_BYTES / per_split;  // splits that fit
+    const int64_t fit = (int64_t)PARALLAX_NO_ALLOC_SCRATCH_BYTES /
+                        (per_split + plx::arrival_bytes(units, 1));  // splits that fit
     const int span = a->window > 0 && a->window < a->max_seq_len - 31 ? a->window + 31
                                                                       : a->max_seq_len;
     int split = (int)round_up(span, kSplitQuantum);  // one split: no partials at all
     if (fit >= 2) split = (int)round_up((span + fit - 1) / fit, kSplitQuantum);
     pl->split = split;
     pl->nsplit = (span + split - 1) / split;
-    pl->workspace_bytes = pl->nsplit > 1 ? (size_t)(per_split * pl->nsplit) : 0;
+    pl->workspace_bytes = decode_ws_bytes(units, pl->group, a->head_dim, pl->nsplit);
     return PARALLAX_OK;
 }
 
@@ -531,6 +571,7 @@ PLX_EXPORT parallax_status_t parallax_decode_lla(const parallax_decode_args_t *d
     fin.rho_sb = (int64_t)dec->num_q_heads * dec->head_dim;
     fin.rho_sh = dec->head_dim;
     plx::DecodeParams sweep = fin;
+    sweep.arrivals = nullptr;  // the sweeps' records go to the merge kernel (the CG step)
     sweep.v = sweep.k;
     sweep.v_s0 = sweep.k_s0;
     sweep.v_sh = sweep.k_sh;

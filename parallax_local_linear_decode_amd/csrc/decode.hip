@@ -115,12 +115,83 @@ __device__ __forceinline__ float finish(float A, float B, float Z, float R) {
     return a - (bb - a * r);
 }
 
+// Reads and writes of split records that other compute units -- possibly on
+// another XCD, whose L2 is not coherent with this one -- exchange within one
+// launch: device-scope atomics, which go through to the device-coherent level.
+__device__ __forceinline__ float load_shared(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// o of element e of head g from the nsp split records at `recs` (one unit):
+// the running max over the records, every record's sums scaled to it.
+// Four records' loads are in flight at a time.
+template <int D, int G, bool SHARED>
+__device__ __forceinline__ float merge_records(const float *recs, int nsp, int g, int e) {
+    constexpr int REC = partial_floats(D);
+    auto ld = [](const float *q) { return SHARED ? load_shared(q) : *q; };
+    float M = -INFINITY, Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
+    for (int c0 = 0; c0 < nsp; c0 += 4) {
+        float mm[4], zz[4], rr[4], aa[4], bb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float *rec = recs + (min(c0 + i, nsp - 1) * G + g) * REC;
+            const bool live = c0 + i < nsp;
+            mm[i] = live ? ld(rec + 2 * D) : -INFINITY;
+            zz[i] = ld(rec + 2 * D + 1);
+            rr[i] = ld(rec + 2 * D + 2);
+            aa[i] = ld(rec + e);
+            bb[i] = ld(rec + D + e);
+        }
+        const float Mn = fmaxf(fmaxf(M, fmaxf(mm[0], mm[1])), fmaxf(mm[2], mm[3]));
+        const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        Z *= sc;
+        R *= sc;
+        A *= sc;
+        B *= sc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float al = mm[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[i] - Mn);
+            Z += al * zz[i];
+            R += al * rr[i];
+            A += al * aa[i];
+            B += al * bb[i];
+        }
+        M = Mn;
+    }
+    return finish(A, B, Z, R);
+}
+
+// Arrival of split `split_idx` of `unit`, by one wave of the workgroup once
+// every wave's record stores are complete at device scope: set this split's
+// flag, then read the row's flags.  True if all nsp carry this call's tag --
+// then every record of the row is complete.  The split whose flag lands last
+// sees them all; one that lands at nearly the same time may too, and both
+// merge (the same records give the same bits).
+__device__ __forceinline__ bool arrive_all(const DecodeParams &p, int unit, int split_idx, int nsp,
+                                           int lane) {
+    unsigned long long *f = p.arrivals + (int64_t)unit * p.nsplit;
+    if (lane == 0)
+        __hip_atomic_store(f + split_idx, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    bool mine = true;
+    for (int i = lane; i < nsp; i += 64)
+        mine &= __hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.epoch;
+    return __all(mine);
+}
+
 // Merge NW per-wave records (red[w][head][...]) of this workgroup; write
-// the output if the row has a single split, else this split's record.
+// the output if the row has a single split, else this split's record -- and,
+// with the in-kernel merge, let the row's last arriving split merge them.
 template <int D, int G, int NW>
 __device__ void finish_block(const DecodeParams &p, float (*red)[G][partial_floats(D)], int b,
                              int hk, int unit, int split_idx, int nsp) {
     constexpr int REC = partial_floats(D);
+    const bool fused = p.arrivals != nullptr && nsp > 1;
     for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
         const int g = idx / D, e = idx % D;
         float M = -INFINITY;
@@ -139,15 +210,53 @@ __device__ void finish_block(const DecodeParams &p, float (*red)[G][partial_floa
             p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = finish(A, B, Z, R);
         } else {
             float *rec = p.partials + (((int64_t)unit * p.nsplit + split_idx) * G + g) * REC;
-            rec[e] = A;
-            rec[D + e] = B;
-            if (e == 0) {
-                rec[2 * D] = M;
-                rec[2 * D + 1] = Z;
-                rec[2 * D + 2] = R;
+            if (fused) {
+                store_shared(rec + e, A);
+                store_shared(rec + D + e, B);
+                if (e == 0) {
+                    store_shared(rec + 2 * D, M);
+                    store_shared(rec + 2 * D + 1, Z);
+                    store_shared(rec + 2 * D + 2, R);
+                }
+            } else {
+                rec[e] = A;
+                rec[D + e] = B;
+                if (e == 0) {
+                    rec[2 * D] = M;
+                    rec[2 * D + 1] = Z;
+                    rec[2 * D + 2] = R;
+                }
             }
         }
     }
+    if (!fused) return;
+    // Every thread waits until its record stores are complete at device
+    // scope (vmcnt counts stores on this architecture); then one thread
+    // counts the workgroup in.  No release fence: the records themselves
+    // were written through to the device-coherent level.
+    __shared__ int last;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const bool all = arrive_all(p, unit, split_idx, nsp, threadIdx.x);
+        if (threadIdx.x == 0) last = all ? 1 : 0;
+    }
+    __syncthreads();
+    if (!last) return;
+    const float *recs = p.partials + (int64_t)unit * p.nsplit * G * REC;
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
+        const int g = idx / D, e = idx % D;
+        p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] =
+            merge_records<D, G, true>(recs, nsp, g, e);
+    }
+    // Every split of the row has arrived: clear its flags, so that the next
+    // launch with this tag (a replayed graph) starts from none.  A split
+    // still reading them then sees fewer than all and does not merge.
+    for (int i = threadIdx.x; i < nsp; i += 64 * NW)
+        __hip_atomic_store(p.arrivals + (int64_t)unit * p.nsplit + i, 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ===================================================== bf16: matrix cores ===
@@ -649,36 +758,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, LlaPa
         const float *recs = p.partials + (int64_t)unit * p.nsplit * G * REC;
         for (int idx = threadIdx.x; idx < G * D; idx += 256) {
             const int g = idx / D, e = idx % D;
-            float M = -INFINITY, Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
-            for (int c0 = 0; c0 < nsp; c0 += 4) {  // four records' loads in flight at once
-                float mm[4], zz[4], rr[4], aa[4], bb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float *rec = recs + (min(c0 + i, nsp - 1) * G + g) * REC;
-                    const bool live = c0 + i < nsp;
-                    mm[i] = live ? rec[2 * D] : -INFINITY;
-                    zz[i] = rec[2 * D + 1];
-                    rr[i] = rec[2 * D + 2];
-                    aa[i] = rec[e];
-                    bb[i] = rec[D + e];
-                }
-                const float Mn = fmaxf(fmaxf(M, fmaxf(mm[0], mm[1])), fmaxf(mm[2], mm[3]));
-                const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-                Z *= sc;
-                R *= sc;
-                A *= sc;
-                B *= sc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float al = mm[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[i] - Mn);
-                    Z += al * zz[i];
-                    R += al * rr[i];
-                    A += al * aa[i];
-                    B += al * bb[i];
-                }
-                M = Mn;
-            }
-            const float o = finish(A, B, Z, R);
+            const float o = merge_records<D, G, false>(recs, nsp, g, e);
             if constexpr (LLA) osh[g][e] = o;
             else p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = o;
         }
@@ -722,7 +802,7 @@ hipError_t launch_all(const DecodeParams &p, bool bf16, int batch, hipStream_t s
     if (lla != nullptr)
         hipLaunchKernelGGL((decode_merge_kernel<D, G, PAGED, true>), dim3(units), dim3(256), 0,
                            stream, p, *lla);
-    else if (p.nsplit > 1)
+    else if (p.nsplit > 1 && p.arrivals == nullptr)
         hipLaunchKernelGGL((decode_merge_kernel<D, G, PAGED, false>), dim3(units), dim3(256), 0,
                            stream, p, LlaParams{});
     return hipGetLastError();

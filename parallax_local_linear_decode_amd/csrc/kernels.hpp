@@ -34,7 +34,20 @@ struct DecodeParams {
     float scale_log2;   // logit scale times log2(e): logits are kept in base 2
     float *partials;    // [B*Hkv*nsplit][G][partial_floats(d)] or null when nsplit == 1
     int32_t window;     // 0: every cached token; W >= 1: each row's last W tokens
+    // Split merge inside the split kernel: when non-null, one 64-bit arrival
+    // flag per split of every (batch, KV head) unit, [units][nsplit], right
+    // after the partials.  A split sets its flag to `epoch` once its records
+    // are complete; a split that then finds every flag of its row set merges
+    // the row and clears the flags.  Null: the partials are left for
+    // decode_merge_kernel.
+    unsigned long long *arrivals;
+    unsigned long long epoch;  // this call's tag, never 0
 };
+
+// Arrival flags after the partials, 8-byte aligned (records are 16).
+__host__ __device__ constexpr int64_t arrival_bytes(int64_t units, int nsplit) {
+    return units * nsplit * 8;
+}
 
 struct PrefillParams {
     const uint16_t *q;

@@ -69,9 +69,10 @@ def test_valid_decode_plan(lib):
     # a single split needs no workspace
     st, n = ws_size(lib, good_decode(split_tokens=4096))
     assert st == plx.PARALLAX_OK and n == 0
-    # explicit split: one record (A, B: d floats each; m, Z, R, pad) per split and head
+    # explicit split: one record (A, B: d floats each; m, Z, R, pad) per split and head,
+    # then one 8-byte arrival flag per split for the in-kernel merge
     st, n = ws_size(lib, good_decode(split_tokens=1024))
-    assert n == 64 * 4 * 2 * (2 * 128 + 4) * 4
+    assert n == 64 * 4 * 2 * (2 * 128 + 4) * 4 + 64 * 4 * 8
 
 
 INVALID = plx.PARALLAX_ERR_INVALID_ARG
