@@ -39,10 +39,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "Parallax decode KV GB/s (% of HBM peak) + tokens/s over batch×ctx sweep"
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
-# elementwise bound of the backward's gradients, max |g - r| / (1 + |r|): the
-# floor set by the bf16 numerators of the forward and the bf16 gradient
-# weights (derived on the CPU in the test suite's rounding model)
-TAU_BWD = 0.15
+# elementwise bound of the backward's gradients, max |g - r| / (1 + |r|):
+# twice the worst ratio of a model of the forward's bf16 numerators and the
+# backward's bf16 weights (tests/test_backward_tolerance.py)
+TAU_BWD = 0.1
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Decode over a bf16 cache runs on bf16 matrix cores (q, rho and the softmax
 # weights enter as two-term bf16 splits; sums accumulate in fp32).

@@ -241,7 +241,12 @@ _workspaces: dict = {}
 
 def _workspace(device, stream, nbytes):
     """A workspace per (device, stream), grown on demand and reused across
-    calls (its contents need no initialisation)."""
+    calls (its contents need no initialisation).  Not under graph capture:
+    growing it would synchronise, and graphs captured on one stream would
+    share it, so a captured call must bring its own workspace."""
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("under HIP graph capture, pass workspace= (a buffer the graph owns) "
+                           "or use parallax_decode_no_alloc")
     key = (str(device), stream.value)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:

@@ -12,13 +12,12 @@ TAU_F32 = 1e-5
 TAU_BF16 = 2e-2
 RMS_DECODE_BF16 = 1e-3
 RMS_PREFILL = 1e-2
-# Prefill backward: the kernels round the weights p (1 + r - t), ds and dt to
-# bf16 before the gradient products, and the forward's statistics carry its own
-# bf16 rounding.  dt_j = p_j (c - u_j) sums to zero over a row's keys, so drho
-# is a cancelling sum whose per-term rounding does not cancel: a simulation of
-# these rounding steps at the test shapes gives elementwise ratios up to
-# 8.8e-2 (drho) and relative RMS errors up to 2.1e-3 for all four gradients.
-TAU_BWD = 0.15
+# Prefill backward: the forward keeps its statistics from bf16-rounded softmax
+# numerators and the backward rounds its weights p (1 + r - t), ds and dt to
+# bf16; tests/test_backward_tolerance.py models both roundings in fp64 at the
+# shapes of the GPU tests and checks that this bound is at least twice the
+# modelled worst ratio (4.8e-2, drho: a cancelling sum) and at most four times.
+TAU_BWD = 0.1
 RMS_BWD = 1e-2
 
 

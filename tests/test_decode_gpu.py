@@ -319,3 +319,37 @@ def test_paged_full_size_sampled(gpu):
     q, rho, k, v, sl, table = gather_sequences(inp, pick)
     ref = oracle.decode(q, rho, k, v, inp.scale, seq_lens=sl, block_table=table)
     assert_parity(out[pick], ref, TAU_BF16, RMS_DECODE_BF16, what="paged full")
+
+
+def test_graph_capture_needs_an_explicit_workspace(gpu):
+    """Under capture the binding does not hand out its cached per-stream
+    workspace (growing it would synchronise, and graphs captured on one
+    stream would share it): a call without workspace= raises, one with it is
+    captured and replays correctly."""
+    inp = to(decode_inputs(4, 16, 8, 128, 2000, seed=32), gpu)
+    ref = oracle_decode(inp)
+    s = torch.cuda.Stream()
+    out = torch.empty((4, 16, 128), dtype=torch.float32, device=gpu)
+    with torch.cuda.stream(s):
+        run(inp, out=out)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            try:  # refused on the host, before any HIP call
+                plx.parallax_decode(inp.q, inp.rho, inp.k, inp.v, scale=inp.scale, out=out)
+                refused = ""
+            except RuntimeError as e:
+                refused = str(e)
+            out.zero_()
+    torch.cuda.synchronize()
+    assert "workspace" in refused
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=gpu)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            plx.parallax_decode(inp.q, inp.rho, inp.k, inp.v, scale=inp.scale, out=out,
+                                workspace=ws)
+    for r in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert_parity(out, ref, TAU_BF16, RMS_DECODE_BF16, what=f"replay {r}")

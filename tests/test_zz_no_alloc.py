@@ -84,3 +84,29 @@ def test_out_must_be_given(gpu):
     inp = decode_inputs(1, 2, 1, 64, 10, seed=6, device=gpu)
     with pytest.raises(TypeError):
         plx.parallax_decode_no_alloc(inp.q, inp.rho, inp.k, inp.v, scale=inp.scale)
+
+
+def test_captured_graph_replays(gpu):
+    """The entry point under HIP graph capture (no workspace to bring): three
+    replays, with eager calls of another shape on the same scratch between
+    them, each checked against the workspace entry point's result."""
+    inp = decode_inputs(4, 16, 8, 128, 3000, seed=7, device=gpu)
+    other = decode_inputs(2, 16, 8, 128, 900, seed=8, device=gpu)
+    want, _ = both(inp)
+    out = torch.empty_like(want)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plx.parallax_decode_no_alloc(inp.q, inp.rho, inp.k, inp.v, out, scale=inp.scale)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            plx.parallax_decode_no_alloc(inp.q, inp.rho, inp.k, inp.v, out, scale=inp.scale)
+    torch.cuda.synchronize()
+    o2 = torch.empty((2, 16, 128), dtype=torch.float32, device=gpu)
+    for r in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {r}"
+        plx.parallax_decode_no_alloc(other.q, other.rho, other.k, other.v, o2, scale=other.scale)
+        torch.cuda.synchronize()
