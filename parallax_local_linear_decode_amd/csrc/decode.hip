@@ -127,16 +127,18 @@ __device__ __forceinline__ void store_shared(float *p, float v) {
 
 // o of element e of head g from the nsp split records at `recs` (one unit):
 // the running max over the records, every record's sums scaled to it.
-// Four records' loads are in flight at a time.
+// Sixteen records' loads are in flight at a time (one round trip for up to
+// sixteen splits: rows with many short splits wait on few dependent reads).
+constexpr int kMergeChunk = 16;
 template <int D, int G, bool SHARED>
 __device__ __forceinline__ float merge_records(const float *recs, int nsp, int g, int e) {
     constexpr int REC = partial_floats(D);
     auto ld = [](const float *q) { return SHARED ? load_shared(q) : *q; };
     float M = -INFINITY, Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
-    for (int c0 = 0; c0 < nsp; c0 += 4) {
-        float mm[4], zz[4], rr[4], aa[4], bb[4];
+    for (int c0 = 0; c0 < nsp; c0 += kMergeChunk) {
+        float mm[kMergeChunk], zz[kMergeChunk], rr[kMergeChunk], aa[kMergeChunk], bb[kMergeChunk];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kMergeChunk; ++i) {
             const float *rec = recs + (min(c0 + i, nsp - 1) * G + g) * REC;
             const bool live = c0 + i < nsp;
             mm[i] = live ? ld(rec + 2 * D) : -INFINITY;
@@ -145,14 +147,16 @@ __device__ __forceinline__ float merge_records(const float *recs, int nsp, int g
             aa[i] = ld(rec + e);
             bb[i] = ld(rec + D + e);
         }
-        const float Mn = fmaxf(fmaxf(M, fmaxf(mm[0], mm[1])), fmaxf(mm[2], mm[3]));
+        float Mn = M;
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) Mn = fmaxf(Mn, mm[i]);
         const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
         Z *= sc;
         R *= sc;
         A *= sc;
         B *= sc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kMergeChunk; ++i) {
             const float al = mm[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[i] - Mn);
             Z += al * zz[i];
             R += al * rr[i];
