@@ -177,7 +177,7 @@ def cpu_baseline_decode(inp, nbytes, budget_s=10.0, window=0):
                  "sample": f"the full workload, {reps} repetition(s), fp64 streaming form"}
 
 
-def read_stream(torch, plx, nbytes, n_bufs, steps, warmup):
+def read_stream(torch, plx, nbytes, n_bufs, steps, warmup, decode_shape_wgs=0):
     """The HBM reference: a plain read-only streaming kernel (its own library,
     libparallax_probe.so) over the same bytes per step and the same number of
     rotating cold copies as the workload; GB/s."""
@@ -200,10 +200,28 @@ def read_stream(torch, plx, nbytes, n_bufs, steps, warmup):
                                    ctypes.c_void_p(sink.data_ptr()), stream) != 0:
             raise SystemExit("read stream probe failed to launch")
     per = time_launches(torch, launch, n_bufs, steps, warmup) / steps
+    rec = {"gbps": round(size / per / 1e9, 2), "bytes": size, "cold_copies": n_bufs,
+           "kernel": "grid-stride 16-byte loads, 2048 x 256 threads (libparallax_probe)"}
+    if decode_shape_wgs:
+        # the same bytes read in the decode kernel's shape with no arithmetic:
+        # the floor that grid shape leaves for a decode step
+        lib.parallax_probe_read_decode_shape.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                                         ctypes.c_int, ctypes.c_void_p,
+                                                         ctypes.c_void_p]
+
+        def launch2(i):
+            if lib.parallax_probe_read_decode_shape(ctypes.c_void_p(bufs[i].data_ptr()), size,
+                                                    decode_shape_wgs,
+                                                    ctypes.c_void_p(sink.data_ptr()),
+                                                    stream) != 0:
+                raise SystemExit("decode-shape read probe failed to launch")
+        per2 = time_launches(torch, launch2, n_bufs, steps, warmup) / steps
+        rec["decode_shape"] = {"gbps": round(size / per2 / 1e9, 2), "us": round(per2 * 1e6, 2),
+                               "kernel": f"{decode_shape_wgs} workgroups x 8 waves, one 32-row "
+                                         "step of K and of V in flight per wave, no arithmetic"}
     del bufs
     torch.cuda.empty_cache()
-    return {"gbps": round(size / per / 1e9, 2), "bytes": size, "cold_copies": n_bufs,
-            "kernel": "grid-stride 16-byte loads, 2048 x 256 threads (libparallax_probe)"}
+    return rec
 
 
 def run_decode(args, torch, plx):
@@ -242,7 +260,8 @@ def run_decode(args, torch, plx):
     traffic = traffic_for(key) if W <= 0 and key else None
     del sets, launch, out  # the read stream needs the memory of a large cache
     torch.cuda.empty_cache()
-    stream_ref = read_stream(torch, plx, kv_bytes, n_bufs, args.steps, args.warmup)
+    wgs = 256 if (B, L, W, args.split) == (8, 4096, 0, 0) else 0  # the library's grid there
+    stream_ref = read_stream(torch, plx, kv_bytes, n_bufs, args.steps, args.warmup, wgs)
     return {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s",
         "ms_per_step": per * 1e3, "dtype": DECODE_DTYPE,
