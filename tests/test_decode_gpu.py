@@ -353,3 +353,26 @@ def test_graph_capture_needs_an_explicit_workspace(gpu):
         g.replay()
         torch.cuda.synchronize()
         assert_parity(out, ref, TAU_BF16, RMS_DECODE_BF16, what=f"replay {r}")
+
+
+def test_concurrent_calls_on_two_streams(gpu):
+    """Two decodes with their own workspaces running at the same time on two
+    streams (their splits' merges in flight together, rows of different
+    lengths and split counts) return the bits of the same calls run one
+    after the other; repeated a few times."""
+    a = to(decode_inputs(8, 16, 8, 128, 4096, seed=40), gpu)
+    b = to(decode_inputs(2, 16, 8, 128, 20000, seed=41), gpu)
+    want_a, want_b = run(a).clone(), run(b).clone()
+    wa = torch.randint(0, 256, (1 << 22,), dtype=torch.uint8, device=gpu)
+    wb = torch.randint(0, 256, (1 << 22,), dtype=torch.uint8, device=gpu)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for i in range(5):
+        sa.wait_stream(torch.cuda.current_stream())
+        sb.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(sa):
+            oa = plx.parallax_decode(a.q, a.rho, a.k, a.v, scale=a.scale, workspace=wa)
+        with torch.cuda.stream(sb):
+            ob = plx.parallax_decode(b.q, b.rho, b.k, b.v, scale=b.scale, workspace=wb)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, want_a), f"round {i}: stream a"
+        assert torch.equal(ob, want_b), f"round {i}: stream b"
