@@ -235,18 +235,28 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
         // 32t + 16rb + 4g + j.
         auto scores = [&](int t, f32x4_t (&d1)[2][4]) {
             const unsigned char *kt = ktile[t & 1];
+            // every K operand of the tile is read before the first MFMA, so
+            // the LDS latency is paid once per tile rather than once per
+            // pair of reads (the compiler otherwise reuses the operand
+            // registers and waits on each pair in turn)
+            bf16x8_t kop[2][KS];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kop[rb][ks] = __builtin_bit_cast(
+                        bf16x8_t, ld16(kt + (16 * rb + c) * RB + 2 * DQ * g + 16 * ks));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8_t kop = __builtin_bit_cast(
-                        bf16x8_t, ld16(kt + (16 * rb + c) * RB + 2 * DQ * g + 16 * ks));
 #pragma unroll
                     for (int cb = 0; cb < 4; ++cb)
-                        d1[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, xop[cb][ks],
-                                                                             d1[rb][cb], 0, 0, 0);
+                        d1[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            kop[rb][ks], xop[cb][ks], d1[rb][cb], 0, 0, 0);
                 }
             }
         };

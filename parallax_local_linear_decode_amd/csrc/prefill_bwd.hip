@@ -296,16 +296,25 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 du[rb][0] = du[rb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                // the half's K and V operands are all read before its MFMAs
+                // (one LDS latency per half, not one per pair of reads)
+                bf16x8_t kop[KS], vop[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8_t kop = __builtin_bit_cast(
+                    kop[ks] = __builtin_bit_cast(
                         bf16x8_t, ld16(kt + (16 * rb + c) * RB + 2 * DQ * g + 16 * ks));
-                    const bf16x8_t vop = __builtin_bit_cast(
+                    vop[ks] = __builtin_bit_cast(
                         bf16x8_t, ld16(vt + (16 * rb + c) * RB + 2 * DQ * g + 16 * ks));
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int cb = 0; cb < 4; ++cb) d1[rb][cb] = mfma(kop, xop[cb][ks], d1[rb][cb]);
+                for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-                    for (int qc = 0; qc < 2; ++qc) du[rb][qc] = mfma(vop, gop[qc][ks], du[rb][qc]);
+                    for (int cb = 0; cb < 4; ++cb)
+                        d1[rb][cb] = mfma(kop[ks], xop[cb][ks], d1[rb][cb]);
+#pragma unroll
+                    for (int qc = 0; qc < 2; ++qc)
+                        du[rb][qc] = mfma(vop[ks], gop[qc][ks], du[rb][qc]);
                 }
             }
         };
@@ -546,17 +555,24 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dkv_kernel(PrefillBwdParam
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc)
                     sd[rb][kc] = td[rb][kc] = ud[rb][kc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                // the half's q, rho and dout operands are all read before its
+                // MFMAs (one LDS latency per half, not one per three reads)
+                bf16x8_t qa[KS], ra[KS], ga[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int off = (16 * rb + c) * RB + 2 * DQ * g + 16 * ks;
-                    const bf16x8_t qa = __builtin_bit_cast(bf16x8_t, ld16(qtile + buf + off));
-                    const bf16x8_t ra = __builtin_bit_cast(bf16x8_t, ld16(rtile + buf + off));
-                    const bf16x8_t ga = __builtin_bit_cast(bf16x8_t, ld16(gtile + buf + off));
+                    qa[ks] = __builtin_bit_cast(bf16x8_t, ld16(qtile + buf + off));
+                    ra[ks] = __builtin_bit_cast(bf16x8_t, ld16(rtile + buf + off));
+                    ga[ks] = __builtin_bit_cast(bf16x8_t, ld16(gtile + buf + off));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                     for (int kc = 0; kc < 2; ++kc) {
-                        sd[rb][kc] = mfma(qa, kop[kc][ks], sd[rb][kc]);
-                        td[rb][kc] = mfma(ra, kop[kc][ks], td[rb][kc]);
-                        ud[rb][kc] = mfma(ga, vop[kc][ks], ud[rb][kc]);
+                        sd[rb][kc] = mfma(qa[ks], kop[kc][ks], sd[rb][kc]);
+                        td[rb][kc] = mfma(ra[ks], kop[kc][ks], td[rb][kc]);
+                        ud[rb][kc] = mfma(ga[ks], vop[kc][ks], ud[rb][kc]);
                     }
                 }
             }
