@@ -47,7 +47,8 @@
 extern "C" {
 #endif
 
-#define PARALLAX_ABI_VERSION 4 /* 4 added parallax_decode_no_alloc */
+#define PARALLAX_ABI_VERSION 5 /* 4 added parallax_decode_no_alloc, 5 the prefill's
+                                  workgroups field */
 
 typedef enum {
     PARALLAX_OK = 0,
@@ -292,6 +293,14 @@ typedef struct {
     float *lse;
     float *rmean;
     float *o_sa;
+    /* Head dim 128 runs a fixed set of persistent workgroups, each taking its
+     * share of the (query block, head block) items in turn, and the shortest
+     * items (about one round of them) as one workgroup each: 0 = one
+     * persistent workgroup per compute unit (the default), n >= 1 = at most
+     * n (for tests and tuning; results do not depend on it).  Head dim 64
+     * runs one workgroup per item and ignores it.  < 0 is
+     * PARALLAX_ERR_INVALID_ARG (added in ABI version 5). */
+    int32_t workgroups;
 } parallax_prefill_args_t;
 
 parallax_status_t parallax_prefill(const parallax_prefill_args_t *args, void *hip_stream);

@@ -30,7 +30,7 @@ PARALLAX_ERR_WORKSPACE = 3
 PARALLAX_ERR_HIP = 4
 PARALLAX_F32 = 0
 PARALLAX_BF16 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 # bytes of the library-owned scratch parallax_decode_no_alloc uses per device
 NO_ALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -68,6 +68,7 @@ class PrefillArgs(ctypes.Structure):
         ("out", _vp), ("out_stride_b", _i64), ("out_stride_s", _i64), ("out_stride_h", _i64),
         ("window", _i32),
         ("lse", _vp), ("rmean", _vp), ("o_sa", _vp),
+        ("workgroups", _i32),
     ]
 
 
@@ -404,12 +405,13 @@ def parallax_qr_projection(x, w_q, w_r, *, num_q_heads, out_dtype=torch.float32,
 
 
 def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, window=0,
-                     stream=None, return_stats=False):
+                     stream=None, return_stats=False, workgroups=0):
     """Causal Parallax prefill.  q, rho bf16 [B, S, Hq, d]; k, v bf16
     [B, S, Hkv, d].  window: 0 for keys 0..i, W >= 1 for keys i-W+1..i.
     Returns out float32 [B, S, Hq, d]; with return_stats, (out, lse, rmean,
     o_sa): what parallax_prefill_backward needs (lse, rmean float32
-    [B, Hq, S]; o_sa float32 like out)."""
+    [B, Hq, S]; o_sa float32 like out).  workgroups: head dim 128's
+    persistent workgroups, 0 for one per compute unit, n >= 1 for at most n."""
     lib = load_library()
     for name, t in (("q", q), ("rho", rho), ("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(-1) != 1:
@@ -430,6 +432,7 @@ def parallax_prefill(q, rho, k, v, *, scale=None, out=None, causal=True, window=
     a.v, a.v_stride_b, a.v_stride_s, a.v_stride_h = _ptr(v), *v.stride()[:3]
     a.out, a.out_stride_b, a.out_stride_s, a.out_stride_h = _ptr(out), *out.stride()[:3]
     a.window = int(window)
+    a.workgroups = int(workgroups)
     if return_stats:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
         rmean = torch.empty_like(lse)

@@ -189,6 +189,8 @@ parallax_status_t check_prefill(const parallax_prefill_args_t *a) {
     if (a->causal != 1)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: only causal = 1 is supported");
     if (a->window < 0) return fail(PARALLAX_ERR_INVALID_ARG, "prefill: window must be >= 0");
+    if (a->workgroups < 0)
+        return fail(PARALLAX_ERR_INVALID_ARG, "prefill: workgroups must be >= 0");
     if (a->head_dim != 64 && a->head_dim != 128)
         return fail(PARALLAX_ERR_UNSUPPORTED, "prefill: head_dim %d (supported: 64, 128)",
                     a->head_dim);
@@ -673,6 +675,7 @@ PLX_EXPORT parallax_status_t parallax_prefill(const parallax_prefill_args_t *a, 
     p.q_sign = a->scale > 0.0f ? 0 : (a->scale < 0.0f ? 1 : 2);
     p.scale_log2 = (float)(a->scale != 0.0f ? fabs((double)a->scale) * 1.4426950408889634 : 1.0);
     p.window = a->window;
+    p.workgroups = a->workgroups;
     p.lse = a->lse;
     p.rmean = a->rmean;
     p.o_sa = a->o_sa;

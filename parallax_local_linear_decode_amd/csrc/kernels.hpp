@@ -73,6 +73,14 @@ struct PrefillParams {
     // 1 negated (scale < 0), 2 zeroed (scale = 0: every logit 0)
     int32_t q_sign;
     int32_t window;  // 0: keys 0..i; W >= 1: keys max(0, i-W+1)..i
+    // head dim 128: at most this many persistent workgroups, each running
+    // its share of the query blocks in turn (0: one per compute unit)
+    int32_t workgroups;
+    // set by the launcher: workgroups 0 .. persist - 1 each run
+    // static_rounds items; the items after those rounds run one per
+    // workgroup (0, 0: every workgroup runs one item)
+    int32_t persist;
+    int32_t static_rounds;
     // optional outputs for a backward pass (each may be null): natural-log
     // softmax denominator and r per row, [B, Hq, S]; o_SA with out's strides
     float *lse;

@@ -185,6 +185,7 @@ def good_prefill(**over):
     (dict(q_stride_s=2052), UNSUPP, "16 bytes"),
     (dict(out_stride_h=130), UNSUPP, "16 bytes"),
     (dict(window=-5), INVALID, "window"),
+    (dict(workgroups=-1), INVALID, "workgroups"),
 ])
 def test_prefill_rejects(lib, over, status, needle):
     a = good_prefill(**over)
@@ -194,13 +195,17 @@ def test_prefill_rejects(lib, over, status, needle):
 
 
 def test_older_structs_are_rejected(lib):
-    """ABI version 2 appended `window` to both argument structs and version 3
-    the three optional statistics outputs to the prefill struct; a caller
-    built against an older header passes a smaller struct_size."""
+    """ABI version 2 appended `window` to both argument structs, version 3
+    the three optional statistics outputs to the prefill struct and version 5
+    its `workgroups`; a caller built against an older header passes a
+    smaller struct_size."""
     old_decode = ctypes.sizeof(plx.DecodeArgs) - 8
     st, _ = ws_size(lib, good_decode(struct_size=old_decode))
     assert st == INVALID and "struct_size" in plx.parallax_last_error()
-    for old_prefill in (ctypes.sizeof(plx.PrefillArgs) - 24, ctypes.sizeof(plx.PrefillArgs) - 32):
+    v5 = ctypes.sizeof(plx.PrefillArgs)
+    assert plx.PrefillArgs.workgroups.offset + 4 <= v5 and plx.PrefillArgs.o_sa.offset + 8 <= v5
+    for old_prefill in (plx.PrefillArgs.workgroups.offset, plx.PrefillArgs.lse.offset,
+                        plx.PrefillArgs.lse.offset - 8):
         a = good_prefill(struct_size=old_prefill)
         assert lib.parallax_prefill(ctypes.byref(a), None) == INVALID
         assert "struct_size" in plx.parallax_last_error()

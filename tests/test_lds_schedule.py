@@ -8,7 +8,8 @@ which LDS buffer every wave reads and writes between two barriers (an
 "epoch"), which tile each buffer holds, and what the register stages of the
 global loads hold when they are stored; then checks, over many grid shapes
 (ragged tile counts, windows that start the loop late, pairs whose row
-ranges differ):
+ranges differ, and for the prefill the work lists of its persistent
+workgroups, whose items follow each other in one stream of positions):
 
   * every role passes the same number of barriers;
   * no buffer is written in an epoch in which another wave may read or
@@ -17,7 +18,8 @@ ranges differ):
   * every register stage stored to LDS holds the tile the store expects.
 
 A planted change (the dq kernel's K tiles double- instead of triple-
-buffered, or the forward's register stages swapped) must be caught.  The
+buffered, the forward's register stages swapped, or its items shorter than
+the three positions its loads run ahead) must be caught.  The
 forward this kernel replaced (four waves, each doing both roles on its own
 rows), which returned wrong results on some launches, is modelled too: the
 model locates its race (K tile 2 stored over tile 0 in the epoch in which
@@ -97,56 +99,149 @@ def check(trace):
 
 # ------------------------------------------------------------------ forward ---
 
-def forward_trace(t_first, ntiles, pairs, swap_stages=False):
-    """prefill_kernel: `pairs` = [(pair_lo, pair_tiles)] per score/value pair.
-    Shared K and V tiles double-buffered (buffer t & 1); per-pair P operands
-    and rescale factors double-buffered.  advance(t): K tile t+1 into K[(t+1)
-    & 1] and V tile t into V[t & 1] from the register stages, then the loads
-    of K tile t+3 and V tile t+2, then the barrier."""
-    tr = Trace()
-    roles = []
-    for p, (lo, hi) in enumerate(pairs):
-        roles.append(("score", p, lo, hi, tr.wave(f"score{p}")))
-        roles.append(("value", p, lo, hi, tr.wave(f"value{p}")))
+def forward_items(S, G, W, units, P, wg, min_len=4, persistent=True):
+    """The work list of workgroup `wg` (prefill_kernel) when P persistent
+    workgroups run: items k = (query block, unit), longest causal rows
+    first.  With R = nitems // P - 1 >= 1 rounds, workgroup wg < P takes one
+    item per round, in workgroup order in even rounds and in reverse order of
+    8-workgroup groups in odd ones; workgroup wg >= P takes item R P + wg - P.
+    (R < 1: every workgroup one item.)  Each item: (tiles t0, t1, stream
+    positions it spans -- even, at least min_len, the last four being its
+    tail --, [(pair_lo, pair_hi)] of the four pairs).  Not persistent (head
+    dim 64): one item per workgroup."""
+    pph = 4 // G
+    qb_rows = 32 * pph
+    nqb = -(-S // qb_rows)
+    nitems = nqb * units
+    R = nitems // P - 1 if persistent else 0
+    if R < 1:
+        P, R = 0, 0
 
-    def advance(w, t, P):
+    def item_id(i):
+        if wg >= P:
+            return R * P + wg - P
+        off = wg
+        if i & 1:
+            off = P - 8 - (wg & ~7) + (wg & 7) if P % 8 == 0 else P - 1 - wg
+        return i * P + off
+
+    n_mine = R if wg < P else 1
+    items = []
+    for i in range(n_mine):
+        qb = nqb - 1 - item_id(i) // units
+        t1 = -(-min(S, (qb + 1) * qb_rows) // 32)
+        t0 = max(0, qb * qb_rows - W + 1) // 32 if W > 0 else 0
+        n = max(t1 - t0, min_len)
+        n += n & 1
+        pairs = []
+        for p in range(4):
+            r0 = qb * qb_rows + (p % pph) * 32
+            hi = min(t1, -(-min(S, r0 + 32) // 32))
+            lo = max(0, r0 - W + 1) // 32 if W > 0 else 0
+            pairs.append((lo, hi))
+        items.append((t0, t1, n, pairs))
+    return items
+
+
+def forward_grid(S, G, units, P):
+    """Workgroups the launcher starts for P persistent ones (P <= items)."""
+    nitems = -(-S // (32 * (4 // G))) * units
+    R = nitems // P - 1
+    return P + nitems - R * P if R >= 1 else nitems
+
+
+def forward_trace(items, swap_stages=False, mfin_slots=2):
+    """prefill_kernel over one workgroup's work list: an outer loop over the
+    items, an inner loop over an item's positions t0 .. t0 + n - 1, all of
+    them one stream of positions (so buffers go by the stream position's
+    parity; items span an even number).  K and V tiles double-buffered;
+    per-pair P operands and rescale factors double-buffered; the final
+    reference max handed to the value wave per item (buffer = item parity).
+    advance(t): K tile of position +1 into K[(j+1) & 1] and V tile of the
+    position into V[j & 1] from the register stages, then the loads for
+    positions +3 and +2, then the barrier.  Loads past an item's positions
+    go to the next item's (its t0 + the overshoot), past the last item to
+    the last position's tile again -- exactly as the kernel maps them, so a
+    register stage stored to LDS is checked against the (item, tile) the
+    position holds."""
+    tr = Trace()
+    pos = [(i, t) for i, (t0, t1, n, prs) in enumerate(items) for t in range(t0, t0 + n)]
+    npos = len(pos)
+
+    def fetched(j, d):  # (item, tile) the kernel loads at position j for position j + d
+        i, t = pos[min(j, npos - 1)]
+        t0, t1, n, prs = items[i]
+        tt = t + d if j < npos else t0 + n + d  # past the end: the final advance
+        if tt < t0 + n:
+            return i, tt
+        if i + 1 < len(items):
+            return i + 1, items[i + 1][0] + tt - (t0 + n)
+        return i, t0 + n - 1
+
+    def want(j):
+        return pos[j] if j < npos else None
+
+    roles = []
+    for p in range(4):
+        roles.append(("score", p, tr.wave(f"score{p}")))
+        roles.append(("value", p, tr.wave(f"value{p}")))
+
+    def store_checked(w, stage, buf, j):
+        if j < npos:
+            w.store(stage, buf, want(j))
+        else:
+            w.write(buf, ("past", j))
+
+    def advance(w, j, P):
         Q = 1 - P
         ks, vs = (("k", Q), ("v", P)) if not swap_stages else (("k", P), ("v", Q))
-        w.store(ks, ("K", (t + 1) & 1), t + 1)
-        w.store(vs, ("V", t & 1), t)
-        w.load(("k", Q), t + 3)
-        w.load(("v", P), t + 2)
+        store_checked(w, ks, ("K", Q), j + 1)
+        store_checked(w, vs, ("V", P), j)
+        w.load(("k", Q), fetched(j, 3))
+        w.load(("v", P), fetched(j, 2))
         w.barrier()
 
-    for kind, p, lo, hi, w in roles:
-        # prologue (every thread of both roles): K tile t_first to LDS, K
-        # tiles t_first + 1, + 2 and V tiles t_first, + 1 in flight
-        w.load(("k", 0), t_first)
-        w.store(("k", 0), ("K", 0), t_first)
-        w.load(("k", 1), t_first + 1)
-        w.load(("v", 0), t_first)
-        w.load(("k", 0), t_first + 2)
-        w.load(("v", 1), t_first + 1)
+    for kind, p, w in roles:
+        # prologue: K tile of position 0 to LDS; K 1, 2 and V 0, 1 in flight
+        w.load(("k", 0), fetched(0, 0))
+        w.store(("k", 0), ("K", 0), want(0))
+        w.load(("k", 1), fetched(0, 1))
+        w.load(("v", 0), fetched(0, 0))
+        w.load(("k", 0), fetched(0, 2))
+        w.load(("v", 1), fetched(0, 1))
         w.barrier()
-        for t in range(t_first, ntiles + 1, 2):
-            for tt, P in ((t, 0), (t + 1, 1)):
+        j = 0
+        for i, (t0, t1, n, prs) in enumerate(items):
+            assert n % 2 == 0
+            for t in range(t0, t0 + n):
+                P = j & 1
                 if kind == "score":
-                    if lo <= tt < hi:
-                        w.read(("K", tt & 1), tt)
-                        w.write(("P", p, tt & 1), tt)
+                    lo, hi = prs[p]
+                    if lo <= t < hi:
+                        w.read(("K", P), pos[j])
+                        w.write(("P", p, P), pos[j])
+                    if t == t0 + n - 1:
+                        w.write(("MFIN", p, i % mfin_slots), i)
                 else:
-                    u = tt - 1
-                    if lo <= u < hi:
-                        w.read(("P", p, u & 1), u)
-                        w.read(("V", u & 1), u)
-                advance(w, tt, P)
-        # the statistics instantiation: the score wave hands its final
-        # reference max to the value wave across one more barrier
-        if kind == "score":
-            w.write(("MFIN", p), "final")
-        w.barrier()
+                    if j > 0:
+                        pi, pt = pos[j - 1]
+                        lo, hi = items[pi][3][p]
+                        if lo <= pt < hi:
+                            w.read(("P", p, (j - 1) & 1), pos[j - 1])
+                            w.read(("V", (j - 1) & 1), pos[j - 1])
+                        if pi != i:  # the previous item's outputs
+                            w.read(("MFIN", p, pi % mfin_slots), pi)
+                advance(w, j, P)
+                j += 1
+        # the position after the last: the value waves' last tile and outputs
         if kind == "value":
-            w.read(("MFIN", p), "final")
+            pi, pt = pos[-1]
+            lo, hi = items[pi][3][p]
+            if lo <= pt < hi:
+                w.read(("P", p, (npos - 1) & 1), pos[-1])
+                w.read(("V", (npos - 1) & 1), pos[-1])
+            w.read(("MFIN", p, pi % mfin_slots), pi)
+        advance(w, npos, 0)
     return tr
 
 
@@ -272,9 +367,29 @@ def replaced_forward_trace(ntiles, wave_tiles):
 # ------------------------------------------------------------------- tests ---
 
 def forward_cases():
-    """(t_first, ntiles, pair ranges) as the kernels derive them: full causal
-    (t_first = 0, pair_lo = 0, pair_tiles = the pair's last row tile + 1) and
-    windows (t_first even, each pair_lo >= t_first)."""
+    """Work lists as the kernel derives them: ragged sequence lengths around
+    the tile and query-block edges, GQA groups 1, 2 and 4, full causal and
+    local windows, and persistent workgroup counts from one to more than a
+    round, multiples of 8 or not; the first, a middle and the last
+    persistent workgroup and the first and last one-item workgroup."""
+    seen = set()
+    for S in (1, 31, 33, 64, 100, 257, 600):
+        for G in (1, 2, 4):
+            for W in (0, 40, 300):
+                for units, P in ((1, 1), (3, 1), (3, 2), (2, 3), (5, 8), (4, 16)):
+                    # the launcher never runs more persistent workgroups than items
+                    P = min(P, -(-S // (32 * (4 // G))) * units)
+                    n = forward_grid(S, G, units, P)
+                    for wg in sorted({0, P // 2, P - 1, P, n - 1} & set(range(n))):
+                        if (S, G, W, units, P, wg) not in seen:
+                            seen.add((S, G, W, units, P, wg))
+                            yield S, G, W, units, P, wg
+
+
+def dq_cases():
+    """(t_first, ntiles, pair ranges) as the dq kernel derives them: full
+    causal (t_first = 0, pair_lo = 0, pair_tiles = the pair's last row tile
+    + 1) and windows (t_first even, each pair_lo >= t_first)."""
     for ntiles in range(1, 11):
         for rows_per_pair in (1, 2):  # GQA groups give pairs of 32 or 64... rows per head
             pts = [min(ntiles, (i + 1) * rows_per_pair) for i in range(4)]
@@ -285,12 +400,39 @@ def forward_cases():
                 yield t_first, ntiles, pairs
 
 
-@pytest.mark.parametrize("t_first,ntiles,pairs", list(forward_cases()))
-def test_forward_schedule(t_first, ntiles, pairs):
-    assert check(forward_trace(t_first, ntiles, pairs)) == []
+@pytest.mark.parametrize("S,G,W,units,P,wg", list(forward_cases()))
+def test_forward_schedule(S, G, W, units, P, wg):
+    items = forward_items(S, G, W, units, P, wg)
+    assert check(forward_trace(items)) == []
 
 
-@pytest.mark.parametrize("t_first,ntiles,pairs", list(forward_cases()))
+def test_forward_work_lists_cover_every_item_once():
+    """The workgroups' lists partition the items, and the odd-round order
+    keeps item % 8 == workgroup % 8 when P is a multiple of 8."""
+    for S, G, W, units in ((600, 2, 0, 8), (257, 4, 40, 3), (64, 1, 0, 16), (2048, 2, 0, 8)):
+        qb_rows = 32 * (4 // G)
+        nqb = -(-S // qb_rows)
+        nitems = nqb * units
+        for P in (1, 3, 8, 16, 24):
+            P = min(P, nitems)
+            seen = []
+            for wg in range(forward_grid(S, G, units, P)):
+                items = forward_items(S, G, W, units, P, wg)
+                R = nitems // P - 1
+                for i in range(len(items)):
+                    if R >= 1 and wg < P:
+                        off = (P - 8 - (wg & ~7) + (wg & 7) if P % 8 == 0 else P - 1 - wg) \
+                            if i & 1 else wg
+                        k = i * P + off
+                    else:
+                        k = R * P + wg - P if R >= 1 else wg
+                    if P % 8 == 0 and R >= 1:
+                        assert k % 8 == wg % 8
+                    seen.append(k)
+            assert sorted(seen) == list(range(nitems))
+
+
+@pytest.mark.parametrize("t_first,ntiles,pairs", list(dq_cases()))
 def test_dq_schedule(t_first, ntiles, pairs):
     assert check(dq_trace(t_first, ntiles, pairs)) == []
 
@@ -337,8 +479,19 @@ def test_planted_double_buffered_dq_k_tiles_are_caught():
 
 
 def test_planted_swapped_forward_stages_are_caught():
-    bad = check(forward_trace(0, 6, [(0, 6)] * 4, swap_stages=True))
+    items = forward_items(257, 2, 0, 3, 2, 0)
+    bad = check(forward_trace(items, swap_stages=True))
     assert any(b[0] == "register stage" for b in bad)
+
+
+def test_planted_short_items_are_caught():
+    """The loads run three positions ahead and the kernel maps a position past
+    an item's end into the next item only, so every item spans at least four
+    positions (two would let a load for the item after next fetch a tile of
+    the next item instead)."""
+    bad = check(forward_trace(forward_items(100, 4, 0, 4, 1, 0, min_len=2)))
+    assert any(b[0] == "register stage" for b in bad)
+    assert check(forward_trace(forward_items(100, 4, 0, 4, 1, 0, min_len=4))) == []
 
 
 def test_checker_sees_a_write_beside_a_read():

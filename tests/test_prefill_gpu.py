@@ -153,3 +153,54 @@ def test_strided_views_equal_contiguous(gpu):
     torch.cuda.synchronize()
     assert torch.equal(out, want)
     assert torch.isnan(wide[..., :d]).all()
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,window", [
+    (33, 2, 2, 0), (257, 4, 2, 0), (257, 16, 2, 0), (600, 2, 1, 0), (600, 4, 1, 100),
+    (100, 8, 2, 40), (500, 16, 1, 0)])
+def test_workgroup_counts_agree(gpu, S, Hq, Hkv, window):
+    """Head dim 128 runs a fixed set of persistent workgroups, each taking its
+    share of the (query block, head block) items in turn (the next item's
+    tiles and q / rho loaded during the current one's last positions), and
+    the shortest items one per workgroup.  One persistent workgroup for
+    almost every item, counts that are and are not multiples of 8 and the
+    default give the same bits (outputs and the backward's statistics); every
+    row of the one-workgroup run matches the oracle."""
+    q, rho, k, v, scale = prefill_inputs(2, S, Hq, Hkv, 128, seed=S + Hq + window)
+    ref = oracle.prefill(*host(q, rho, k, v), scale, window=window)
+    dev = [t.to(gpu) for t in (q, rho, k, v)]
+    runs = {}
+    for wgs in (1, 3, 8, 16, 0):
+        plain = plx.parallax_prefill(*dev, scale=scale, window=window, workgroups=wgs)
+        stats = plx.parallax_prefill(*dev, scale=scale, window=window, workgroups=wgs,
+                                     return_stats=True)
+        torch.cuda.synchronize()
+        assert torch.equal(plain, stats[0]), f"workgroups={wgs}: stats build differs"
+        runs[wgs] = stats
+    for wgs, got in runs.items():
+        for name, a, b in zip(("out", "lse", "rmean", "o_sa"), got, runs[0]):
+            assert torch.equal(a, b), f"workgroups={wgs}: {name} differs from the default"
+    assert_parity(runs[1][0], ref, TAU_BF16, RMS_PREFILL, what=f"one workgroup S={S} W={window}")
+
+
+def test_workgroups_ignored_at_head_dim_64(gpu):
+    q, rho, k, v, scale = (t.to(gpu) if isinstance(t, torch.Tensor) else t
+                           for t in prefill_inputs(2, 300, 8, 2, 64, seed=11))
+    a = plx.parallax_prefill(q, rho, k, v, scale=scale, workgroups=1)
+    b = plx.parallax_prefill(q, rho, k, v, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_full_size_few_workgroups_agree(gpu):
+    """Batch 4 x 8192 (16/8 heads): the default one workgroup per CU, and 40
+    workgroups (about a hundred items each), give identical bits, window or
+    not."""
+    B, S, Hq, Hkv = 4, 8192, 16, 8
+    q, rho, k, v, scale = prefill_inputs(B, S, Hq, Hkv, 128, seed=13, device=gpu)
+    for window in (0, 1024):
+        a = plx.parallax_prefill(q, rho, k, v, scale=scale, window=window)
+        b = plx.parallax_prefill(q, rho, k, v, scale=scale, window=window, workgroups=40)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), f"window {window}"
