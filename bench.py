@@ -94,9 +94,22 @@ def decode_bytes(B, Hq, Hkv, d, lens, kv_elem=2):
     return sum(lens) * Hkv * d * 2 * kv_elem + B * Hq * d * 4 * 3
 
 
+# Least wall time of warm-up work before a timed region: an idle GPU needs
+# on the order of 0.1 s of load to reach its working clock, and a short
+# workload's W warm-up launches alone can end before that.
+MIN_WARMUP_SECONDS = 0.25
+
+
 def time_launches(torch, launch, n_bufs, steps, warmup):
     for i in range(warmup):
         launch(i % n_bufs)
+    torch.cuda.synchronize()
+    t0, i = time.perf_counter(), warmup
+    while warmup > 0 and time.perf_counter() - t0 < MIN_WARMUP_SECONDS:
+        launch(i % n_bufs)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
