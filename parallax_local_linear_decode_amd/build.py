@@ -32,6 +32,11 @@ HIPCC_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# The projection's large-tile GEMM holds 256 fp32 accumulators per lane, which
+# only fit in the accumulation registers, and no VALU code touches them, so
+# its file keeps the compiler's default register form.
+VGPR_FORM = ("-mllvm", "-amdgpu-mfma-vgpr-form=1")
+AGPR_FORM = ("proj.hip",)
 
 
 def _hipcc():
@@ -48,7 +53,11 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        flags = HIPCC_FLAGS
+        if src in AGPR_FORM:
+            i = HIPCC_FLAGS.index(VGPR_FORM[1])
+            flags = HIPCC_FLAGS[:i - 1] + HIPCC_FLAGS[i + 1:]
+        cmd = [hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

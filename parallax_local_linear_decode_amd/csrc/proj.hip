@@ -322,18 +322,249 @@ hipError_t launch_tiled(const ProjParams &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ big tiles ---
+// The largest prefill sizes (N a multiple of 256 and enough 256 x 256 tiles
+// to fill the CUs): 256 x 256 output tiles on four waves of 128 x 128 each
+// (8 x 8 16x16x32 MFMA tiles, 256 fp32 accumulators per lane, which only fit
+// in the accumulation registers).  Per k a wave reads (128 + 128) * 2 bytes
+// from LDS for 2 * 128 * 128 flops, half the LDS traffic per flop of the
+// eight-wave tile.
+//
+// K runs in steps of 32 through four LDS stages of 32 KB (the weight tile,
+// then the token tile, 64-byte rows), filled by global->LDS buffer loads (16
+// bytes per lane, no staging registers, no LDS store instructions) issued
+// three steps ahead of their use.  A load instruction writes 1 KB = sixteen
+// 64-byte rows in lane order, so rows cannot be padded; the four 16-byte
+// pieces of row R are stored in the order piece ^ swz(R) instead, which puts
+// the rows one operand read touches on distinct banks.  One barrier per
+// step: it publishes step s + 1's stage (every wave has waited for its own
+// loads of it) and frees step s's stage (every wave has its operands of step
+// s in registers), which then takes step s + 4; the operand reads of step
+// s + 1 run under the MFMAs of step s.
+constexpr int kBigT = 256;                    // tile rows and tokens
+constexpr int kBigK = 32;                     // k per stage
+constexpr int kBigRow = kBigK * 2;            // 64-byte rows
+constexpr int kBigOp = kBigT * kBigRow;       // one operand of one stage
+constexpr int kBigStage = 2 * kBigOp;         // weights then tokens
+
+// s_waitcnt immediates: vector memory count (bits 3:0 and 15:14) at most 16,
+// 8 or 0 loads pending, LDS count (bits 11:8) 0, export count (6:4) free
+constexpr int kWait16 = 0x4070, kWait8 = 0x0078, kWait0 = 0x0070;
+
+// The workgroup barrier of the big-tile kernel, after the caller's explicit
+// wait.  __syncthreads() would add a release fence, for which the compiler
+// waits for every pending global->LDS load, including the ones issued for
+// later steps; the empty asm statements keep the compiler from moving
+// memory accesses across the barrier instead.
+__device__ __forceinline__ void big_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Rows r and r + 1 share a 128-byte bank window; pieces are permuted by
+// (r / 2) % 4, so rows 0..7 of one read land on distinct 16-byte bank groups
+// (the LDS bank-conflict counter reads zero for this kernel).
+__device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 3; }
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, int n_tb) {
+    __shared__ __attribute__((aligned(1024))) unsigned char st0[kBigStage];
+    __shared__ __attribute__((aligned(1024))) unsigned char st1[kBigStage];
+    __shared__ __attribute__((aligned(1024))) unsigned char st2[kBigStage];
+    __shared__ __attribute__((aligned(1024))) unsigned char st3[kBigStage];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15;
+    const int g = lane >> 4;
+
+    // Tile order: workgroups are dealt to the eight XCDs in turn, so when
+    // the tile count divides by 8, XCD x gets the x-th eighth of the order;
+    // the order walks groups of four token blocks, row block by row block,
+    // so the 32 workgroups an XCD runs at a time cover 4 token blocks x 8
+    // row blocks and share those tiles in its L2.
+    const int nt = n_rb * n_tb;
+    const int bid = blockIdx.x;
+    const int lid = nt % 8 == 0 ? (bid % 8) * (nt / 8) + bid / 8 : bid;
+    const int grp = lid / (4 * n_rb);
+    const int gsz = min(4, n_tb - 4 * grp);
+    const int in = lid - grp * 4 * n_rb;
+    const int tb = 4 * grp + in % gsz, rb = in / gsz;
+    const int row0 = rb * kBigT, t0 = tb * kBigT;
+    const int T = p.tokens;
+    const bool is_r = row0 >= p.n;  // N is a multiple of 256: a tile never straddles
+    const uint16_t *wbase = (is_r ? p.w_r : p.w_q) + (int64_t)(row0 - (is_r ? p.n : 0)) * p.w_sn;
+    const uint16_t *xbase = p.x + (int64_t)t0 * p.x_st;
+
+    // Buffer resources over the tile's weight rows and token rows: a load
+    // past the last token row returns zeros (those outputs are not stored).
+    // Byte offsets fit 32 bits: the launcher checks 256 * stride * 2 < 2^31.
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)wbase, (short)0, (int)(((kBigT - 1) * p.w_sn + p.model_dim) * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)xbase, (short)0, (int)(((min(T - t0, kBigT) - 1) * (int64_t)p.x_st + p.model_dim) * 2),
+        0x00020000);
+    // Loads: wave w fills rows 64 w + 16 j + lane / 4 (j = 0..3) of both
+    // operands; lane i lands at byte 16 i of its instruction's 1 KB, i.e.
+    // physical piece i % 4 of its row, which holds logical piece
+    // (i % 4) ^ swz(row) (row % 16 == lane / 4 for every j).
+    const int wsn = (int)p.w_sn, xst = (int)p.x_st;
+    const int lr = lane >> 2, lp = (lane & 3) ^ big_swz(lane >> 2);
+    const int wv = (lr * wsn + 8 * lp) * 2, xv = (lr * xst + 8 * lp) * 2;
+    auto dma = [&](unsigned char *stage, int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 64 * wave + 16 * j;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wres, (__attribute__((address_space(3))) void *)(stage + r * kBigRow), 16, wv,
+                (r * wsn + k0) * 2, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xres, (__attribute__((address_space(3))) void *)(stage + kBigOp + r * kBigRow), 16, xv,
+                (r * xst + k0) * 2, 0, 0);
+        }
+    };
+
+    // Operand reads: wave (wr, wc) = (wave % 2, wave / 2) owns weight rows
+    // 128 wr .. + 127 and tokens 128 wc .. + 127 of the tile; MFMA tile i
+    // (j) is rows (tokens) 16 i + c, k-slots 8 g .. 8 g + 7 = logical piece
+    // g.  Every such row has row % 16 == c, so the swizzle is the lane's own.
+    const int wr = wave & 1, wc = wave >> 1;
+    const int po = 16 * (g ^ big_swz(c));
+    const int aoff = (128 * wr + c) * kBigRow + po, boff = kBigOp + (128 * wc + c) * kBigRow + po;
+    struct Ops {
+        bf16x8_t a[8], b[8];
+    };
+    auto read_ops = [&](const unsigned char *stage, Ops &o) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            o.a[n] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                      stage + aoff + 16 * n * kBigRow));
+            o.b[n] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                                                      stage + boff + 16 * n * kBigRow));
+        }
+    };
+
+    f32x4_t acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto mfmas = [&](const Ops &o) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+    };
+
+    // Step s: `cur` holds operands of step s; `stage` is step s's stage,
+    // `next` step s + 1's.  WAIT is the pending-load bound that leaves step
+    // s + 1's loads landed (the later steps' loads may still run) and this
+    // wave's operand reads of step s back.
+    // Scheduling barriers pin the order (the compiler otherwise moves each
+    // read next to its first use and waits for it there, and sinks MFMAs
+    // below the barrier).
+    const int nsteps = p.model_dim / kBigK;  // a multiple of 8 (model_dim % 256 == 0)
+    Ops oa, ob;
+    auto step = [&](int s, unsigned char *stage, const unsigned char *next, Ops &cur, Ops &nxt,
+                    auto wait, auto more_loads, auto more_reads) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(more_reads)::value) {
+            __builtin_amdgcn_s_waitcnt(decltype(wait)::value);
+            big_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (decltype(more_loads)::value) dma(stage, (s + 4) * kBigK);
+            read_ops(next, nxt);
+        }
+        mfmas(cur);
+        // One wave per SIMD: the loads and reads are spread over the MFMAs
+        // (one load, two reads, eight MFMAs), so the matrix core is not idle
+        // while the wave issues them.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (decltype(more_loads)::value) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            if constexpr (decltype(more_reads)::value) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+    };
+    using W16 = std::integral_constant<int, kWait16>;
+    using W8 = std::integral_constant<int, kWait8>;
+    using W0 = std::integral_constant<int, kWait0>;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    dma(st0, 0);
+    dma(st1, kBigK);
+    dma(st2, 2 * kBigK);
+    dma(st3, 3 * kBigK);
+    __builtin_amdgcn_s_waitcnt(kWait16 + 8);  // step 0's loads landed (24 may run)
+    big_barrier();
+    read_ops(st0, oa);
+    for (int s = 0; s < nsteps - 4; s += 4) {
+        step(s, st0, st1, oa, ob, W16{}, T_{}, T_{});
+        step(s + 1, st1, st2, ob, oa, W16{}, T_{}, T_{});
+        step(s + 2, st2, st3, oa, ob, W16{}, T_{}, T_{});
+        step(s + 3, st3, st0, ob, oa, W16{}, T_{}, T_{});
+    }
+    step(nsteps - 4, st0, st1, oa, ob, W16{}, F_{}, T_{});
+    step(nsteps - 3, st1, st2, ob, oa, W8{}, F_{}, T_{});
+    step(nsteps - 2, st2, st3, oa, ob, W0{}, F_{}, T_{});
+    step(nsteps - 1, st3, st0, ob, oa, W0{}, F_{}, F_{});
+
+    // acc[i][j]: lane (c, g) holds stacked rows row0 + 128 wr + 16 i + 4 g +
+    // (0..3) of token t0 + 128 wc + 16 j + c
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int f = row0 - (is_r ? p.n : 0) + 128 * wr + 16 * i + 4 * g;
+        const int h = f / p.head_dim, e = f % p.head_dim;
+        const int64_t hoff = (int64_t)h * (is_r ? p.r_sh : p.q_sh) + e;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int t = t0 + 128 * wc + 16 * j + c;
+            if (t >= T) continue;
+            const int64_t off = (int64_t)t * (is_r ? p.r_st : p.q_st) + hoff;
+            const f32x4_t v = acc[i][j];
+            if constexpr (BF16OUT) {
+                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+                const bf16x4_t b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(is_r ? p.rho : p.q) + off) =
+                    __builtin_bit_cast(uint2, b);
+            } else {
+                *reinterpret_cast<float4 *>(static_cast<float *>(is_r ? p.rho : p.q) + off) =
+                    float4{v[0], v[1], v[2], v[3]};
+            }
+        }
+    }
+}
+
+hipError_t launch_big(const ProjParams &p, hipStream_t stream) {
+    const int n_rb = 2 * p.n / kBigT, n_tb = (p.tokens + kBigT - 1) / kBigT;
+    const dim3 grid((unsigned)(n_rb * n_tb));
+    if (p.out_bf16)
+        hipLaunchKernelGGL((proj_big_kernel<true>), grid, dim3(256), 0, stream, p, n_rb, n_tb);
+    else
+        hipLaunchKernelGGL((proj_big_kernel<false>), grid, dim3(256), 0, stream, p, n_rb, n_tb);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Up to 16 tokens (decode): token blocks of 16 and the weight-streaming
 // kernel; up to 64: blocks of 64; up to 128: blocks of 64 with two row tiles
-// per workgroup (one row tile doubled the weight re-reads there); beyond: the LDS-tiled GEMM, with 256 x 256
-// tiles when 2N is a multiple of 256 and that grid fills the CUs, else with
+// per workgroup (one row tile doubled the weight re-reads there); beyond: an
+// LDS-tiled GEMM.  256 x 256 tiles when that grid fills the CUs: the
+// four-wave kernel when N is a multiple of 256 (and its 32-bit offsets
+// reach), else the eight-wave one when 2N is a multiple of 256; otherwise
 // 128 x 128 tiles (2N is always a multiple of 128: head_dim is 64 or 128).
 hipError_t launch_qr_projection(const ProjParams &p, hipStream_t stream) {
     if (p.tokens <= 16) return launch_nt<1, 1>(p, stream);
     if (p.tokens <= 64) return launch_nt<1, 4>(p, stream);
     if (p.tokens <= 128) return launch_nt<2, 4>(p, stream);
     const int64_t big = (int64_t)(2 * p.n / Tile256::kMT) * ((p.tokens + Tile256::kNT - 1) / Tile256::kNT);
+    // the large-tile kernel's 32-bit buffer offsets span 256 rows of either operand
+    const bool offsets32 = (int64_t)kBigT * p.w_sn * 2 + 2 * p.model_dim < (1LL << 31) &&
+                           (int64_t)kBigT * p.x_st * 2 + 2 * p.model_dim < (1LL << 31);
+    if (p.n % kBigT == 0 && big >= kCUs && offsets32) return launch_big(p, stream);
     if ((2 * p.n) % Tile256::kMT == 0 && big >= kCUs) return launch_tiled<Tile256>(p, stream);
     return launch_tiled<Tile128>(p, stream);
 }

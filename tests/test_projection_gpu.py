@@ -42,13 +42,16 @@ def test_every_element(gpu, T, D, Hq, d, out_dtype):
 
 
 @pytest.mark.parametrize("T,D,Hq,d", [(4096, 2048, 16, 128), (4100, 1024, 16, 128),
-                                      (8200, 512, 8, 128), (4100, 256, 1, 64)])
+                                      (8200, 512, 8, 128), (32900, 256, 2, 128),
+                                      (22000, 256, 3, 128), (4100, 256, 1, 64)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_prefill_token_counts(gpu, T, D, Hq, d, out_dtype):
-    """Token counts of prefill (the LDS-tiled GEMM: 256 x 256 tiles where 2N
-    is a multiple of 256 and the grid fills the device, 128 x 128 tiles for
-    Hq = 1, d = 64; ragged last token tiles): sampled rows against the oracle,
-    the first and last tiles and rows across tile edges."""
+    """Token counts of prefill, the LDS-tiled GEMMs with ragged last token
+    tiles: the four-wave 256 x 256 kernel (N a multiple of 256; the 32900-token
+    grid of 258 tiles is not a multiple of eight, so its tiles keep launch
+    order), the eight-wave 256 x 256 kernel (N = 384) and 128 x 128 tiles
+    (Hq = 1, d = 64).  Sampled rows against the oracle: the first and last
+    tiles and rows across tile edges."""
     x, w_q, w_r = weights(T, D, Hq * d, T + D + Hq, gpu)
     q, rho = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=Hq, out_dtype=out_dtype)
     torch.cuda.synchronize()
@@ -73,6 +76,22 @@ def test_prefill_token_counts_into_strided_views(gpu):
     torch.cuda.synchronize()
     assert torch.equal(q, qc) and torch.equal(rho, rc)
     assert not torch.isnan(buf.float()).any()
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_prefill_token_counts_strided_x(gpu, out_dtype):
+    """x as a column slice of a wider buffer (row stride 1536, offset 256):
+    the four-wave kernel's buffer bounds follow the stride; equal to the
+    contiguous copy's result bit for bit."""
+    T, D, Hq, d = 4100, 1024, 16, 128
+    x, w_q, w_r = weights(T, D, Hq * d, 77, gpu)
+    wide = torch.full((T, 1536), float("nan"), dtype=torch.bfloat16, device=gpu)
+    wide[:, 256:256 + D] = x
+    xs = wide[:, 256:256 + D]
+    q, rho = plx.parallax_qr_projection(xs, w_q, w_r, num_q_heads=Hq, out_dtype=out_dtype)
+    qc, rc = plx.parallax_qr_projection(x, w_q, w_r, num_q_heads=Hq, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(q, qc) and torch.equal(rho, rc)
 
 
 def test_zero_probe_weights_give_zero_rho(gpu):
