@@ -346,6 +346,7 @@ constexpr int kBigK = 32;                     // k per stage
 constexpr int kBigRow = kBigK * 2;            // 64-byte rows
 constexpr int kBigOp = kBigT * kBigRow;       // one operand of one stage
 constexpr int kBigStage = 2 * kBigOp;         // weights then tokens
+static_assert(4 * kBigStage <= 160 * 1024, "four stages fit the 160 KB of LDS of a gfx950 CU");
 
 // s_waitcnt immediates: vector memory count (bits 3:0 and 15:14) at most 16,
 // 8 or 0 loads pending, LDS count (bits 11:8) 0, export count (6:4) free
