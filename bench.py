@@ -12,7 +12,8 @@ parallax_decode call over the whole batch, timed exactly --steps times after
 --warmup untimed steps.  The same line carries the other workloads as
 sub-records: decode at batch 8 x 4096, paged decode (256 sequences, ctx
 U[128, 32768], 16-token pages), causal prefill (batch 4 x 8192) and its
-backward pass, each parity-gated and with its oracle baseline.
+backward pass, and the q / rho projection at 32768 tokens, each
+parity-gated and with its oracle baseline.
 
 The KV cache is resident in HBM before timing starts.  To keep the 256 MB
 last-level cache from serving it, caches below 1 GiB are cloned R times (R x
@@ -401,17 +402,20 @@ def run_qr_proj(args, torch, plx):
     gate(rho[rows].reshape(len(rows), -1).double().cpu().numpy(), rr, tau, 1e-2)
     cpu = None
     if args.cpu_baseline:
-        hx, hq_, hr_ = host_array(x), host_array(ws[0][0]), host_array(ws[0][1])
+        Ts = min(T, 1024)  # a bounded sample of token rows at prefill sizes
+        hx, hq_, hr_ = host_array(x[:Ts]), host_array(ws[0][0]), host_array(ws[0][1])
         t0 = time.perf_counter()
         reps = 0
         while time.perf_counter() - t0 < 2.0:
             oracle.qr_projection(hx, hq_, hr_)
             reps += 1
         per_cpu = (time.perf_counter() - t0) / reps
-        cpu = {"value": 2 * T * 2 * N * D / per_cpu / 1e12, "unit": "TFLOP/s",
+        cpu = {"value": 2 * Ts * 2 * N * D / per_cpu / 1e12, "unit": "TFLOP/s",
                "cores": oracle.default_threads(), "kind": "oracle",
-               "seconds_per_step": per_cpu,
-               "sample": f"the full workload, {reps} repetition(s), numpy fp64 matmul"}
+               "seconds_per_step": per_cpu * T / Ts,
+               "sample": (f"the full workload, {reps} repetition(s)" if Ts == T else
+                          f"the first {Ts} of {T} token rows, {reps} repetition(s), scaled by "
+                          f"{T / Ts:g} for seconds_per_step") + ", numpy fp64 matmul"}
     # pre-marshalled C-ABI calls: the host loop must not be the bottleneck
     import ctypes
     lib = plx.load_library()
@@ -686,6 +690,8 @@ def run_suite(args, torch, plx):
     sub.steps, sub.warmup = max(args.steps, 20), max(args.warmup, 3)
     recs["prefill"] = run_prefill(sub, torch, plx)
     recs["prefill_bwd"] = run_prefill_bwd(sub, torch, plx)
+    sub.tokens, sub.model_dim = 32768, 2048
+    recs["qr_proj"] = run_qr_proj(sub, torch, plx)
     for r in recs.values():  # the sub-records' own JSON keys, minus the shared ones
         for k in ("metric", "dtype"):
             r.pop(k, None)
