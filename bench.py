@@ -398,8 +398,11 @@ def run_qr_proj(args, torch, plx):
     rows = list(range(min(T, 64)))
     rq, rr = oracle.qr_projection(host_array(x[rows]), host_array(ws[0][0]), host_array(ws[0][1]))
     tau = 1e-5 if out_dtype == torch.float32 else 2.0 ** -8
-    gate(q[rows].reshape(len(rows), -1).double().cpu().numpy(), rq, tau, 1e-2)
-    gate(rho[rows].reshape(len(rows), -1).double().cpu().numpy(), rr, tau, 1e-2)
+    pq = gate(q[rows].reshape(len(rows), -1).double().cpu().numpy(), rq, tau, 1e-2)
+    pr = gate(rho[rows].reshape(len(rows), -1).double().cpu().numpy(), rr, tau, 1e-2)
+    parity = {"rows": f"the first {len(rows)} token rows, every feature",
+              "q": {"max_err_ratio": pq[0], "rel_rms": pq[1]},
+              "rho": {"max_err_ratio": pr[0], "rel_rms": pr[1]}}
     cpu = None
     if args.cpu_baseline:
         Ts = min(T, 1024)  # a bounded sample of token rows at prefill sizes
@@ -457,7 +460,7 @@ def run_qr_proj(args, torch, plx):
                    "tokens": T, "model_dim": D, "cold_copies": n_bufs},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s": T / per,
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "parity": parity, "cpu_baseline": cpu,
     }
 
 
