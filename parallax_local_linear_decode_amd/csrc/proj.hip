@@ -348,9 +348,9 @@ constexpr int kBigOp = kBigT * kBigRow;       // one operand of one stage
 constexpr int kBigStage = 2 * kBigOp;         // weights then tokens
 static_assert(4 * kBigStage <= 160 * 1024, "four stages fit the 160 KB of LDS of a gfx950 CU");
 
-// s_waitcnt immediates: vector memory count (bits 3:0 and 15:14) at most 16,
-// 8 or 0 loads pending, LDS count (bits 11:8) 0, export count (6:4) free
-constexpr int kWait16 = 0x4070, kWait8 = 0x0078, kWait0 = 0x0070;
+// s_waitcnt immediates: vector memory count (bits 3:0 and 15:14) at most 24,
+// 16, 8 or 0 loads pending, LDS count (bits 11:8) 0, export count (6:4) free
+constexpr int kWait24 = 0x4078, kWait16 = 0x4070, kWait8 = 0x0078, kWait0 = 0x0070;
 
 // The workgroup barrier of the big-tile kernel, after the caller's explicit
 // wait.  __syncthreads() would add a release fence, for which the compiler
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
     dma(st1, kBigK);
     dma(st2, 2 * kBigK);
     dma(st3, 3 * kBigK);
-    __builtin_amdgcn_s_waitcnt(kWait16 + 8);  // step 0's loads landed (24 may run)
+    __builtin_amdgcn_s_waitcnt(kWait24);  // step 0's loads landed (steps 1-3's may run)
     big_barrier();
     read_ops(st0, oa);
     for (int s = 0; s < nsteps - 4; s += 4) {
