@@ -42,8 +42,9 @@ def test_every_element(gpu, T, D, Hq, d, out_dtype):
 
 
 @pytest.mark.parametrize("T,D,Hq,d", [(4096, 2048, 16, 128), (4100, 1024, 16, 128),
-                                      (8200, 512, 8, 128), (32900, 256, 2, 128),
-                                      (22000, 256, 3, 128), (4100, 256, 1, 64)])
+                                      (4100, 8192, 16, 128), (8200, 512, 8, 128),
+                                      (32900, 256, 2, 128), (22000, 256, 3, 128),
+                                      (4100, 256, 1, 64)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_prefill_token_counts(gpu, T, D, Hq, d, out_dtype):
     """Token counts of prefill, the LDS-tiled GEMMs with ragged last token
