@@ -8,15 +8,22 @@
 // outputs, and the results land directly in the strided [T, Hq, d] layouts
 // the attention kernels read (fp32 for decode, bf16 for prefill).
 //
-// Workgroup: 16 RT stacked weight rows x 16 NT tokens; its eight waves split
-// the model dimension D into eighths, each accumulating partial 16 x 16
-// tiles with 16x16x32 bf16 MFMAs and fp32 accumulation; the partials are
-// summed in LDS in wave order.  At decode sizes (up to 64 tokens) the product
-// is bound by streaming the weights from HBM: one row tile per workgroup
-// (2N / 16 workgroups, 256 for 2N = 4096, so every CU streams), and a wave
-// issues all loads of its eighth of D before the MFMAs, so the whole weight
-// set is requested at once.  From 65 to 128 tokens two row tiles per
-// workgroup let one token load serve two weight loads.
+// Three kernels, by token count (all bf16 MFMAs with fp32 accumulation, the
+// same k order per output element, so their results agree bit for bit):
+//  * up to 128 tokens (decode), proj_kernel: bound by streaming the weights
+//    from HBM.  Workgroup: 16 RT stacked weight rows x 16 NT tokens; its
+//    eight waves split the model dimension D into eighths, each accumulating
+//    partial 16 x 16 tiles; the partials are summed in LDS in wave order.
+//    One row tile per workgroup (2N / 16 workgroups, 256 for 2N = 4096, so
+//    every CU streams), and a wave issues all loads of its eighth of D before
+//    the MFMAs, so the whole weight set is requested at once.  From 65 to 128
+//    tokens two row tiles per workgroup let one token load serve two weight
+//    loads.
+//  * prefill sizes, proj_tiled_kernel: an LDS-tiled GEMM, 256 x 256 tiles on
+//    eight waves (or 128 x 128 on four), loads one chunk ahead in registers.
+//  * prefill sizes with N a multiple of 256, proj_big_kernel: 256 x 256 tiles
+//    on four waves of 128 x 128, fed by global->LDS loads through a ring of
+//    four LDS stages.
 #include "kernels.hpp"
 
 #include <type_traits>
