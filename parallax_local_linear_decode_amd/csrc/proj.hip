@@ -8,8 +8,9 @@
 // outputs, and the results land directly in the strided [T, Hq, d] layouts
 // the attention kernels read (fp32 for decode, bf16 for prefill).
 //
-// Three kernels, by token count (all bf16 MFMAs with fp32 accumulation, the
-// same k order per output element, so their results agree bit for bit):
+// Three kernels, by token count, all on bf16 MFMAs with fp32 accumulation
+// (the two LDS-tiled ones add the k terms of an output element in the same
+// order, so their results agree bit for bit):
 //  * up to 128 tokens (decode), proj_kernel: bound by streaming the weights
 //    from HBM.  Workgroup: 16 RT stacked weight rows x 16 NT tokens; its
 //    eight waves split the model dimension D into eighths, each accumulating
