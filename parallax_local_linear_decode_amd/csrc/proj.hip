@@ -23,8 +23,8 @@
 //  * prefill sizes, proj_tiled_kernel: an LDS-tiled GEMM, 256 x 256 tiles on
 //    eight waves (or 128 x 128 on four), loads one chunk ahead in registers.
 //  * prefill sizes with N a multiple of 256, proj_big_kernel: 256 x 256 tiles
-//    on four waves of 128 x 128, fed by global->LDS loads through a ring of
-//    four LDS stages.
+//    on four waves of 128 x 128, fed by global->LDS loads through two LDS
+//    stages of 64-wide K chunks.
 #include "kernels.hpp"
 
 #include <type_traits>
@@ -338,32 +338,34 @@ hipError_t launch_tiled(const ProjParams &p, hipStream_t stream) {
 // from LDS for 2 * 128 * 128 flops, half the LDS traffic per flop of the
 // eight-wave tile.
 //
-// K runs in steps of 32 through four LDS stages of 32 KB (the weight tile,
-// then the token tile, 64-byte rows), filled by global->LDS buffer loads (16
-// bytes per lane, no staging registers, no LDS store instructions) issued
-// three steps ahead of their use.  A load instruction writes 1 KB = sixteen
-// 64-byte rows in lane order, so rows cannot be padded; the four 16-byte
-// pieces of row R are stored in the order piece ^ swz(R) instead, which puts
-// the rows one operand read touches on distinct banks.  One barrier per
-// step: it publishes step s + 1's stage (every wave has waited for its own
-// loads of it) and frees step s's stage (every wave has its operands of step
-// s in registers), which then takes step s + 4; the operand reads of step
-// s + 1 run under the MFMAs of step s.
+// K runs in chunks of 64 through two LDS stages of 64 KB (the weight tile,
+// then the token tile, 128-byte rows), filled by global->LDS buffer loads
+// (16 bytes per lane, no staging registers, no LDS store instructions).  A
+// load instruction writes 1 KB = eight 128-byte rows in lane order (so every
+// request is a whole 128-byte line), and rows cannot be padded: the eight
+// 16-byte pieces of row R are stored in the order piece ^ (R % 8) instead,
+// which puts the eight rows one operand read touches on distinct banks.  A
+// chunk is two k-steps of 32, each 64 MFMAs per wave on operands read one
+// k-step ahead into a second register set: the second k-step's reads run
+// under the first one's MFMAs; then one barrier publishes chunk c + 1's stage
+// (every wave has waited for its own loads of it) and frees chunk c's (every
+// wave has its operands in registers), which takes chunk c + 2's loads while
+// chunk c + 1's first k-step is read, both under the second k-step's MFMAs.
 constexpr int kBigT = 256;                    // tile rows and tokens
-constexpr int kBigK = 32;                     // k per stage
-constexpr int kBigRow = kBigK * 2;            // 64-byte rows
+constexpr int kBigK = 64;                     // k per stage
+constexpr int kBigRow = kBigK * 2;            // 128-byte rows
 constexpr int kBigOp = kBigT * kBigRow;       // one operand of one stage
 constexpr int kBigStage = 2 * kBigOp;         // weights then tokens
-static_assert(4 * kBigStage <= 160 * 1024, "four stages fit the 160 KB of LDS of a gfx950 CU");
+static_assert(2 * kBigStage <= 160 * 1024, "two stages fit the 160 KB of LDS of a gfx950 CU");
 
-// s_waitcnt immediates: vector memory count (bits 3:0 and 15:14) at most 24,
-// 16, 8 or 0 loads pending, LDS count (bits 11:8) 0, export count (6:4) free
-constexpr int kWait24 = 0x4078, kWait16 = 0x4070, kWait8 = 0x0078, kWait0 = 0x0070;
+// s_waitcnt immediates: vector memory count (bits 3:0 and 15:14) at most 16
+// or 0 loads pending, LDS count (bits 11:8) 0, export count (6:4) free
+constexpr int kWait16 = 0x4070, kWait0 = 0x0070;
 
 // The workgroup barrier of the big-tile kernel, after the caller's explicit
 // wait.  __syncthreads() would add a release fence, for which the compiler
-// waits for every pending global->LDS load, including the ones issued for
-// later steps; the empty asm statements keep the compiler from moving
+// may wait for every pending global->LDS load, including the ones issued for
+// later chunks; the empty asm statements keep the compiler from moving
 // memory accesses across the barrier instead.
 __device__ __forceinline__ void big_barrier() {
     asm volatile("" ::: "memory");
@@ -371,17 +373,10 @@ __device__ __forceinline__ void big_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Rows r and r + 1 share a 128-byte bank window; pieces are permuted by
-// (r / 2) % 4, so rows 0..7 of one read land on distinct 16-byte bank groups
-// (the LDS bank-conflict counter reads zero for this kernel).
-__device__ __forceinline__ int big_swz(int row) { return (row >> 1) & 3; }
-
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, int n_tb) {
     __shared__ __attribute__((aligned(1024))) unsigned char st0[kBigStage];
     __shared__ __attribute__((aligned(1024))) unsigned char st1[kBigStage];
-    __shared__ __attribute__((aligned(1024))) unsigned char st2[kBigStage];
-    __shared__ __attribute__((aligned(1024))) unsigned char st3[kBigStage];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -414,17 +409,17 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
         (void *)xbase, (short)0, (int)(((min(T - t0, kBigT) - 1) * (int64_t)p.x_st + p.model_dim) * 2),
         0x00020000);
-    // Loads: wave w fills rows 64 w + 16 j + lane / 4 (j = 0..3) of both
+    // Loads: wave w fills rows 64 w + 8 j + lane / 8 (j = 0..7) of both
     // operands; lane i lands at byte 16 i of its instruction's 1 KB, i.e.
-    // physical piece i % 4 of its row, which holds logical piece
-    // (i % 4) ^ swz(row) (row % 16 == lane / 4 for every j).
+    // physical piece i % 8 of its row, which holds logical piece
+    // (i % 8) ^ (row % 8) (row % 8 == lane / 8 for every j).
     const int wsn = (int)p.w_sn, xst = (int)p.x_st;
-    const int lr = lane >> 2, lp = (lane & 3) ^ big_swz(lane >> 2);
+    const int lr = lane >> 3, lp = (lane & 7) ^ lr;
     const int wv = (lr * wsn + 8 * lp) * 2, xv = (lr * xst + 8 * lp) * 2;
     auto dma = [&](unsigned char *stage, int k0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 64 * wave + 16 * j;
+        for (int j = 0; j < 8; ++j) {
+            const int r = 64 * wave + 8 * j;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 wres, (__attribute__((address_space(3))) void *)(stage + r * kBigRow), 16, wv,
                 (r * wsn + k0) * 2, 0, 0);
@@ -436,21 +431,21 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
 
     // Operand reads: wave (wr, wc) = (wave % 2, wave / 2) owns weight rows
     // 128 wr .. + 127 and tokens 128 wc .. + 127 of the tile; MFMA tile i
-    // (j) is rows (tokens) 16 i + c, k-slots 8 g .. 8 g + 7 = logical piece
-    // g.  Every such row has row % 16 == c, so the swizzle is the lane's own.
+    // (j) is rows (tokens) 16 i + c, k-slots 8 g .. 8 g + 7 of k-step kk =
+    // logical piece 4 kk + g.  Every such row has row % 8 == c % 8.
     const int wr = wave & 1, wc = wave >> 1;
-    const int po = 16 * (g ^ big_swz(c));
-    const int aoff = (128 * wr + c) * kBigRow + po, boff = kBigOp + (128 * wc + c) * kBigRow + po;
+    const int aoff = (128 * wr + c) * kBigRow, boff = kBigOp + (128 * wc + c) * kBigRow;
     struct Ops {
         bf16x8_t a[8], b[8];
     };
-    auto read_ops = [&](const unsigned char *stage, Ops &o) __attribute__((always_inline)) {
+    auto read_ops = [&](const unsigned char *stage, int kk, Ops &o) __attribute__((always_inline)) {
+        const int po = 16 * ((4 * kk + g) ^ (c & 7));
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
             o.a[n] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                      stage + aoff + 16 * n * kBigRow));
+                                                      stage + aoff + po + 16 * n * kBigRow));
             o.b[n] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                                                      stage + boff + 16 * n * kBigRow));
+                                                      stage + boff + po + 16 * n * kBigRow));
         }
     };
 
@@ -467,58 +462,56 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
     };
 
-    // Step s: `cur` holds operands of step s; `stage` is step s's stage,
-    // `next` step s + 1's.  WAIT is the pending-load bound that leaves step
-    // s + 1's loads landed (the later steps' loads may still run) and this
-    // wave's operand reads of step s back.
-    // Scheduling barriers pin the order (the compiler otherwise moves each
-    // read next to its first use and waits for it there, and sinks MFMAs
-    // below the barrier).
-    const int nsteps = p.model_dim / kBigK;  // a multiple of 8 (model_dim % 256 == 0)
+    // Chunk ch in stage `cur` (the other stage is `nxt`): oa holds its first
+    // k-step on entry and the next chunk's first k-step on exit.  The last
+    // two chunks load nothing more (and the last reads nothing more): those
+    // are separate instances, so the loop body has no branches.  Scheduling
+    // barriers pin the order (the compiler otherwise moves each read next to
+    // its first use and waits for it there, and sinks MFMAs below the
+    // barrier); scheduling-group barriers spread the loads and reads over
+    // the MFMAs, so the matrix core is not idle while the wave (one per SIMD)
+    // issues them.
+    const int nch = p.model_dim / kBigK;  // a multiple of 4 (model_dim % 256 == 0)
     Ops oa, ob;
-    auto step = [&](int s, unsigned char *stage, const unsigned char *next, Ops &cur, Ops &nxt,
-                    auto wait, auto more_loads, auto more_reads) __attribute__((always_inline)) {
+    auto chunk = [&](int ch, unsigned char *cur, unsigned char *nxt, auto more_loads, auto more_reads)
+        __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (decltype(more_reads)::value) {
-            __builtin_amdgcn_s_waitcnt(decltype(wait)::value);
-            big_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (decltype(more_loads)::value) dma(stage, (s + 4) * kBigK);
-            read_ops(next, nxt);
-        }
-        mfmas(cur);
-        // One wave per SIMD: the loads and reads are spread over the MFMAs
-        // (one load, two reads, eight MFMAs), so the matrix core is not idle
-        // while the wave issues them.
+        read_ops(cur, 1, ob);
+        mfmas(oa);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if constexpr (decltype(more_loads)::value) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // eight MFMAs
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's reads of `cur` back and its loads of chunk ch + 1
+        // landed (no later loads are in flight)
+        __builtin_amdgcn_s_waitcnt(kWait0);
+        big_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(more_loads)::value) dma(cur, (ch + 2) * kBigK);
+        if constexpr (decltype(more_reads)::value) read_ops(nxt, 0, oa);
+        mfmas(ob);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (decltype(more_loads)::value) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
             if constexpr (decltype(more_reads)::value) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
     };
-    using W16 = std::integral_constant<int, kWait16>;
-    using W8 = std::integral_constant<int, kWait8>;
-    using W0 = std::integral_constant<int, kWait0>;
     using T_ = std::true_type;
     using F_ = std::false_type;
     dma(st0, 0);
     dma(st1, kBigK);
-    dma(st2, 2 * kBigK);
-    dma(st3, 3 * kBigK);
-    __builtin_amdgcn_s_waitcnt(kWait24);  // step 0's loads landed (steps 1-3's may run)
+    __builtin_amdgcn_s_waitcnt(kWait16);  // chunk 0's loads landed (chunk 1's may run)
     big_barrier();
-    read_ops(st0, oa);
-    for (int s = 0; s < nsteps - 4; s += 4) {
-        step(s, st0, st1, oa, ob, W16{}, T_{}, T_{});
-        step(s + 1, st1, st2, ob, oa, W16{}, T_{}, T_{});
-        step(s + 2, st2, st3, oa, ob, W16{}, T_{}, T_{});
-        step(s + 3, st3, st0, ob, oa, W16{}, T_{}, T_{});
+    read_ops(st0, 0, oa);
+    for (int ch = 0; ch < nch - 2; ch += 2) {
+        chunk(ch, st0, st1, T_{}, T_{});
+        chunk(ch + 1, st1, st0, T_{}, T_{});
     }
-    step(nsteps - 4, st0, st1, oa, ob, W16{}, F_{}, T_{});
-    step(nsteps - 3, st1, st2, ob, oa, W8{}, F_{}, T_{});
-    step(nsteps - 2, st2, st3, oa, ob, W0{}, F_{}, T_{});
-    step(nsteps - 1, st3, st0, ob, oa, W0{}, F_{}, F_{});
+    chunk(nch - 2, st0, st1, F_{}, T_{});
+    chunk(nch - 1, st1, st0, F_{}, F_{});
 
     // acc[i][j]: lane (c, g) holds stacked rows row0 + 128 wr + 16 i + 4 g +
     // (0..3) of token t0 + 128 wc + 16 j + c

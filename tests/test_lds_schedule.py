@@ -3,9 +3,9 @@
 The causal prefill kernel (csrc/prefill.hip) and the backward's dq and dk/dv
 kernels (csrc/prefill_bwd.hip) split each 32-row block between a score wave
 and a value wave that hand tiles to each other through LDS, with one barrier
-per tile; the projection's large-tile GEMM (csrc/proj.hip) fills a ring of
-four LDS stages with global->LDS loads that land at no fixed time, bounded
-only by each wave's explicit wait counts.  This module restates, role by role and in each kernel's own order,
+per tile; the projection's large-tile GEMM (csrc/proj.hip) fills two LDS
+stages with global->LDS loads that land at no fixed time, bounded only by
+each wave's explicit wait counts.  This module restates, role by role and in each kernel's own order,
 which LDS buffer every wave reads and writes between two barriers (an
 "epoch"), which tile each buffer holds, and what the register stages of the
 global loads hold when they are stored; then checks, over many grid shapes
@@ -21,8 +21,8 @@ workgroups, whose items follow each other in one stream of positions):
 
 A planted change (the dq kernel's K tiles double- instead of triple-
 buffered, the forward's register stages swapped, its items shorter than
-the three positions its loads run ahead, or the projection's last waits
-one step too loose or its ring one stage short) must be caught.  The
+the three positions its loads run ahead, or the projection's waits one
+chunk too loose or its loads issued before the barrier) must be caught.  The
 forward this kernel replaced (four waves, each doing both roles on its own
 rows), which returned wrong results on some launches, is modelled too: the
 model locates its race (K tile 2 stored over tile 0 in the epoch in which
@@ -328,16 +328,18 @@ def dkv_trace(ntiles, active_sets):
 
 # ----------------------------------------------------------- projection ---
 
-def proj_trace(nsteps, waits=None, stages=4):
-    """proj_big_kernel: four waves, K step s of both operand tiles in stage
+def proj_trace(nsteps, waits=None, stages=2, early_loads=False):
+    """proj_big_kernel: four waves, K chunk s of both operand tiles in stage
     s % stages, filled by global->LDS loads that each wave issues for its own
-    rows: steps 0-3 in the prologue, step s + 4 right after step s's barrier.
-    Such a load lands at no fixed time: the model writes its stage in every
-    epoch from its issue up to the one in which the issuing wave's explicit
-    wait (pending loads at most `bound` steps' worth, oldest first) covers
-    it.  The prologue waits for step 0 and publishes it; step s waits for
-    step s + 1's loads, passes the barrier and reads step s + 1's operands
-    (all rows, so every wave's loads).  `waits[s]` = step s's bound."""
+    rows: chunks 0 and 1 in the prologue, chunk s + 2 right after chunk s's
+    barrier.  Such a load lands at no fixed time: the model writes its stage
+    in every epoch from its issue up to the one in which the issuing wave's
+    explicit wait (pending loads at most `bound` chunks' worth, oldest first)
+    covers it.  The prologue waits for chunk 0 and publishes it; chunk s
+    reads its second k-step (same stage), waits for chunk s + 1's loads,
+    passes the barrier and reads chunk s + 1's first k-step (all rows, so
+    every wave's loads).  `waits[s]` = chunk s's bound; `early_loads` plants
+    the mistake of issuing chunk s + 2's loads before the barrier."""
     if waits is None:
         waits = proj_waits(nsteps)
     tr = Trace()
@@ -359,10 +361,13 @@ def proj_trace(nsteps, waits=None, stages=4):
         wv.barrier()
         wv.read(("S", 0), 0)
         for st in range(nsteps):
+            wv.read(("S", st % stages), st)  # the chunk's second k-step
             if waits[st] is not None:
+                if early_loads and st + stages < nsteps:
+                    issue(st + stages)
                 wait(waits[st])
                 wv.barrier()
-                if st + stages < nsteps:
+                if not early_loads and st + stages < nsteps:
                     issue(st + stages)
                 wv.read(("S", (st + 1) % stages), st + 1)
         end = wv.epoch
@@ -373,9 +378,9 @@ def proj_trace(nsteps, waits=None, stages=4):
 
 
 def proj_waits(nsteps):
-    """The bounds the kernel's steps use (in steps of loads): two in the
-    loop and at nsteps - 4, then one, none, and no wait at the last step."""
-    return [2] * (nsteps - 3) + [1, 0, None]
+    """The kernel's bounds: every chunk but the last waits for all of its
+    loads (none are issued past the next chunk); the last reads nothing."""
+    return [0] * (nsteps - 1) + [None]
 
 
 # ------------------------------------------------- the replaced forward ---
@@ -502,19 +507,19 @@ def test_dkv_schedule(ntiles):
     assert check(dkv_trace(ntiles, sets)) == []
 
 
-@pytest.mark.parametrize("nsteps", [8, 16, 24, 64])
+@pytest.mark.parametrize("nsteps", [4, 8, 16, 32])
 def test_projection_schedule(nsteps):
-    assert check(proj_trace(nsteps, proj_waits(nsteps))) == []
+    assert check(proj_trace(nsteps)) == []
 
 
 def test_planted_projection_errors_are_caught():
-    """A wait one step too loose at the end (step nsteps - 3 waiting as in
-    the loop) reads step nsteps - 2 while its loads may still land; three
-    stages for four steps of loads in flight store over a stage being read."""
+    """A chunk that waits only for its older loads (one chunk still
+    pending) reads the next chunk while it may still land; loads of chunk
+    s + 2 issued before the barrier store over the stage others still read."""
     w = proj_waits(16)
-    w[-3] = 2
+    w[5] = 1
     assert any(b[0] == "unordered access" for b in check(proj_trace(16, w)))
-    assert any(b[0] == "unordered access" for b in check(proj_trace(16, proj_waits(16), stages=3)))
+    assert any(b[0] == "unordered access" for b in check(proj_trace(16, early_loads=True)))
 
 
 @pytest.mark.parametrize("ntiles", range(1, 12))
