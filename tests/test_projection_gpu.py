@@ -48,7 +48,8 @@ def test_every_element(gpu, T, D, Hq, d, out_dtype):
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_prefill_token_counts(gpu, T, D, Hq, d, out_dtype):
     """Token counts of prefill, the LDS-tiled GEMMs with ragged last token
-    tiles: the four-wave 256 x 256 kernel (N a multiple of 256; the 32900-token
+    tiles: the four-wave 256 x 256 kernel (N a multiple of 256; model dims 256
+    to 8192, i.e. 4 to 128 chunks through its two LDS stages; the 32900-token
     grid of 258 tiles is not a multiple of eight, so its tiles keep launch
     order), the eight-wave 256 x 256 kernel (N = 384) and 128 x 128 tiles
     (Hq = 1, d = 64).  Sampled rows against the oracle: the first and last
