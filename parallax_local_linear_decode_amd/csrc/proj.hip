@@ -515,23 +515,61 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
 
     // acc[i][j]: lane (c, g) holds stacked rows row0 + 128 wr + 16 i + 4 g +
     // (0..3) of token t0 + 128 wc + 16 j + c
+    const int fbase = row0 - (is_r ? p.n : 0);
+    if constexpr (BF16OUT) {
+        // bf16 outputs go through LDS, so every token's 256 features leave
+        // as 16-byte pieces of whole lines (the lane layout above writes 8
+        // bytes per token and row group, 16 tokens apart).  The tile is
+        // [256 tokens][256 features] bf16, 512-byte rows (tokens 0..127 in
+        // st0, 128..255 in st1); 16-byte piece k of row r sits at k ^ (r % 16),
+        // so the 16 rows one write touches land on distinct banks.
+        __builtin_amdgcn_s_waitcnt(kWait0);
+        big_barrier();  // every wave's last operand reads are back
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        unsigned char *ot = wc ? st1 : st0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int f = row0 - (is_r ? p.n : 0) + 128 * wr + 16 * i + 4 * g;
-        const int h = f / p.head_dim, e = f % p.head_dim;
-        const int64_t hoff = (int64_t)h * (is_r ? p.r_sh : p.q_sh) + e;
+        for (int i = 0; i < 8; ++i) {
+            const int col = 128 * wr + 16 * i + 4 * g;  // feature, a multiple of 4
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int t = t0 + 128 * wc + 16 * j + c;
-            if (t >= T) continue;
-            const int64_t off = (int64_t)t * (is_r ? p.r_st : p.q_st) + hoff;
-            const f32x4_t v = acc[i][j];
-            if constexpr (BF16OUT) {
-                typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+            for (int j = 0; j < 8; ++j) {
+                const int r = 16 * j + c;  // row within the half (r % 16 == c)
+                const f32x4_t v = acc[i][j];
                 const bf16x4_t b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(is_r ? p.rho : p.q) + off) =
+                const int piece = (col >> 3) ^ c;
+                *reinterpret_cast<uint2 *>(ot + r * 512 + 16 * piece + 2 * (col & 7)) =
                     __builtin_bit_cast(uint2, b);
-            } else {
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWait0);
+        big_barrier();
+        // wave w stores tokens 64 w .. 64 w + 63, two per instruction: lane
+        // half hl = lane / 32 takes token 64 w + 2 s + hl, piece lane % 32
+        const int hl = lane >> 5, k = lane & 31;
+        const unsigned char *it = wave < 2 ? st0 : st1;
+        const int f = fbase + 8 * k;
+        const int h = f / p.head_dim, e = f % p.head_dim;
+        uint16_t *out = static_cast<uint16_t *>(is_r ? p.rho : p.q) + (int64_t)h * (is_r ? p.r_sh : p.q_sh) + e;
+        const int64_t ost = is_r ? p.r_st : p.q_st;
+#pragma unroll 8
+        for (int s2 = 0; s2 < 32; ++s2) {
+            const int tr = 64 * wave + 2 * s2 + hl;  // token within the tile
+            const int r = tr & 127;
+            const uint4 v = *reinterpret_cast<const uint4 *>(it + r * 512 + 16 * (k ^ (r & 15)));
+            const int t = t0 + tr;
+            if (t < T) *reinterpret_cast<uint4 *>(out + (int64_t)t * ost) = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int f = fbase + 128 * wr + 16 * i + 4 * g;
+            const int h = f / p.head_dim, e = f % p.head_dim;
+            const int64_t hoff = (int64_t)h * (is_r ? p.r_sh : p.q_sh) + e;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int t = t0 + 128 * wc + 16 * j + c;
+                if (t >= T) continue;
+                const int64_t off = (int64_t)t * (is_r ? p.r_st : p.q_st) + hoff;
+                const f32x4_t v = acc[i][j];
                 *reinterpret_cast<float4 *>(static_cast<float *>(is_r ? p.rho : p.q) + off) =
                     float4{v[0], v[1], v[2], v[3]};
             }
