@@ -27,6 +27,7 @@
 //    stages of 64-wide K chunks.
 #include "kernels.hpp"
 
+#include <atomic>
 #include <type_traits>
 
 namespace plx {
@@ -358,9 +359,10 @@ constexpr int kBigOp = kBigT * kBigRow;       // one operand of one stage
 constexpr int kBigStage = 2 * kBigOp;         // weights then tokens
 static_assert(2 * kBigStage <= 160 * 1024, "two stages fit the 160 KB of LDS of a gfx950 CU");
 
-// s_waitcnt immediates: vector memory count (bits 3:0 and 15:14) at most 16
-// or 0 loads pending, LDS count (bits 11:8) 0, export count (6:4) free
-constexpr int kWait16 = 0x4070, kWait0 = 0x0070;
+// s_waitcnt immediates: vector memory count (bits 3:0 and 15:14) 0 pending,
+// LDS count (bits 11:8) 0, export count (6:4) free;
+// kWaitLds: the LDS count only (vector memory count 63)
+constexpr int kWait0 = 0x0070, kWaitLds = 0xC07F;
 
 // The workgroup barrier of the big-tile kernel, after the caller's explicit
 // wait.  __syncthreads() would add a release fence, for which the compiler
@@ -382,33 +384,49 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane & 15;
     const int g = lane >> 4;
-
-    // Tile order: workgroups are dealt to the eight XCDs in turn, so when
-    // the tile count divides by 8, XCD x gets the x-th eighth of the order;
-    // the order walks groups of four token blocks, row block by row block,
-    // so the 32 workgroups an XCD runs at a time cover 4 token blocks x 8
-    // row blocks and share those tiles in its L2.
-    const int nt = n_rb * n_tb;
-    const int bid = blockIdx.x;
-    const int lid = nt % 8 == 0 ? (bid % 8) * (nt / 8) + bid / 8 : bid;
-    const int grp = lid / (4 * n_rb);
-    const int gsz = min(4, n_tb - 4 * grp);
-    const int in = lid - grp * 4 * n_rb;
-    const int tb = 4 * grp + in % gsz, rb = in / gsz;
-    const int row0 = rb * kBigT, t0 = tb * kBigT;
     const int T = p.tokens;
-    const bool is_r = row0 >= p.n;  // N is a multiple of 256: a tile never straddles
-    const uint16_t *wbase = (is_r ? p.w_r : p.w_q) + (int64_t)(row0 - (is_r ? p.n : 0)) * p.w_sn;
-    const uint16_t *xbase = p.x + (int64_t)t0 * p.x_st;
+    const int nt = n_rb * n_tb;
 
-    // Buffer resources over the tile's weight rows and token rows: a load
-    // past the last token row returns zeros (those outputs are not stored).
-    // Byte offsets fit 32 bits: the launcher checks 256 * stride * 2 < 2^31.
-    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)wbase, (short)0, (int)(((kBigT - 1) * p.w_sn + p.model_dim) * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)xbase, (short)0, (int)(((min(T - t0, kBigT) - 1) * (int64_t)p.x_st + p.model_dim) * 2),
-        0x00020000);
+    // One workgroup per CU runs tiles blockIdx.x, + gridDim.x, ... (the
+    // grid is a multiple of 8, so a workgroup's tiles stay on its XCD); the
+    // next tile's first loads are issued before this tile's outputs are
+    // stored.  Tile order: workgroups are dealt to the eight XCDs in turn,
+    // so when the tile count divides by 8, XCD x gets the x-th eighth of the
+    // order; the order walks groups of four token blocks, row block by row
+    // block, so the 32 tiles an XCD runs at a time cover 4 token blocks x 8
+    // row blocks and share those tiles in its L2.
+    struct Tile {
+        int row0, t0;
+        bool is_r;
+    };
+    auto tile_of = [&](int bid) __attribute__((always_inline)) {
+        Tile ti;
+        const int lid = nt % 8 == 0 ? (bid % 8) * (nt / 8) + bid / 8 : bid;
+        const int grp = lid / (4 * n_rb);
+        const int gsz = min(4, n_tb - 4 * grp);
+        const int in = lid - grp * 4 * n_rb;
+        const int tb = 4 * grp + in % gsz, rb = in / gsz;
+        ti.row0 = rb * kBigT;
+        ti.t0 = tb * kBigT;
+        ti.is_r = ti.row0 >= p.n;  // N is a multiple of 256: a tile never straddles
+        return ti;
+    };
+    // Buffer resources over a tile's weight rows and token rows: a load past
+    // the last token row returns zeros (those outputs are not stored); byte
+    // offsets fit 32 bits (the launcher checks 256 * stride * 2 < 2^31).
+    auto wres_of = [&](const Tile &ti) __attribute__((always_inline)) {
+        const uint16_t *wbase =
+            (ti.is_r ? p.w_r : p.w_q) + (int64_t)(ti.row0 - (ti.is_r ? p.n : 0)) * p.w_sn;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)wbase, (short)0,
+                                                 (int)(((kBigT - 1) * p.w_sn + p.model_dim) * 2), 0x00020000);
+    };
+    auto xres_of = [&](const Tile &ti) __attribute__((always_inline)) {
+        const uint16_t *xbase = p.x + (int64_t)ti.t0 * p.x_st;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)xbase, (short)0,
+            (int)(((min(T - ti.t0, kBigT) - 1) * (int64_t)p.x_st + p.model_dim) * 2), 0x00020000);
+    };
+
     // Loads: wave w fills rows 64 w + 8 j + lane / 8 (j = 0..7) of both
     // operands; lane i lands at byte 16 i of its instruction's 1 KB, i.e.
     // physical piece i % 8 of its row, which holds logical piece
@@ -416,7 +434,8 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
     const int wsn = (int)p.w_sn, xst = (int)p.x_st;
     const int lr = lane >> 3, lp = (lane & 7) ^ lr;
     const int wv = (lr * wsn + 8 * lp) * 2, xv = (lr * xst + 8 * lp) * 2;
-    auto dma = [&](unsigned char *stage, int k0) __attribute__((always_inline)) {
+    auto dma = [&](const Tile &ti, unsigned char *stage, int k0) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t wres = wres_of(ti), xres = xres_of(ti);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = 64 * wave + 8 * j;
@@ -450,10 +469,6 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
     };
 
     f32x4_t acc[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     auto mfmas = [&](const Ops &o) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -473,8 +488,8 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
     // issues them.
     const int nch = p.model_dim / kBigK;  // a multiple of 4 (model_dim % 256 == 0)
     Ops oa, ob;
-    auto chunk = [&](int ch, unsigned char *cur, unsigned char *nxt, auto more_loads, auto more_reads)
-        __attribute__((always_inline)) {
+    auto chunk = [&](const Tile &ti, int ch, unsigned char *cur, unsigned char *nxt, auto more_loads,
+                     auto more_reads) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         read_ops(cur, 1, ob);
         mfmas(oa);
@@ -489,7 +504,7 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
         __builtin_amdgcn_s_waitcnt(kWait0);
         big_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (decltype(more_loads)::value) dma(cur, (ch + 2) * kBigK);
+        if constexpr (decltype(more_loads)::value) dma(ti, cur, (ch + 2) * kBigK);
         if constexpr (decltype(more_reads)::value) read_ops(nxt, 0, oa);
         mfmas(ob);
 #pragma unroll
@@ -501,89 +516,163 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
-    dma(st0, 0);
-    dma(st1, kBigK);
-    __builtin_amdgcn_s_waitcnt(kWait16);  // chunk 0's loads landed (chunk 1's may run)
-    big_barrier();
-    read_ops(st0, 0, oa);
-    for (int ch = 0; ch < nch - 2; ch += 2) {
-        chunk(ch, st0, st1, T_{}, T_{});
-        chunk(ch + 1, st1, st0, T_{}, T_{});
-    }
-    chunk(nch - 2, st0, st1, F_{}, T_{});
-    chunk(nch - 1, st1, st0, F_{}, F_{});
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-    // acc[i][j]: lane (c, g) holds stacked rows row0 + 128 wr + 16 i + 4 g +
-    // (0..3) of token t0 + 128 wc + 16 j + c
-    const int fbase = row0 - (is_r ? p.n : 0);
-    if constexpr (BF16OUT) {
-        // bf16 outputs go through LDS, so every token's 256 features leave
-        // as 16-byte pieces of whole lines (the lane layout above writes 8
-        // bytes per token and row group, 16 tokens apart).  The tile is
-        // [256 tokens][256 features] bf16, 512-byte rows (tokens 0..127 in
-        // st0, 128..255 in st1); 16-byte piece k of row r sits at k ^ (r % 16),
-        // so the 16 rows one write touches land on distinct banks.
-        __builtin_amdgcn_s_waitcnt(kWait0);
-        big_barrier();  // every wave's last operand reads are back
-        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-        unsigned char *ot = wc ? st1 : st0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int col = 128 * wr + 16 * i + 4 * g;  // feature, a multiple of 4
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int r = 16 * j + c;  // row within the half (r % 16 == c)
-                const f32x4_t v = acc[i][j];
-                const bf16x4_t b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-                const int piece = (col >> 3) ^ c;
-                *reinterpret_cast<uint2 *>(ot + r * 512 + 16 * piece + 2 * (col & 7)) =
-                    __builtin_bit_cast(uint2, b);
-            }
-        }
+    // (tiles are rebuilt from their index where needed: a tile kept across
+    // loop iterations went to scratch memory)
+    int bid = blockIdx.x;
+    {
+        const Tile first = tile_of(bid);
+        dma(first, st0, 0);
+        dma(first, st1, kBigK);
+    }
+    for (;;) {
+        const Tile cur = tile_of(bid);
+        // chunk 0 (and 1) landed; the previous tile's stores have completed
+        // too (one counter for loads and stores, which need not complete in
+        // order, so nothing finer can be waited for)
         __builtin_amdgcn_s_waitcnt(kWait0);
         big_barrier();
-        // wave w stores tokens 64 w .. 64 w + 63, two per instruction: lane
-        // half hl = lane / 32 takes token 64 w + 2 s + hl, piece lane % 32
-        const int hl = lane >> 5, k = lane & 31;
-        const unsigned char *it = wave < 2 ? st0 : st1;
-        const int f = fbase + 8 * k;
-        const int h = f / p.head_dim, e = f % p.head_dim;
-        uint16_t *out = static_cast<uint16_t *>(is_r ? p.rho : p.q) + (int64_t)h * (is_r ? p.r_sh : p.q_sh) + e;
-        const int64_t ost = is_r ? p.r_st : p.q_st;
-#pragma unroll 8
-        for (int s2 = 0; s2 < 32; ++s2) {
-            const int tr = 64 * wave + 2 * s2 + hl;  // token within the tile
-            const int r = tr & 127;
-            const uint4 v = *reinterpret_cast<const uint4 *>(it + r * 512 + 16 * (k ^ (r & 15)));
-            const int t = t0 + tr;
-            if (t < T) *reinterpret_cast<uint4 *>(out + (int64_t)t * ost) = v;
+        read_ops(st0, 0, oa);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ch = 0; ch < nch - 2; ch += 2) {
+            chunk(cur, ch, st0, st1, T_{}, T_{});
+            chunk(cur, ch + 1, st1, st0, T_{}, T_{});
         }
-    } else {
+        chunk(cur, nch - 2, st0, st1, F_{}, T_{});
+        chunk(cur, nch - 1, st1, st0, F_{}, F_{});
+
+        // acc[i][j]: lane (c, g) holds stacked rows row0 + 128 wr + 16 i +
+        // 4 g + (0..3) of token t0 + 128 wc + 16 j + c
+        const int fbase = cur.row0 - (cur.is_r ? p.n : 0);
+        const int nbid = bid + (int)gridDim.x;
+        const bool more = nbid < nt;
+        if constexpr (BF16OUT) {
+            // bf16 outputs go through LDS, so every token's 256 features
+            // leave as 16-byte pieces of whole lines (the lane layout above
+            // writes 8 bytes per token and row group, 16 tokens apart).  The
+            // tile is [256 tokens][256 features] bf16, 512-byte rows (tokens
+            // 0..127 in st0, 128..255 in st1); 16-byte piece k of row r sits
+            // at k ^ (r % 16), so the 16 rows one write touches land on
+            // distinct banks.
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            big_barrier();  // every wave's last operand reads are back
+            unsigned char *ot = wc ? st1 : st0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int f = fbase + 128 * wr + 16 * i + 4 * g;
+            for (int i = 0; i < 8; ++i) {
+                const int col = 128 * wr + 16 * i + 4 * g;  // feature, a multiple of 4
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int r = 16 * j + c;  // row within the half (r % 16 == c)
+                    const f32x4_t v = acc[i][j];
+                    const bf16x4_t b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+                    const int piece = (col >> 3) ^ c;
+                    *reinterpret_cast<uint2 *>(ot + r * 512 + 16 * piece + 2 * (col & 7)) =
+                        __builtin_bit_cast(uint2, b);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            big_barrier();
+            // Two halves: tokens 0..127 (st0), then 128..255 (st1).  In each,
+            // wave w takes tokens 32 w .. 32 w + 31 of the half, two per
+            // instruction (lane half hl = lane / 32, piece lane % 32); once
+            // every wave has read a half, its stage takes the next tile's
+            // first (second) chunk while the half's pieces are stored.
+            const int hl = lane >> 5, k = lane & 31;
+            const int f = fbase + 8 * k;
             const int h = f / p.head_dim, e = f % p.head_dim;
-            const int64_t hoff = (int64_t)h * (is_r ? p.r_sh : p.q_sh) + e;
+            uint16_t *out = static_cast<uint16_t *>(cur.is_r ? p.rho : p.q) +
+                            (int64_t)h * (cur.is_r ? p.r_sh : p.q_sh) + e;
+            const int64_t ost = cur.is_r ? p.r_st : p.q_st;
+            auto half_out = [&](const unsigned char *it, unsigned char *stage, int half, int k0)
+                __attribute__((always_inline)) {
+                uint4 vals[16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int t = t0 + 128 * wc + 16 * j + c;
-                if (t >= T) continue;
-                const int64_t off = (int64_t)t * (is_r ? p.r_st : p.q_st) + hoff;
-                const f32x4_t v = acc[i][j];
-                *reinterpret_cast<float4 *>(static_cast<float *>(is_r ? p.rho : p.q) + off) =
-                    float4{v[0], v[1], v[2], v[3]};
+                for (int s2 = 0; s2 < 16; ++s2) {
+                    const int r = 32 * wave + 2 * s2 + hl;
+                    vals[s2] = *reinterpret_cast<const uint4 *>(it + r * 512 + 16 * (k ^ (r & 15)));
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitLds);
+                big_barrier();  // every wave has read this half: its stage is free
+                if (more) dma(tile_of(nbid), stage, k0);
+                // tokens t0 + 128 half + 32 w + hl + 2 s2; a whole tile stores
+                // unconditionally (per-store conditions sent vals to scratch)
+                const int tb0 = cur.t0 + 128 * half + 32 * wave + hl;
+                uint16_t *o = out + (int64_t)tb0 * ost;
+                if (cur.t0 + kBigT <= T) {
+#pragma unroll
+                    for (int s2 = 0; s2 < 16; ++s2)
+                        *reinterpret_cast<uint4 *>(o + 2 * s2 * ost) = vals[s2];
+                } else {
+                    const int nv = T - tb0;  // this lane's stores with t < T: 2 s2 < nv
+#pragma unroll
+                    for (int s2 = 0; s2 < 16; ++s2) {
+                        const uint4 v = vals[s2];
+                        if (2 * s2 < nv) *reinterpret_cast<uint4 *>(o + 2 * s2 * ost) = v;
+                    }
+                }
+            };
+            half_out(st0, st0, 0, 0);
+            half_out(st1, st1, 1, kBigK);
+        } else {
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            big_barrier();  // every wave's last operand reads are back
+            if (more) {
+                const Tile nx = tile_of(nbid);
+                dma(nx, st0, 0);
+                dma(nx, st1, kBigK);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int f = fbase + 128 * wr + 16 * i + 4 * g;
+                const int h = f / p.head_dim, e = f % p.head_dim;
+                const int64_t hoff = (int64_t)h * (cur.is_r ? p.r_sh : p.q_sh) + e;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = cur.t0 + 128 * wc + 16 * j + c;
+                    if (t >= T) continue;
+                    const int64_t off = (int64_t)t * (cur.is_r ? p.r_st : p.q_st) + hoff;
+                    const f32x4_t v = acc[i][j];
+                    *reinterpret_cast<float4 *>(static_cast<float *>(cur.is_r ? p.rho : p.q) + off) =
+                        float4{v[0], v[1], v[2], v[3]};
+                }
             }
         }
+        if (!more) break;
+        bid = nbid;
     }
+}
+
+// Compute units of the stream's device (cached per device; 0 if unknown).
+int stream_cus(hipStream_t stream) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = -1;
+    if ((stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev)) != hipSuccess ||
+        dev < 0)
+        return 0;
+    if (dev < kMaxDevices) {
+        const int n = cache[dev].load(std::memory_order_relaxed);
+        if (n > 0) return n;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 hipError_t launch_big(const ProjParams &p, hipStream_t stream) {
     const int n_rb = 2 * p.n / kBigT, n_tb = (p.tokens + kBigT - 1) / kBigT;
-    const dim3 grid((unsigned)(n_rb * n_tb));
+    // one workgroup per CU (128 KB of LDS each), a multiple of 8 workgroups
+    const int cap = max(8, (stream_cus(stream) > 0 ? stream_cus(stream) : kCUs) / 8 * 8);
+    const int grid = min(n_rb * n_tb, cap);
     if (p.out_bf16)
-        hipLaunchKernelGGL((proj_big_kernel<true>), grid, dim3(256), 0, stream, p, n_rb, n_tb);
+        hipLaunchKernelGGL((proj_big_kernel<true>), dim3((unsigned)grid), dim3(256), 0, stream, p, n_rb, n_tb);
     else
-        hipLaunchKernelGGL((proj_big_kernel<false>), grid, dim3(256), 0, stream, p, n_rb, n_tb);
+        hipLaunchKernelGGL((proj_big_kernel<false>), dim3((unsigned)grid), dim3(256), 0, stream, p, n_rb, n_tb);
     return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ workgroups, whose items follow each other in one stream of positions):
 A planted change (the dq kernel's K tiles double- instead of triple-
 buffered, the forward's register stages swapped, its items shorter than
 the three positions its loads run ahead, or the projection's waits one
-chunk too loose or its loads issued before the barrier) must be caught.  The
+chunk too loose, its loads issued before the barrier or the next tile's
+before the output is read back) must be caught.  The
 forward this kernel replaced (four waves, each doing both roles on its own
 rows), which returned wrong results on some launches, is modelled too: the
 model locates its race (K tile 2 stored over tile 0 in the epoch in which
@@ -87,7 +88,7 @@ def check(trace):
         # all threads may store pieces of one tile together; a read, or a
         # second tile, beside a store in the same epoch is unordered
         if written and (len(written) > 1 or any(e[2] == "r" for e in evs)):
-            bad.append(("unordered access", ep, buf, sorted(evs)))
+            bad.append(("unordered access", ep, buf, sorted(evs, key=repr)))
     last = {}  # buffer -> (epoch, tile) of the latest store
     for ev in sorted(trace.events, key=lambda e: (e[0], e[2] == "r")):
         ep, who, op, buf, tile = ev
@@ -328,18 +329,26 @@ def dkv_trace(ntiles, active_sets):
 
 # ----------------------------------------------------------- projection ---
 
-def proj_trace(nsteps, waits=None, stages=2, early_loads=False):
-    """proj_big_kernel: four waves, K chunk s of both operand tiles in stage
-    s % stages, filled by global->LDS loads that each wave issues for its own
-    rows: chunks 0 and 1 in the prologue, chunk s + 2 right after chunk s's
-    barrier.  Such a load lands at no fixed time: the model writes its stage
-    in every epoch from its issue up to the one in which the issuing wave's
-    explicit wait (pending loads at most `bound` chunks' worth, oldest first)
-    covers it.  The prologue waits for chunk 0 and publishes it; chunk s
-    reads its second k-step (same stage), waits for chunk s + 1's loads,
-    passes the barrier and reads chunk s + 1's first k-step (all rows, so
-    every wave's loads).  `waits[s]` = chunk s's bound; `early_loads` plants
-    the mistake of issuing chunk s + 2's loads before the barrier."""
+def proj_trace(nsteps, waits=None, stages=2, early_loads=False, ntiles=1, early_next=False):
+    """proj_big_kernel: four waves, each running `ntiles` tiles in turn; K
+    chunk s of a tile's operands in stage s % stages, filled by global->LDS
+    loads that each wave issues for its own rows.  Such a load lands at no
+    fixed time: the model writes its stage in every epoch from its issue up
+    to the one in which the issuing wave's explicit wait (pending loads at
+    most `bound` chunks' worth, oldest first) covers it.
+
+    Per tile: chunks 0 and 1 are loaded before the tile (the first tile's in
+    the prologue, the next tile's during this tile's output), the tile
+    starts with a wait for all loads and a barrier, then reads chunk 0's
+    first k-step.  Chunk s reads its second k-step (same stage), waits for
+    chunk s + 1's loads, passes the barrier, loads chunk s + 2 into its own
+    stage and reads chunk s + 1's first k-step.  The output: a barrier,
+    the accumulators written into both stages ([256 tokens][256 features],
+    half h in stage h), a barrier, each half read back, a barrier, and that
+    half's stage takes the next tile's chunk h.  `waits[s]` = chunk s's
+    bound; `early_loads` plants loads of chunk s + 2 issued before the
+    barrier, `early_next` the next tile's loads issued before the output is
+    read back."""
     if waits is None:
         waits = proj_waits(nsteps)
     tr = Trace()
@@ -356,24 +365,38 @@ def proj_trace(nsteps, waits=None, stages=2, early_loads=False):
                 landed.setdefault(c, wv.epoch)
 
         for c in range(min(stages, nsteps)):
-            issue(c)
-        wait(stages - 1)
-        wv.barrier()
-        wv.read(("S", 0), 0)
-        for st in range(nsteps):
-            wv.read(("S", st % stages), st)  # the chunk's second k-step
-            if waits[st] is not None:
-                if early_loads and st + stages < nsteps:
-                    issue(st + stages)
-                wait(waits[st])
+            issue((0, c))
+        for tl in range(ntiles):
+            wait(0)
+            wv.barrier()
+            wv.read(("S", 0), (tl, 0))
+            for st in range(nsteps):
+                wv.read(("S", st % stages), (tl, st))  # the chunk's second k-step
+                if waits[st] is not None:
+                    if early_loads and st + stages < nsteps:
+                        issue((tl, st + stages))
+                    wait(waits[st])
+                    wv.barrier()
+                    if not early_loads and st + stages < nsteps:
+                        issue((tl, st + stages))
+                    wv.read(("S", (st + 1) % stages), (tl, st + 1))
+            more = tl + 1 < ntiles
+            wv.barrier()  # every wave's last operand reads are back
+            for h in range(2):
+                wv.write(("S", h), ("out", tl))
+            if more and early_next:
+                for h in range(2):
+                    issue((tl + 1, h))
+            wv.barrier()
+            for h in range(2):
+                wv.read(("S", h), ("out", tl))
                 wv.barrier()
-                if not early_loads and st + stages < nsteps:
-                    issue(st + stages)
-                wv.read(("S", (st + 1) % stages), st + 1)
+                if more and not early_next:
+                    issue((tl + 1, h))
         end = wv.epoch
         for c in issued:
             for e in range(since[c], landed.get(c, end) + 1):
-                tr.events.append((e, wv.name, "w", ("S", c % stages), c))
+                tr.events.append((e, wv.name, "w", ("S", c[1] % stages), c))
     return tr
 
 
@@ -508,18 +531,22 @@ def test_dkv_schedule(ntiles):
 
 
 @pytest.mark.parametrize("nsteps", [4, 8, 16, 32])
-def test_projection_schedule(nsteps):
-    assert check(proj_trace(nsteps)) == []
+@pytest.mark.parametrize("ntiles", [1, 2, 3])
+def test_projection_schedule(nsteps, ntiles):
+    assert check(proj_trace(nsteps, ntiles=ntiles)) == []
 
 
 def test_planted_projection_errors_are_caught():
     """A chunk that waits only for its older loads (one chunk still
     pending) reads the next chunk while it may still land; loads of chunk
-    s + 2 issued before the barrier store over the stage others still read."""
+    s + 2 issued before the barrier store over the stage others still read;
+    the next tile's loads issued before the output is read back overwrite
+    it."""
     w = proj_waits(16)
     w[5] = 1
     assert any(b[0] == "unordered access" for b in check(proj_trace(16, w)))
     assert any(b[0] == "unordered access" for b in check(proj_trace(16, early_loads=True)))
+    assert any(b[0] == "unordered access" for b in check(proj_trace(8, ntiles=2, early_next=True)))
 
 
 @pytest.mark.parametrize("ntiles", range(1, 12))
