@@ -646,7 +646,8 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
     }
 }
 
-// Compute units of the stream's device (cached per device; 0 if unknown).
+// Compute units of the stream's device (cached per device; 0 if unknown).  The
+// prefill's launcher keeps its own copy of this helper in its file.
 int stream_cus(hipStream_t stream) {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cache[kMaxDevices];
@@ -667,7 +668,8 @@ int stream_cus(hipStream_t stream) {
 hipError_t launch_big(const ProjParams &p, hipStream_t stream) {
     const int n_rb = 2 * p.n / kBigT, n_tb = (p.tokens + kBigT - 1) / kBigT;
     // one workgroup per CU (128 KB of LDS each), a multiple of 8 workgroups
-    const int cap = max(8, (stream_cus(stream) > 0 ? stream_cus(stream) : kCUs) / 8 * 8);
+    const int cus = stream_cus(stream);
+    const int cap = max(8, (cus > 0 ? cus : kCUs) / 8 * 8);
     const int grid = min(n_rb * n_tb, cap);
     if (p.out_bf16)
         hipLaunchKernelGGL((proj_big_kernel<true>), dim3((unsigned)grid), dim3(256), 0, stream, p, n_rb, n_tb);
