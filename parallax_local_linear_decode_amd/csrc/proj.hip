@@ -366,9 +366,10 @@ constexpr int kWait0 = 0x0070, kWaitLds = 0xC07F;
 
 // The workgroup barrier of the big-tile kernel, after the caller's explicit
 // wait.  __syncthreads() would add a release fence, for which the compiler
-// may wait for every pending global->LDS load, including the ones issued for
-// later chunks; the empty asm statements keep the compiler from moving
-// memory accesses across the barrier instead.
+// may wait for every pending vector memory operation (at the output's
+// barriers: the next tile's loads and this tile's stores, which need no
+// wait); the empty asm statements keep the compiler from moving memory
+// accesses across the barrier instead.
 __device__ __forceinline__ void big_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
