@@ -603,17 +603,23 @@ __global__ __launch_bounds__(256) void proj_big_kernel(ProjParams p, int n_rb, i
                 // unconditionally (per-store conditions sent vals to scratch)
                 const int tb0 = cur.t0 + 128 * half + 32 * wave + hl;
                 uint16_t *o = out + (int64_t)tb0 * ost;
+                // non-temporal stores: the outputs are not read again here,
+                // and streaming them past the caches let them complete sooner
+                // (the next tile waits for them: one counter for loads and
+                // stores); +3-5% at 32768 tokens
+                typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+                auto put = [&](int s2) __attribute__((always_inline)) {
+                    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, vals[s2]),
+                                                reinterpret_cast<u32x4_t *>(o + 2 * s2 * ost));
+                };
                 if (cur.t0 + kBigT <= T) {
 #pragma unroll
-                    for (int s2 = 0; s2 < 16; ++s2)
-                        *reinterpret_cast<uint4 *>(o + 2 * s2 * ost) = vals[s2];
+                    for (int s2 = 0; s2 < 16; ++s2) put(s2);
                 } else {
                     const int nv = T - tb0;  // this lane's stores with t < T: 2 s2 < nv
 #pragma unroll
-                    for (int s2 = 0; s2 < 16; ++s2) {
-                        const uint4 v = vals[s2];
-                        if (2 * s2 < nv) *reinterpret_cast<uint4 *>(o + 2 * s2 * ost) = v;
-                    }
+                    for (int s2 = 0; s2 < 16; ++s2)
+                        if (2 * s2 < nv) put(s2);
                 }
             };
             half_out(st0, st0, 0, 0);
