@@ -535,8 +535,21 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
         };
 
         // ---- o = a - (b - a r) per query row of item u (range x); lane (c, g)
-        // holds d = 16db + 4g + j
-        auto epilogue = [&](const Item &u, const PairRange &x) __attribute__((always_inline)) {
+        // holds d = 16db + 4g + j.  Output rows are written with non-temporal
+        // stores (nothing here reads them again).  DEFER: o replaces the E
+        // sums in the accumulators and store_outputs writes it later.
+        auto store_outputs = [&](const Item &u, const PairRange &x) __attribute__((always_inline)) {
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc) {
+                const int qi = x.r0 + 16 * qc + c;
+                if (qi >= S) continue;
+                float *orow = p.out + (int64_t)u.b * p.o_sb + (int64_t)qi * p.o_ss + (int64_t)x.head * p.o_sh;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    __builtin_nontemporal_store(acc[db][qc], reinterpret_cast<f32x4_t *>(orow + 16 * db + 4 * g));
+            }
+        };
+        auto epilogue = [&](const Item &u, const PairRange &x, auto defer) __attribute__((always_inline)) {
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc) {
                 const int qi = x.r0 + 16 * qc + c;
@@ -548,17 +561,28 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
                 float *orow = p.out + ooff;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    float o[4];
+                    // fused steps written out: left to the compiler, the
+                    // contraction would depend on whether a is also stored
+                    // (o_SA), and the two builds would differ in the last bit
+                    float o[4], a[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float a = acc[db][qc][j] * inv, bb = acc[db][qc + 2][j] * inv;
-                        o[j] = a - (bb - a * r);
+                        a[j] = acc[db][qc][j] * inv;
+                        const float bmar = __builtin_fmaf(inv, acc[db][qc + 2][j], -(a[j] * r));  // b - a r
+                        o[j] = __builtin_fmaf(inv, acc[db][qc][j], -bmar);
                     }
-                    *reinterpret_cast<float4 *>(orow + 16 * db + 4 * g) =
-                        float4{o[0], o[1], o[2], o[3]};
+                    // o_SA for a backward pass
+                    if (STATS && p.o_sa != nullptr)
+                        *reinterpret_cast<float4 *>(p.o_sa + ooff + 16 * db + 4 * g) =
+                            float4{a[0], a[1], a[2], a[3]};
+                    if constexpr (decltype(defer)::value)
+                        acc[db][qc] = f32x4_t{o[0], o[1], o[2], o[3]};
+                    else
+                        __builtin_nontemporal_store(f32x4_t{o[0], o[1], o[2], o[3]},
+                                                    reinterpret_cast<f32x4_t *>(orow + 16 * db + 4 * g));
                 }
-                // what a backward pass needs: log of the softmax denominator
-                // (natural log; Z is kept relative to 2^m), r and o_SA
+                // and the log of its softmax denominator (natural log; Z is
+                // kept relative to 2^m) and r
                 if constexpr (STATS) {
                     const int64_t ri = ((int64_t)u.b * p.num_q_heads + x.head) * S + qi;
                     if (p.lse != nullptr && g == 0)
@@ -566,18 +590,15 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
                                     0.6931471805599453f;
                     if (p.rmean != nullptr && g == 0) p.rmean[ri] = r;
                 }
-                if (STATS && p.o_sa != nullptr) {
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        *reinterpret_cast<float4 *>(p.o_sa + ooff + 16 * db + 4 * g) =
-                            float4{acc[db][qc][0] * inv, acc[db][qc][1] * inv, acc[db][qc][2] * inv,
-                                   acc[db][qc][3] * inv};
-                }
             }
         };
         // Position t sums the tile of position t - 1 (parity 1 - P).  At an
         // item's first position that is the previous item's last position,
-        // whose outputs are then written.
+        // whose outputs are then written: stored after the position's
+        // barrier, since the staging wait before it counts the stores too
+        // (the memory counter holds loads and stores, and the wait is sized
+        // for the positions without stores) and would hold the wave until
+        // they were written.
         PairRange pr = pair_range(cur), pv = pr;
         Item prv = cur;
         auto value_half = [&](int t, auto par, auto tail) __attribute__((always_inline)) {
@@ -588,11 +609,12 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
             const int u = first ? prv.tend - 1 : t - 1;
             const int lo = first ? pv.lo : pr.lo, hi = first ? pv.hi : pr.hi;
             if (u >= lo && u < hi && (!first || cur.i > 0)) value_tile(Q{});
+            if (first && cur.i > 0) epilogue(prv, pv, std::true_type{});
+            advance(t, par, tail);
             if (first && cur.i > 0) {
-                epilogue(prv, pv);
+                store_outputs(prv, pv);
                 clear();
             }
-            advance(t, par, tail);
         };
 
         prologue();
@@ -619,7 +641,7 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
         }
         // the position after the last: its last tile and outputs
         if (cur.tend - 1 >= pr.lo && cur.tend - 1 < pr.hi) value_tile(I1{});
-        epilogue(cur, pr);
+        epilogue(cur, pr, std::false_type{});
         advance(cur.tend, I0{}, Tail{});
     }
 }
