@@ -345,7 +345,10 @@ def proj_trace(nsteps, waits=None, stages=2, early_loads=False, ntiles=1, early_
     stage and reads chunk s + 1's first k-step.  The output: a barrier,
     the accumulators written into both stages ([256 tokens][256 features],
     half h in stage h), a barrier, each half read back, a barrier, and that
-    half's stage takes the next tile's chunk h.  `waits[s]` = chunk s's
+    half's stage takes the next tile's chunk h.  (The kernel's wait at a
+    tile's start leaves the previous tile's last 16 stores pending, which
+    follow every load in issue order: for the loads it is the full wait
+    modelled here.)  `waits[s]` = chunk s's
     bound; `early_loads` plants loads of chunk s + 2 issued before the
     barrier, `early_next` the next tile's loads issued before the output is
     read back."""
