@@ -60,6 +60,7 @@ KERNEL_SOURCES = {  # what the kernels of a workload are built from
     "prefill_bwd": ["parallax_local_linear_decode_amd/csrc/prefill_bwd.hip"] + _COMMON,
 }
 KERNEL_SOURCES["decode_headline"] = KERNEL_SOURCES["decode"]
+KERNEL_SOURCES["qr_proj"] = ["parallax_local_linear_decode_amd/csrc/proj.hip"] + _COMMON
 
 
 def log(*a):
@@ -450,7 +451,8 @@ def run_qr_proj(args, torch, plx):
              "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None} if hbm else
             {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
              "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-             "traffic": None})
+             # counters were taken at 32768 tokens, model dim 2048
+             "traffic": traffic_for("qr_proj") if (T, D) == (32768, 2048) else None})
     return {
         "metric": "q and rho projection in one launch: " + ("weight GB/s" if hbm else "TFLOP/s"),
         "value": round(gbps, 2) if hbm else round(tflops, 1),
