@@ -20,3 +20,23 @@ def test_a_second_rank_is_refused():
                        env=env)
     assert r.returncode == 2
     assert "single process" in r.stderr
+
+
+def test_committed_traffic_figures_match_the_kernel_sources():
+    """profiles/traffic.json holds the counter-measured HBM bytes that the
+    bench line reports as `traffic`; each entry names a hash of the sources
+    its kernels were built from, and the bench drops a figure whose hash no
+    longer matches.  Every committed entry is current, and every kernel set
+    the bench looks up has an entry."""
+    import importlib.util
+    import json
+    spec = importlib.util.spec_from_file_location("bench_mod", BENCH)
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    with open(bench.TRAFFIC_FILE) as f:
+        traffic = json.load(f)
+    assert set(traffic) == set(bench.KERNEL_SOURCES)
+    for name, entry in traffic.items():
+        assert entry["kernel_sha"] == bench.kernel_sha(name), f"{name}: re-take its counters"
+        assert abs(entry["bytes_per_launch"] - entry["fetch_bytes"] - entry["write_bytes"]) <= 1
+        assert bench.traffic_for(name) == float(entry["bytes_per_launch"])
