@@ -690,6 +690,7 @@ def run_suite(args, torch, plx):
     recs = {}
     sub.batch, sub.ctx, sub.window, sub.split = 8, 4096, 0, 0
     recs["decode_b8_ctx4096"] = run_decode(sub, torch, plx)
+    recs["lla"] = run_lla(sub, torch, plx)
     recs["paged"] = run_paged(sub, torch, plx)
     sub.head_dim, sub.q_heads, sub.kv_heads = 128, 16, 8
     sub.steps, sub.warmup = max(args.steps, 20), max(args.warmup, 3)
