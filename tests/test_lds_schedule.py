@@ -290,11 +290,12 @@ def dq_trace(t_first, ntiles, pairs, kslots=3):
 
 # ---------------------------------------------------------------------- dkv ---
 
-def dkv_trace(ntiles, active_sets):
+def dkv_trace(ntiles, active_sets, early_loads=False):
     """bwd_dkv_kernel: q, rho, dout tiles and row statistics of tile t in
     buffer t % 3 (one register stage: tile t + 1 goes to LDS at the start of
-    epoch t, the stage then loads tile t + 2); per-pair W, dS, dT operands
-    double-buffered.  `active_sets` = the tiles each pair works on."""
+    epoch t, the stage then loads tile t + 2, after the value MFMAs' reads
+    or, `early_loads` (head dim 64), before them); per-pair W, dS, dT
+    operands double-buffered.  `active_sets` = the tiles each pair works on."""
     tr = Trace()
     for p, act in enumerate(active_sets):
         s = tr.wave(f"score{p}")
@@ -314,11 +315,14 @@ def dkv_trace(ntiles, active_sets):
         for t in range(ntiles):
             for a in ("Q", "R", "G", "STAT"):
                 v.store("st", (a, (t + 1) % 3), t + 1)
+            if early_loads:
+                v.load("st", t + 2)
             if t - 1 in act:
                 v.read(("P", p, (t - 1) & 1), t - 1)
                 for a in ("Q", "R", "G"):
                     v.read((a, (t - 1) % 3), t - 1)
-            v.load("st", t + 2)
+            if not early_loads:
+                v.load("st", t + 2)
             v.barrier()
         if ntiles - 1 in act:  # after the last barrier
             v.read(("P", p, (ntiles - 1) & 1), ntiles - 1)
@@ -523,14 +527,15 @@ def test_dq_schedule(t_first, ntiles, pairs):
     assert check(dq_trace(t_first, ntiles, pairs)) == []
 
 
+@pytest.mark.parametrize("early_loads", [False, True])
 @pytest.mark.parametrize("ntiles", range(1, 13))
-def test_dkv_schedule(ntiles):
+def test_dkv_schedule(ntiles, early_loads):
     # pairs see contiguous runs of query tiles, per head of the group (G = 2:
     # two runs of nq tiles), some pairs none at all
     nq = max(1, ntiles // 2)
     sets = [set(range(ntiles)), {t for t in range(ntiles) if t % nq >= 1},
             {t for t in range(ntiles) if t % nq >= nq - 1}, set()]
-    assert check(dkv_trace(ntiles, sets)) == []
+    assert check(dkv_trace(ntiles, sets, early_loads)) == []
 
 
 @pytest.mark.parametrize("nsteps", [4, 8, 16, 32])
