@@ -690,11 +690,17 @@ def run_suite(args, torch, plx):
     recs = {}
     sub.batch, sub.ctx, sub.window, sub.split = 8, 4096, 0, 0
     recs["decode_b8_ctx4096"] = run_decode(sub, torch, plx)
+    sub.ctx, sub.window = 32768, 4096  # the local window: each row's last 4096 tokens
+    recs["decode_window4096"] = run_decode(sub, torch, plx)
+    sub.ctx, sub.window = 4096, 0
     recs["lla"] = run_lla(sub, torch, plx)
     recs["paged"] = run_paged(sub, torch, plx)
     sub.head_dim, sub.q_heads, sub.kv_heads = 128, 16, 8
     sub.steps, sub.warmup = max(args.steps, 20), max(args.warmup, 3)
     recs["prefill"] = run_prefill(sub, torch, plx)
+    sub.window = 1024
+    recs["prefill_window1024"] = run_prefill(sub, torch, plx)
+    sub.window = 0
     recs["prefill_bwd"] = run_prefill_bwd(sub, torch, plx)
     sub.tokens, sub.model_dim = 32768, 2048
     recs["qr_proj"] = run_qr_proj(sub, torch, plx)
