@@ -125,22 +125,24 @@ __device__ __forceinline__ void store_shared(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// o of element e of head g from the nsp split records at `recs` (one unit):
-// the running max over the records, every record's sums scaled to it.
-// Sixteen records' loads are in flight at a time (one round trip for up to
-// sixteen splits: rows with many short splits wait on few dependent reads).
+// Sums of element e of head g over split records [lo, hi) at `recs` (one
+// unit): the running max M over the records, and Z, R, A, B with every
+// record's sums scaled to it.  Sixteen records' loads are in flight at a time
+// (one round trip for up to sixteen records).
 constexpr int kMergeChunk = 16;
 template <int D, int G, bool SHARED>
-__device__ __forceinline__ float merge_records(const float *recs, int nsp, int g, int e) {
+__device__ __forceinline__ void merge_range(const float *recs, int lo, int hi, int g, int e,
+                                            float &M, float &Z, float &R, float &A, float &B) {
     constexpr int REC = partial_floats(D);
     auto ld = [](const float *q) { return SHARED ? load_shared(q) : *q; };
-    float M = -INFINITY, Z = 0.f, R = 0.f, A = 0.f, B = 0.f;
-    for (int c0 = 0; c0 < nsp; c0 += kMergeChunk) {
+    M = -INFINITY;
+    Z = R = A = B = 0.f;
+    for (int c0 = lo; c0 < hi; c0 += kMergeChunk) {
         float mm[kMergeChunk], zz[kMergeChunk], rr[kMergeChunk], aa[kMergeChunk], bb[kMergeChunk];
 #pragma unroll
         for (int i = 0; i < kMergeChunk; ++i) {
-            const float *rec = recs + (min(c0 + i, nsp - 1) * G + g) * REC;
-            const bool live = c0 + i < nsp;
+            const float *rec = recs + (min(c0 + i, hi - 1) * G + g) * REC;
+            const bool live = c0 + i < hi;
             mm[i] = live ? ld(rec + 2 * D) : -INFINITY;
             zz[i] = ld(rec + 2 * D + 1);
             rr[i] = ld(rec + 2 * D + 2);
@@ -165,6 +167,13 @@ __device__ __forceinline__ float merge_records(const float *recs, int nsp, int g
         }
         M = Mn;
     }
+}
+
+// o of element e of head g from the nsp split records at `recs` (one unit).
+template <int D, int G, bool SHARED>
+__device__ __forceinline__ float merge_records(const float *recs, int nsp, int g, int e) {
+    float M, Z, R, A, B;
+    merge_range<D, G, SHARED>(recs, 0, nsp, g, e, M, Z, R, A, B);
     return finish(A, B, Z, R);
 }
 
@@ -250,10 +259,48 @@ __device__ void finish_block(const DecodeParams &p, float (*red)[G][partial_floa
     __syncthreads();
     if (!last) return;
     const float *recs = p.partials + (int64_t)unit * p.nsplit * G * REC;
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
+    // With more threads than elements, a row of more than sixteen splits is
+    // merged in PARTS record ranges side by side (one round trip of loads
+    // instead of one per sixteen records); ranges 1.. hand their sums to
+    // range 0 through `red`, which is free again after the barriers above.
+    constexpr int PARTS = 64 * NW > G * D ? 64 * NW / (G * D) : 1;
+    if (PARTS > 1 && nsp > kMergeChunk) {
+        const int part = threadIdx.x / (G * D), idx = threadIdx.x % (G * D);
         const int g = idx / D, e = idx % D;
-        p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] =
-            merge_records<D, G, true>(recs, nsp, g, e);
+        const int per = (nsp + PARTS - 1) / PARTS;
+        const int lo = min(part * per, nsp), hi = min(lo + per, nsp);
+        float M, Z, R, A, B;
+        merge_range<D, G, true>(recs, lo, hi, g, e, M, Z, R, A, B);
+        if (part > 0) {
+            red[part][g][e] = A;
+            red[part][g][D + e] = B;
+            if (e == 0) {
+                red[part][g][2 * D] = M;
+                red[part][g][2 * D + 1] = Z;
+                red[part][g][2 * D + 2] = R;
+            }
+        }
+        __syncthreads();
+        if (part == 0) {
+            for (int q = 1; q < PARTS; ++q) {
+                const float Mq = red[q][g][2 * D];
+                const float Mn = fmaxf(M, Mq);
+                const float s0 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+                const float s1 = Mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mq - Mn);
+                Z = Z * s0 + s1 * red[q][g][2 * D + 1];
+                R = R * s0 + s1 * red[q][g][2 * D + 2];
+                A = A * s0 + s1 * red[q][g][e];
+                B = B * s0 + s1 * red[q][g][D + e];
+                M = Mn;
+            }
+            p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] = finish(A, B, Z, R);
+        }
+    } else {
+        for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
+            const int g = idx / D, e = idx % D;
+            p.out[b * p.out_sb + (int64_t)(hk * G + g) * p.out_sh + e] =
+                merge_records<D, G, true>(recs, nsp, g, e);
+        }
     }
     // Every split of the row has arrived: clear its flags, so that the next
     // launch with this tag (a replayed graph) starts from none.  A split

@@ -163,6 +163,31 @@ def test_ragged_lengths(gpu, kv_dtype, d, G):
         assert torch.all(out[lens.index(0)] == 0)
 
 
+@pytest.mark.parametrize("kv_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_many_splits(gpu, kv_dtype, d, G):
+    """Rows of up to 36 splits of 256 tokens: above sixteen splits the last
+    arriving split merges the records in several ranges side by side when
+    the workgroup has threads to spare (G * d below its thread count), else
+    in one range; rows of 17, 16, 2, 1 and 0 splits beside them."""
+    lens = [9000, 4300, 4096, 300, 0, 8193]
+    B, Hkv, Lcap = len(lens), 2, 9000
+    inp = decode_inputs(B, Hkv * G, Hkv, d, Lcap, kv_dtype=kv_dtype, seed=G * 7 + d)
+    inp.seq_lens = torch.tensor(lens, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        inp.k[b, :, L:] = float("nan")
+        inp.v[b, :, L:] = float("nan")
+    ref = oracle_decode(inp)
+    inp = to(inp, gpu)
+    tau = TAU_F32 if kv_dtype == torch.float32 else TAU_BF16
+    out = run(inp, split_tokens=256)
+    assert_parity(out, ref, tau, None if kv_dtype == torch.float32 else RMS_DECODE_BF16,
+                  what=f"many splits G={G} d={d}")
+    assert torch.all(out[lens.index(0)] == 0)
+    assert torch.equal(run(inp, split_tokens=256), out)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_short_rows(gpu, d, G):
