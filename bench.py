@@ -49,8 +49,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # weights enter as two-term bf16 splits; sums accumulate in fp32).
 DECODE_DTYPE = "bf16"
 _COMMON = ["parallax_local_linear_decode_amd/csrc/kernels.hpp",
-           "parallax_local_linear_decode_amd/csrc/api.hip",
-           "parallax_local_linear_decode_amd/build.py"]
+           "parallax_local_linear_decode_amd/csrc/api.hip"]
 KERNEL_SOURCES = {  # what the kernels of a workload are built from
     "decode": ["parallax_local_linear_decode_amd/csrc/decode.hip",
                "parallax_local_linear_decode_amd/csrc/lla_row.hpp"] + _COMMON,
@@ -68,10 +67,17 @@ def log(*a):
 
 
 def kernel_sha(workload):
+    """Hash of what a workload's kernels are built from: their sources and
+    the compiler flags they are built with."""
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    from parallax_local_linear_decode_amd import build
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES.get(workload, []):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+        flags = build.flags_for(os.path.basename(rel))
+        h.update(" ".join(f for f in flags if not f.startswith("-I")).encode())
     return h.hexdigest()[:16]
 
 
@@ -704,6 +710,7 @@ def run_suite(args, torch, plx):
     recs["prefill_bwd"] = run_prefill_bwd(sub, torch, plx)
     sub.tokens, sub.model_dim = 32768, 2048
     recs["qr_proj"] = run_qr_proj(sub, torch, plx)
+    probe = issue_probe(torch, plx)
     for r in recs.values():  # the sub-records' own JSON keys, minus the shared ones
         for k in ("metric", "dtype"):
             r.pop(k, None)
@@ -723,8 +730,69 @@ def run_suite(args, torch, plx):
         "kv_tokens_per_s": head["kv_tokens_per_s"], "parity": head["parity"],
         "roofline": roof, "cpu_baseline": head["cpu_baseline"],
         "sweep_summary": sweep_summary(points), "sweep": points, **recs,
-        "host": host_info(),
+        "issue_probe": probe, "host": host_info(),
     }
+
+
+def issue_probe(torch, plx, steps=5, warmup=2):
+    """How matrix-core and vector work share a SIMD (libparallax_probe): one
+    workgroup of eight waves per CU, waves 0-3 running independent 16x16x32
+    bf16 MFMAs and waves 4-7 (one beside each) independent fp32 FMAs or
+    base-2 exponentials, each group alone and both together, and FMAs on two
+    waves per SIMD (how much of the vector rate one wave issues).  `overlap` is
+    (t_a + t_b - t_ab) / min(t_a, t_b): 1 when the two kinds of work run side
+    by side, 0 when they take turns."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(plx.__file__)), "libparallax_probe.so")
+    if not os.path.exists(path):
+        log(f"issue probe: {path} missing (run the build); not reported")
+        return None
+    lib = ctypes.CDLL(path)
+    lib.parallax_probe_issue.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(512, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    M, F, E = 40000, 160000, 40000  # iterations: about 2 ms alone each
+
+    def timed(mode, valu_iters):
+        def launch(i):
+            if lib.parallax_probe_issue(mode, M, valu_iters, cus, ctypes.c_void_p(sink.data_ptr()),
+                                        stream) != 0:
+                raise SystemExit("issue probe failed to launch")
+        return time_launches(torch, launch, 1, steps, warmup) / steps
+
+    t_m, t_f, t_mf, t_ff = timed(1, F), timed(2, F), timed(3, F), timed(10, F)
+    t_e, t_me = timed(6, E), timed(7, E)
+    mfma_flops = cus * 4 * M * 8 * 16 * 16 * 32 * 2
+    fma_flops = cus * 4 * 64 * F * 8 * 2
+
+    def overlap(a, b, ab):
+        return round((a + b - ab) / min(a, b), 3)
+    return {
+        "kernel": f"{cus} workgroups x 8 waves (one per CU); per SIMD one MFMA wave and one "
+                  "vector wave, 8 independent chains each",
+        "mfma_alone_us": round(t_m * 1e6, 1),
+        "mfma_alone_tflops": round(mfma_flops / t_m / 1e12, 1),
+        "fma_alone_us": round(t_f * 1e6, 1),
+        "fma_alone_tflops": round(fma_flops / t_f / 1e12, 1),
+        "fma_two_waves_per_simd_tflops": round(2 * fma_flops / t_ff / 1e12, 1),
+        "mfma_with_fma_us": round(t_mf * 1e6, 1),
+        "overlap_mfma_fma": overlap(t_m, t_f, t_mf),
+        "exp_alone_us": round(t_e * 1e6, 1),
+        "exp_alone_per_s": round(cus * 4 * 64 * E * 8 / t_e, 1),
+        "mfma_with_exp_us": round(t_me * 1e6, 1),
+        "overlap_mfma_exp": overlap(t_m, t_e, t_me),
+    }
+
+
+def run_issue(args, torch, plx):
+    rec = issue_probe(torch, plx, args.steps, args.warmup)
+    if rec is None:
+        raise SystemExit("issue probe library missing")
+    return {"metric": "MFMA and vector work on one SIMD (overlap)", "value": rec["overlap_mfma_fma"],
+            "unit": "fraction", "ms_per_step": rec["mfma_with_fma_us"] * 1e-3, "dtype": "bf16",
+            "config": {"workload": "issue probe: MFMA waves beside FMA or exp waves"},
+            "roofline": None, "cpu_baseline": None, **rec}
 
 
 def run_copy(args, torch, plx):
@@ -976,7 +1044,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="suite",
                     choices=["suite", "decode", "paged", "prefill", "prefill_bwd", "lla", "qr_proj",
-                             "sweep", "copy"])
+                             "sweep", "copy", "issue"])
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--ctx", type=int, default=4096)
     ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
@@ -1012,7 +1080,7 @@ def main():
     runner = {"suite": run_suite, "decode": run_decode, "paged": run_paged, "sweep": run_sweep,
               "copy": run_copy, "prefill": run_prefill,
               "prefill_bwd": run_prefill_bwd, "lla": run_lla,
-              "qr_proj": run_qr_proj}.get(args.workload)
+              "qr_proj": run_qr_proj, "issue": run_issue}.get(args.workload)
     if runner is None:
         raise SystemExit(f"workload {args.workload} is not available")
     rec = runner(args, torch, plx)

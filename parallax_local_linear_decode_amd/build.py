@@ -19,7 +19,7 @@ SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill_bwd.hip", "lla.hip",
 # A plain read-stream kernel the benchmark times as the HBM reference; its
 # own library, not part of libparallax.
 PROBE_LIB = os.path.join(PKG, "libparallax_probe.so")
-PROBE_SOURCES = ["read_probe.hip"]
+PROBE_SOURCES = ["read_probe.hip", "issue_probe.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the generated code.  MFMA
@@ -39,6 +39,14 @@ VGPR_FORM = ("-mllvm", "-amdgpu-mfma-vgpr-form=1")
 AGPR_FORM = ("proj.hip",)
 
 
+def flags_for(src: str) -> list:
+    """hipcc flags of one source file (a name under csrc/)."""
+    if src in AGPR_FORM:
+        i = HIPCC_FLAGS.index(VGPR_FORM[1])
+        return HIPCC_FLAGS[:i - 1] + HIPCC_FLAGS[i + 1:]
+    return list(HIPCC_FLAGS)
+
+
 def _hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -53,11 +61,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        flags = HIPCC_FLAGS
-        if src in AGPR_FORM:
-            i = HIPCC_FLAGS.index(VGPR_FORM[1])
-            flags = HIPCC_FLAGS[:i - 1] + HIPCC_FLAGS[i + 1:]
-        cmd = [hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *flags_for(src), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
