@@ -74,6 +74,7 @@ constexpr int pf_row_bytes() { return 2 * D + 16; }
 template <int D>
 constexpr int pf_vrow_bytes() { return 2 * D + 32; }
 constexpr float kSlack = 8.0f;            // base-2 headroom before a row's reference max moves
+constexpr float kSlackWeight = 256.0f;    // 2^kSlack: the largest weight a kept reference allows
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -368,13 +369,10 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
                               auto mask_tag) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_tag)::value;
             constexpr int P = decltype(par)::value;
-            // The two 16-row halves (qc) run side by side, phase by phase, so
-            // their dependency chains (max, cross-group max, exp) overlap.
-            float sv[2][8], gm[2];
+            float sv[2][8];
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc) {
                 const int qi = pr.r0 + 16 * qc + c;
-                float tmax = -INFINITY;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     sv[qc][r] = r < 4 ? d1[0][qc][r] : d1[1][qc][r - 4];
@@ -384,35 +382,65 @@ __global__ __launch_bounds__(128 * kPfPairs, D == 64 ? 4 : 1) void prefill_kerne
                                         ? sv[qc][r]
                                         : -INFINITY;
                     }
-                    tmax = __builtin_fmaxf(tmax, sv[qc][r]);
                 }
-                gm[qc] = tmax;
             }
+            // The weights against the rows' current reference.  It stays
+            // unless a weight exceeds 2^kSlack or a row has no reference yet;
+            // only then (a wave-uniform branch, rare after an item's first
+            // tile) are the rows' tile maxima taken across the lane groups
+            // and the weights formed again against the moved reference.
+            float ev[2][8];
+            float emax = 0.0f;
 #pragma unroll
-            for (int qc = 0; qc < 2; ++qc) gm[qc] = group_max(gm[qc]);
-            float mnew[2], alpha[2];
+            for (int qc = 0; qc < 2; ++qc)
 #pragma unroll
-            for (int qc = 0; qc < 2; ++qc) {
-                const float tm2 = gm[qc] * c2;
-                mnew[qc] = tm2 > mref[qc] + kSlack ? tm2 : mref[qc];
-                alpha[qc] = __builtin_amdgcn_exp2f(mref[qc] - mnew[qc]);  // 1 unless moved
-                if constexpr (MASK && WIN) {
-                    // a row that has met no key yet (its window starts past
-                    // this tile) keeps m = -inf: weights 0, factor 1
-                    if (mnew[qc] == -INFINITY) alpha[qc] = 1.0f;
+                for (int r = 0; r < 8; ++r) {
+                    ev[qc][r] = __builtin_amdgcn_exp2f(fmaf(sv[qc][r], c2, -mref[qc]));
+                    emax = __builtin_fmaxf(emax, ev[qc][r]);
                 }
-                mref[qc] = mnew[qc];
-                if constexpr (MASK && WIN) {
-                    if (mnew[qc] == -INFINITY) mnew[qc] = 0.0f;  // exp2(-inf - 0) = 0 below
+            float alpha[2] = {1.0f, 1.0f};
+            const bool move = !(emax <= kSlackWeight) || mref[0] == -INFINITY || mref[1] == -INFINITY;
+            if (__builtin_amdgcn_ballot_w64(move)) {
+                // The two 16-row halves (qc) run side by side, phase by phase,
+                // so their dependency chains (max, cross-group max, exp) overlap.
+                float gm[2];
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc) {
+                    float tmax = -INFINITY;
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) tmax = __builtin_fmaxf(tmax, sv[qc][r]);
+                    gm[qc] = tmax;
                 }
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc) gm[qc] = group_max(gm[qc]);
+                float mnew[2];
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc) {
+                    const float tm2 = gm[qc] * c2;
+                    mnew[qc] = tm2 > mref[qc] + kSlack ? tm2 : mref[qc];
+                    alpha[qc] = __builtin_amdgcn_exp2f(mref[qc] - mnew[qc]);  // 1 unless moved
+                    if constexpr (MASK && WIN) {
+                        // a row that has met no key yet (its window starts past
+                        // this tile) keeps m = -inf: weights 0, factor 1
+                        if (mnew[qc] == -INFINITY) alpha[qc] = 1.0f;
+                    }
+                    mref[qc] = mnew[qc];
+                    if constexpr (MASK && WIN) {
+                        if (mnew[qc] == -INFINITY) mnew[qc] = 0.0f;  // exp2(-inf - 0) = 0 below
+                    }
+                }
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+                        ev[qc][r] = __builtin_amdgcn_exp2f(fmaf(sv[qc][r], c2, -mnew[qc]));
             }
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc) {
                 uint32_t ew[4], etw[4];
 #pragma unroll
                 for (int r = 0; r < 8; r += 2) {
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sv[qc][r], c2, -mnew[qc]));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sv[qc][r + 1], c2, -mnew[qc]));
+                    const float e0 = ev[qc][r], e1 = ev[qc][r + 1];
                     const float t0 = r < 4 ? d1[0][qc + 2][r] : d1[1][qc + 2][r - 4];
                     const float t1 = r < 4 ? d1[0][qc + 2][r + 1] : d1[1][qc + 2][r - 3];
                     ew[r / 2] = pack_bf16x2(e0, e1);
