@@ -342,9 +342,11 @@ __global__ __launch_bounds__(128 * kBwPairs) void bwd_dq_kernel(PrefillBwdParams
                             const int key = t * kBwTile + (rr < 4 ? 4 * g + rr : 16 + 4 * g + rr - 4);
                             pw = key <= qi && key < S && (W == 0 || key > qi - W) ? pw : 0.0f;
                         }
-                        // dL/dp - D = u (1 + r - t) + (c t - D)
-                        ds2[h2] = pw * fmaf(uu, r1 - tt, fmaf(tt, cc, -dd));
-                        dt2[h2] = pw * (cc - uu);
+                        // dL/dp - D = u (1 + r - t) + (c t - D), formed as
+                        // (u (1 + r) - D) + t (c - u): c - u is dT's factor too
+                        const float cu = cc - uu;
+                        ds2[h2] = pw * fmaf(tt, cu, fmaf(uu, r1, -dd));
+                        dt2[h2] = pw * cu;
                     }
                     sw[r / 2] = pack_bf16x2(ds2[0], ds2[1]);
                     tw[r / 2] = pack_bf16x2(dt2[0], dt2[1]);
