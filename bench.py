@@ -795,6 +795,46 @@ def run_issue(args, torch, plx):
             "roofline": None, "cpu_baseline": None, **rec}
 
 
+def run_sdpa(args, torch, plx):
+    """Context, not the method: torch's fused softmax attention (its flash
+    backend on this ROCm build) on the decode and prefill shapes above,
+    with equal head counts (the fused kernels take no grouped heads). The
+    decode case streams the same 134 MB cache as batch 8 x 4096 at 16/8
+    heads; the prefill case does the causal softmax-attention half of the
+    Parallax prefill's matrix products (2 of 4)."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    F = torch.nn.functional
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device=dev, dtype=torch.bfloat16, generator=gen)
+
+    def timed(sets, causal):
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            def launch(i):
+                F.scaled_dot_product_attention(*sets[i], is_causal=causal)
+            launch(0)
+            torch.cuda.synchronize()
+            return time_launches(torch, launch, len(sets), args.steps, args.warmup) / args.steps
+    B, H, L, d = 8, 8, 4096, 128
+    sets = [(rnd(B, H, 1, d), rnd(B, H, L, d), rnd(B, H, L, d)) for _ in range(8)]
+    t_dec = timed(sets, False)
+    kv = B * H * L * d * 2 * 2
+    del sets
+    S, Hq = 8192, 16
+    t_pf = timed([(rnd(4, Hq, S, d), rnd(4, Hq, S, d), rnd(4, Hq, S, d))], True)
+    fl = 2 * 2 * d * causal_pairs(S) * 4 * Hq
+    return {"metric": "torch fused softmax attention (flash backend), for context",
+            "value": round(fl / t_pf / 1e12, 1), "unit": "TFLOP/s", "ms_per_step": t_pf * 1e3,
+            "dtype": "bf16",
+            "config": {"workload": "torch SDPA: decode 8 x 4096 at 8/8 heads; causal prefill "
+                                   "4 x 8192 at 16/16 heads, d 128"},
+            "roofline": None, "cpu_baseline": None,
+            "decode_us": round(t_dec * 1e6, 2), "decode_gbps": round(kv / t_dec / 1e9, 1),
+            "prefill_ms": round(t_pf * 1e3, 4), "prefill_tflops": round(fl / t_pf / 1e12, 1)}
+
+
 def run_copy(args, torch, plx):
     """A plain device-to-device copy of a known size, to calibrate counters."""
     n = args.copy_bytes
@@ -1044,7 +1084,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="suite",
                     choices=["suite", "decode", "paged", "prefill", "prefill_bwd", "lla", "qr_proj",
-                             "sweep", "copy", "issue"])
+                             "sweep", "copy", "issue", "sdpa"])
     ap.add_argument("--batch", type=int, default=8)
     ap.add_argument("--ctx", type=int, default=4096)
     ap.add_argument("--split", type=int, default=0, help="split_tokens (0 = library choice)")
@@ -1080,7 +1120,8 @@ def main():
     runner = {"suite": run_suite, "decode": run_decode, "paged": run_paged, "sweep": run_sweep,
               "copy": run_copy, "prefill": run_prefill,
               "prefill_bwd": run_prefill_bwd, "lla": run_lla,
-              "qr_proj": run_qr_proj, "issue": run_issue}.get(args.workload)
+              "qr_proj": run_qr_proj, "issue": run_issue,
+              "sdpa": run_sdpa}.get(args.workload)
     if runner is None:
         raise SystemExit(f"workload {args.workload} is not available")
     rec = runner(args, torch, plx)
