@@ -404,3 +404,21 @@ def test_projection_rejects(lib, over, status, needle):
     assert lib.parallax_qr_projection(ctypes.byref(a), None) == status
     assert needle in plx.parallax_last_error()
     assert lib.parallax_qr_projection(None, None) == INVALID
+
+
+def test_probe_library_exports_its_kernels_and_rejects_bad_arguments():
+    """The benchmark's reference kernels (read stream, decode-shaped read,
+    matrix/vector issue probe) live in their own library; its launchers check
+    their arguments on the host before any HIP call."""
+    path = os.path.join(os.path.dirname(plx.LIB_PATH), "libparallax_probe.so")
+    probe = ctypes.CDLL(path)
+    for n in ("parallax_probe_read", "parallax_probe_read_decode_shape", "parallax_probe_issue"):
+        assert hasattr(probe, n), n
+    probe.parallax_probe_issue.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
+    probe.parallax_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    assert probe.parallax_probe_issue(16, 1, 1, 256, FAKE, None) == 1   # unknown mode bit
+    assert probe.parallax_probe_issue(1, -1, 1, 256, FAKE, None) == 1   # negative count
+    assert probe.parallax_probe_issue(1, 1, 1, 0, FAKE, None) == 1      # no workgroups
+    assert probe.parallax_probe_issue(1, 1, 1, 256, None, None) == 1    # no sink
+    assert probe.parallax_probe_read(FAKE, 24, FAKE, None) == 1         # not whole 16 bytes
